@@ -1,0 +1,70 @@
+"""Seeded input generators: layout, determinism and the length/paging recipes."""
+import numpy as np
+import pytest
+
+import workloads
+
+
+def test_bf16_rounding_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 10,
+                        np.array([1.0 + 2**-8, 1.0 + 3 * 2**-8, -(1.0 + 2**-8), 0.0, -0.0], np.float32)])
+    ours = workloads.bf16_bits(x)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_tiny_layout():
+    t = workloads.tiny(0)
+    assert t.q.shape == (192, 2, 64) and t.k.shape == (192, 2, 64)
+    np.testing.assert_array_equal(t.cu_q, [0, 37, 101, 102, 192])
+    assert t.cu_q.dtype == np.int32
+    # values are exactly representable in bf16
+    np.testing.assert_array_equal(workloads.bf16_round(t.q), t.q)
+
+
+def test_seed_determinism():
+    a, b = workloads.tiny(3), workloads.tiny(3)
+    np.testing.assert_array_equal(a.q, b.q)
+    np.testing.assert_array_equal(a.do, b.do)
+    assert not np.array_equal(workloads.tiny(4).q, a.q)
+
+
+@pytest.mark.parametrize("s", [0.1, 0.5, 0.9])
+def test_sparsity_lengths(s):
+    rng = np.random.default_rng(0)
+    L = workloads.sparsity_lengths(rng, 20000, 1024, s)
+    hi = int(np.floor(1024 * (1 - s) * 2))
+    assert L.min() >= 1 and L.max() <= min(hi, 1024)
+    unclipped_mean = (1 + hi) / 2
+    expected = np.mean(np.minimum(np.arange(1, hi + 1), 1024))
+    assert abs(L.mean() - expected) < 0.02 * expected
+    if s >= 0.5:
+        assert abs(L.mean() - unclipped_mean) < 0.02 * unclipped_mean
+
+
+def test_offsets_monotone():
+    cu = workloads.offsets([3, 0, 5])
+    np.testing.assert_array_equal(cu, [0, 3, 3, 8])
+
+
+def test_paged_cache_holds_contiguous_rows():
+    inp = workloads.decode(7, [5, 16, 1, 33], heads_q=4, heads_kv=2, head_dim=8, page_size=4)
+    assert inp.num_pages == 2 + 4 + 1 + 9
+    used = np.concatenate([inp.page_table[b, :-(-L // 4)] for b, L in enumerate(inp.seqlens_k)])
+    np.testing.assert_array_equal(np.sort(used), np.arange(inp.num_pages))   # a permutation
+    for b, L in enumerate(inp.seqlens_k):
+        for t in range(L):
+            page, slot = inp.page_table[b, t // 4], t % 4
+            np.testing.assert_array_equal(inp.k_cache[page, slot], inp.k[inp.cu_k[b] + t])
+            np.testing.assert_array_equal(inp.v_cache[page, slot], inp.v[inp.cu_k[b] + t])
+        if L % 4:
+            assert np.isnan(inp.k_cache[inp.page_table[b, L // 4], L % 4:]).all()
+
+
+def test_config_shapes_small():
+    g = workloads.gem(0, 0.9)
+    assert g.q.shape[1:] == (8, 128) and g.batch == 256 and g.max_len_q <= 1024
+    bq = workloads.broadcast_q(0, 0.9, batch=8)
+    assert bq.q.shape == (256, 4, 128) and bq.do.shape == (8, 256, 4, 128)
