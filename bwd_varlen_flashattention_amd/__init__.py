@@ -1,0 +1,161 @@
+"""Python binding of libjfa.so: exact jagged FlashAttention fwd/bwd and split-KV
+paged decode on MI355X (gfx950).
+
+The functions keep the C ABI's names and only marshal arguments: they check
+dtypes and shapes, allocate outputs and the workspace with torch on the current
+device, and call the library on torch's current stream.  Every step of the
+computation runs in the library's HIP kernels; there is no CPU or PyTorch
+fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+from typing import Optional
+
+from . import _lib
+from ._lib import AttnParams, DecodeParams, JfaError, load  # noqa: F401
+
+__all__ = ["jfa_fwd", "jfa_bwd", "jfa_decode_paged", "jfa_decode_num_splits", "timing", "JfaError", "load"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None or t.numel() == 0 else t.data_ptr()
+
+
+def _stream():
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check_bf16(name, t, ndim):
+    torch = _torch()
+    if t.dtype != torch.bfloat16 or t.dim() != ndim or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous bfloat16 CUDA tensor with {ndim} dims, got "
+                         f"{t.dtype} {tuple(t.shape)} cuda={t.is_cuda} contiguous={t.is_contiguous()}")
+
+
+def _check_i32(name, t):
+    torch = _torch()
+    if t.dtype != torch.int32 or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous int32 CUDA tensor")
+
+
+def _attn_params(q, k, cu_q, cu_k, max_q, max_k, causal, scale, broadcast_q, batch):
+    nb = batch if batch is not None else (cu_k.numel() - 1)
+    return AttnParams(
+        batch=nb, num_heads_q=q.shape[1], num_heads_kv=k.shape[1], head_dim=q.shape[2],
+        total_q=q.shape[0], total_k=k.shape[0], max_seqlen_q=int(max_q), max_seqlen_k=int(max_k),
+        causal=int(bool(causal)), broadcast_q=int(bool(broadcast_q)),
+        softmax_scale=float(scale) if scale is not None else 0.0)
+
+
+def jfa_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+            causal: bool = False, softmax_scale: Optional[float] = None, broadcast_q: bool = False,
+            out=None, lse=None, workspace=None):
+    """Jagged forward.  Self-attention: q [Tq,Hq,d], k/v [Tk,Hkv,d] -> o [Tq,Hq,d], lse [Hq,Tq].
+    Broadcast-Q: q [Nq,Hq,d] shared by B items -> o [B,Nq,Hq,d], lse [B,Hq,Nq]."""
+    torch = _torch()
+    lib = load()
+    _check_bf16("q", q, 3); _check_bf16("k", k, 3); _check_bf16("v", v, 3)
+    _check_i32("cu_seqlens_k", cu_seqlens_k)
+    if not broadcast_q:
+        _check_i32("cu_seqlens_q", cu_seqlens_q)
+    nb = cu_seqlens_k.numel() - 1
+    p = _attn_params(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, causal, softmax_scale,
+                     broadcast_q, nb)
+    if broadcast_q:
+        o_shape, lse_shape = (nb, q.shape[0], q.shape[1], q.shape[2]), (nb, q.shape[1], q.shape[0])
+    else:
+        o_shape, lse_shape = tuple(q.shape), (q.shape[1], q.shape[0])
+    o = out if out is not None else torch.empty(o_shape, dtype=torch.bfloat16, device=q.device)
+    l = lse if lse is not None else torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+    need = lib.jfa_fwd_workspace_size(ctypes.byref(p))
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib.jfa_fwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v),
+                     None if broadcast_q else _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                     _ptr(o), _ptr(l), ws.data_ptr(), ws.numel(), _stream())
+    _lib.check(st, "jfa_fwd")
+    return o, l
+
+
+def jfa_bwd(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+            causal: bool = False, softmax_scale: Optional[float] = None, broadcast_q: bool = False,
+            dq=None, dk=None, dv=None, workspace=None):
+    """Jagged backward: returns (dq, dk, dv) in the layouts of q, k, v."""
+    torch = _torch()
+    lib = load()
+    for n, t in (("q", q), ("k", k), ("v", v)):
+        _check_bf16(n, t, 3)
+    _check_bf16("o", o, 4 if broadcast_q else 3)
+    _check_bf16("dout", dout, 4 if broadcast_q else 3)
+    if lse.dtype != torch.float32 or not lse.is_contiguous():
+        raise ValueError("lse: expected contiguous float32")
+    nb = cu_seqlens_k.numel() - 1
+    p = _attn_params(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, causal, softmax_scale,
+                     broadcast_q, nb)
+    dq = dq if dq is not None else torch.empty_like(q)
+    dk = dk if dk is not None else torch.empty_like(k)
+    dv = dv if dv is not None else torch.empty_like(v)
+    need = lib.jfa_bwd_workspace_size(ctypes.byref(p))
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib.jfa_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(dout),
+                     None if broadcast_q else _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+                     _ptr(dq), _ptr(dk), _ptr(dv), ws.data_ptr(), ws.numel(), _stream())
+    _lib.check(st, "jfa_bwd")
+    return dq, dk, dv
+
+
+def _decode_params(q, k_cache, page_table, num_splits, scale):
+    return DecodeParams(
+        batch=q.shape[0], num_heads_q=q.shape[1], num_heads_kv=k_cache.shape[2], head_dim=q.shape[2],
+        page_size=k_cache.shape[1], num_pages=k_cache.shape[0], max_pages_per_seq=page_table.shape[1],
+        num_splits=int(num_splits), softmax_scale=float(scale) if scale is not None else 0.0)
+
+
+def jfa_decode_num_splits(q, k_cache, page_table, num_splits: int = 0) -> int:
+    p = _decode_params(q, k_cache, page_table, num_splits, None)
+    return int(load().jfa_decode_num_splits(ctypes.byref(p)))
+
+
+def jfa_decode_paged(q, k_cache, v_cache, page_table, seqlens_k, num_splits: int = 0,
+                     softmax_scale: Optional[float] = None, out=None, lse=None, workspace=None):
+    """Paged decode: q [B,Hq,d], caches [num_pages,page_size,Hkv,d] -> o [B,Hq,d], lse [B,Hq]."""
+    torch = _torch()
+    lib = load()
+    _check_bf16("q", q, 3); _check_bf16("k_cache", k_cache, 4); _check_bf16("v_cache", v_cache, 4)
+    _check_i32("page_table", page_table); _check_i32("seqlens_k", seqlens_k)
+    p = _decode_params(q, k_cache, page_table, num_splits, softmax_scale)
+    o = out if out is not None else torch.empty_like(q)
+    l = lse if lse is not None else torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=q.device)
+    need = lib.jfa_decode_workspace_size(ctypes.byref(p))
+    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    st = lib.jfa_decode_paged(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+                              _ptr(seqlens_k), _ptr(o), _ptr(l), ws.data_ptr(), ws.numel(), _stream())
+    _lib.check(st, "jfa_decode_paged")
+    return o, l
+
+
+class timing:
+    """Kernel timing through the library's own HIP events (see jfa_timing_enable)."""
+
+    @staticmethod
+    def enable(on: bool = True) -> None:
+        _lib.check(load().jfa_timing_enable(int(on)), "jfa_timing_enable")
+
+    @staticmethod
+    def collect():
+        """Returns {'fwd': (total_ms, count), 'bwd': ..., 'decode': ...} and clears the record."""
+        ms = (ctypes.c_double * 3)()
+        cnt = (ctypes.c_int64 * 3)()
+        _lib.check(load().jfa_timing_collect(ms, cnt), "jfa_timing_collect")
+        return {name: (ms[i], cnt[i]) for i, name in enumerate(("fwd", "bwd", "decode"))}
+
+
+def default_scale(head_dim: int, softmax_scale: Optional[float] = None) -> float:
+    return softmax_scale if softmax_scale and softmax_scale > 0 else 1.0 / math.sqrt(head_dim)

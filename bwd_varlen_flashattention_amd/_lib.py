@@ -1,0 +1,110 @@
+"""ctypes loader for libjfa.so and the C structs of include/jfa.h.
+
+The library is built in-tree by ``bwd_varlen_flashattention_amd.build``.  There
+is no fallback: if the library is missing or fails to load, importing the
+binding raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libjfa.so")
+
+JFA_OK = 0
+JFA_ERR_INVALID_ARGUMENT = 1
+JFA_ERR_UNSUPPORTED = 2
+JFA_ERR_WORKSPACE_TOO_SMALL = 3
+JFA_ERR_HIP = 4
+
+# every symbol include/jfa.h declares
+EXPORTS = (
+    "jfa_fwd_workspace_size", "jfa_fwd", "jfa_bwd_workspace_size", "jfa_bwd",
+    "jfa_decode_workspace_size", "jfa_decode_paged", "jfa_decode_num_splits",
+    "jfa_status_string", "jfa_abi_version", "jfa_timing_enable", "jfa_timing_collect",
+)
+
+
+class AttnParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_heads_q", ctypes.c_int32),
+        ("num_heads_kv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("total_q", ctypes.c_int32),
+        ("total_k", ctypes.c_int32),
+        ("max_seqlen_q", ctypes.c_int32),
+        ("max_seqlen_k", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
+        ("broadcast_q", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+
+class DecodeParams(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32),
+        ("num_heads_q", ctypes.c_int32),
+        ("num_heads_kv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int32),
+        ("max_pages_per_seq", ctypes.c_int32),
+        ("num_splits", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+
+class JfaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where} failed: {status_string(status)} ({status})")
+
+
+_lib = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libjfa.so once; raise if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run `python -m bwd_varlen_flashattention_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, sz, i32p = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p
+    ap, dp = ctypes.POINTER(AttnParams), ctypes.POINTER(DecodeParams)
+    lib.jfa_fwd_workspace_size.argtypes = [ap]
+    lib.jfa_fwd_workspace_size.restype = sz
+    lib.jfa_fwd.argtypes = [ap, vp, vp, vp, i32p, i32p, vp, vp, vp, sz, vp]
+    lib.jfa_fwd.restype = ctypes.c_int
+    lib.jfa_bwd_workspace_size.argtypes = [ap]
+    lib.jfa_bwd_workspace_size.restype = sz
+    lib.jfa_bwd.argtypes = [ap, vp, vp, vp, vp, vp, vp, i32p, i32p, vp, vp, vp, vp, sz, vp]
+    lib.jfa_bwd.restype = ctypes.c_int
+    lib.jfa_decode_workspace_size.argtypes = [dp]
+    lib.jfa_decode_workspace_size.restype = sz
+    lib.jfa_decode_num_splits.argtypes = [dp]
+    lib.jfa_decode_num_splits.restype = ctypes.c_int32
+    lib.jfa_decode_paged.argtypes = [dp, vp, vp, vp, i32p, i32p, vp, vp, vp, sz, vp]
+    lib.jfa_decode_paged.restype = ctypes.c_int
+    lib.jfa_status_string.argtypes = [ctypes.c_int]
+    lib.jfa_status_string.restype = ctypes.c_char_p
+    lib.jfa_abi_version.argtypes = []
+    lib.jfa_abi_version.restype = ctypes.c_int
+    lib.jfa_timing_enable.argtypes = [ctypes.c_int]
+    lib.jfa_timing_enable.restype = ctypes.c_int
+    lib.jfa_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    lib.jfa_timing_collect.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().jfa_status_string(int(status)).decode()
+
+
+def check(status: int, where: str) -> None:
+    if status != JFA_OK:
+        raise JfaError(status, where)

@@ -1,0 +1,75 @@
+// Device-side helpers shared by the gfx950 kernels of libjfa.
+//
+// MFMA lane layouts used throughout (checked on gfx950 with an in-bounds probe):
+//   v_mfma_f32_32x32x16_bf16  A[m][k]: lane l holds row m = l%32 and 8 k-slots
+//                             (half h = l/32, element j);  B[k][n]: column n = l%32,
+//                             the same (h, j) k-slots;  C[m][n]: lane l, register r
+//                             holds m = 8*(r/4) + 4*(l/32) + r%4, n = l%32.
+//   Which logical k sits in slot (h, j) is the caller's choice as long as A and B
+//   agree, so a C tile can feed the next contraction straight from registers.
+//   ds_read_tr16_b64: inside each 16-lane group, lane i supplies an address of
+//   four 16-bit values; call them M[i][0..3].  Lane i receives M[4e + i/4][i%4]
+//   for e = 0..3.  With lane i pointing at row (r0 + i/4), column (c0 + 4*(i%4))
+//   of a row-major bf16 tile, lane i receives the column c0 + i, rows r0..r0+3:
+//   a transposed 4x16 read.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace jfa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+#define JFA_LDS __attribute__((address_space(3)))
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Transposed 4x16 read of a row-major bf16 tile in LDS (see the layout note above).
+__device__ __forceinline__ bf16x4 lds_read_tr4(const __bf16* p) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((JFA_LDS s16x4*)(p));
+  return __builtin_bit_cast(bf16x4, r);
+}
+
+__device__ __forceinline__ bf16x8 cat8(bf16x4 a, bf16x4 b) {
+  return __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Reductions across the two 32-lane halves of a wave: permlane32_swap(x, x)
+// leaves {x[l], x[l^32]} in the pair (order depends on the half), so one
+// combine of the pair gives the cross-half result in every lane.
+__device__ __forceinline__ float xhalf_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ bf16x8 to_bf16x8(const float* s) {
+  bf16x8 r;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)s[i];
+  return r;
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8() {
+  return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+}
+
+__device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+}  // namespace jfa

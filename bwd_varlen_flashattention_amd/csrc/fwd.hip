@@ -1,0 +1,266 @@
+// Jagged FlashAttention forward for gfx950.
+//
+// What is computed: for each packed sequence (or broadcast-Q item) and query head,
+// O = softmax(Q K^T * scale) V and the natural-log LSE of the scaled scores,
+// tiled along the key axis with an online softmax so that neither padding nor the
+// score matrix ever reaches memory ("Optimizing Jagged Flash Attention with TLX",
+// third paragraph; the tiling recap of "Cutting edge isn't plug-and-play:
+// customising FlashAttention-4 on B300").
+//
+// How it maps to CDNA4:
+//   * persistent workgroups pull (sequence, 128-row query tile, head) items from
+//     the cost-sorted list built by sched.hip;
+//   * 4 waves, each owning 32 query rows whose Q fragment stays in VGPRs for the
+//     whole key loop;
+//   * K/V tiles of 64 keys are double-buffered in LDS: the global loads of tile
+//     j+1 are in flight while tile j is consumed;
+//   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 so each lane owns one query column:
+//     the row max/sum reductions are in-lane plus one permlane32 swap;
+//   * the S^T accumulator, rounded to bf16, is directly the B operand of
+//     O^T += V^T P^T, whose A operand comes from row-major V in LDS through the
+//     transposed read ds_read_b64_tr_b16;
+//   * the key loop is split into a branch-free bulk and masked tail/diagonal tiles
+//     (loop peeling, TLX page fifth paragraph);
+//   * the running max is only moved (and the accumulator rescaled) when it grows
+//     by more than 2^8, which keeps the result exact because the final
+//     normalisation uses the same stale max.
+#include "jfa_internal.h"
+#include "device_common.h"
+
+namespace jfa {
+
+template <int D>
+struct FwdTile {
+  static constexpr int NT = 256;            // 4 waves
+  static constexpr int BM = 128;            // query rows per item (32 per wave)
+  static constexpr int BN = 64;             // keys per KV tile
+  static constexpr int KP = D + 8;          // K row pitch in LDS (elements): +16 B staggers banks
+  static constexpr int VP = D + 16;         // V row pitch: +32 B keeps the 4-row transposed reads apart
+  static constexpr int CH = D / 8;          // 16-byte chunks per row
+  static constexpr int LOADS = BN * CH / NT;
+  static constexpr int KS = D / 16;         // k-steps of K Q^T
+  static constexpr int DB = D / 32;         // 32-wide output column blocks
+  static_assert(BN * CH % NT == 0, "tile load split");
+};
+
+constexpr float kRescaleThreshold = 8.0f;   // log2 units
+
+template <int D, bool CAUSAL, bool BCAST>
+__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
+  using T = FwdTile<D>;
+  constexpr int BM = T::BM, BN = T::BN, KP = T::KP, VP = T::VP, KS = T::KS, DB = T::DB;
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][BN * KP];
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds[2][BN * VP];
+  __shared__ int s_item;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const int g16 = lane >> 4, i16 = lane & 15;
+  const int n_items = *a.n_entries * a.hq;
+  const float NEG_INF = -__builtin_inff();
+
+  for (;;) {
+    if (tid == 0) s_item = (int)atomicAdd(a.counter, 1u);
+    __syncthreads();
+    const int item = s_item;
+    if (item >= n_items) break;
+    const WorkEntry e = a.entries[item / a.hq];
+    const int h = item % a.hq;
+    const int g = h / a.group;
+    const int b = e.b;
+
+    int lq, q_base;
+    if (BCAST) { lq = a.bcast_nq; q_base = 0; }
+    else { q_base = a.cu_q[b]; lq = a.cu_q[b + 1] - q_base; }
+    const int k_base = a.cu_k[b];
+    const int lk = a.cu_k[b + 1] - k_base;
+    const int row0 = e.t * BM;
+    const int my_row = row0 + w * 32 + l32;
+    const bool row_ok = my_row < lq;
+    const int off = lk - lq;                 // bottom-right causal alignment
+
+    // Q fragment: B operand of S^T = K Q^T, lane holds row my_row, d-slots 16*ks + 8*hh + 0..7
+    bf16x8 qf[KS];
+    {
+      const __bf16* qp = a.q + ((int64_t)(q_base + my_row) * a.hq + h) * D + 8 * hh;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks)
+        qf[ks] = row_ok ? *(const bf16x8*)(qp + 16 * ks) : zero_bf16x8();
+    }
+
+    int n_tiles, n_bulk;
+    if (CAUSAL) {
+      const int kmax = min(lk, row0 + BM + off);
+      n_tiles = kmax > 0 ? cdiv(kmax, BN) : 0;
+      const int full = min(lk, row0 + off + 1);
+      n_bulk = full > 0 ? full / BN : 0;
+    } else {
+      n_tiles = cdiv(lk, BN);
+      n_bulk = lk / BN;
+    }
+
+    f32x16 acc[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+    float m_run = NEG_INF, l_run = 0.f;
+
+    u32x4 kr[T::LOADS], vr[T::LOADS];
+    auto load_regs = [&](int j) {
+#pragma unroll
+      for (int i = 0; i < T::LOADS; ++i) {
+        const int id = tid + i * T::NT;
+        const int r = id / T::CH, c = id % T::CH;
+        const int key = min(j * BN + r, lk - 1);     // clamp: rows past the end are masked later
+        const int64_t goff = ((int64_t)(k_base + key) * a.hkv + g) * D + c * 8;
+        kr[i] = *(const u32x4*)(a.k + goff);
+        vr[i] = *(const u32x4*)(a.v + goff);
+      }
+    };
+    auto store_lds = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < T::LOADS; ++i) {
+        const int id = tid + i * T::NT;
+        const int r = id / T::CH, c = id % T::CH;
+        *(u32x4*)&k_lds[buf][r * KP + c * 8] = kr[i];
+        *(u32x4*)&v_lds[buf][r * VP + c * 8] = vr[i];
+      }
+    };
+
+    if (n_tiles > 0) {
+      load_regs(0);
+      store_lds(0);
+      __syncthreads();
+    }
+
+    for (int j = 0; j < n_tiles; ++j) {
+      const int buf = j & 1;
+      if (j + 1 < n_tiles) load_regs(j + 1);
+
+      // S^T[key][query] for two 32-key blocks
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+        const __bf16* kp = &k_lds[buf][(32 * kb + l32) * KP + 8 * hh];
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks)
+          s[kb] = mfma32x32x16(*(const bf16x8*)(kp + 16 * ks), qf[ks], s[kb]);
+      }
+
+      if (j >= n_bulk) {   // tail tile (keys past Lk) or causal diagonal tile
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = j * BN + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+            bool ok = key < lk;
+            if (CAUSAL) ok = ok && key <= my_row + off;
+            s[kb][r] = ok ? s[kb][r] : NEG_INF;
+          }
+      }
+
+      float mx = NEG_INF;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+      mx = xhalf_max(mx);
+      const float m_new = fmaxf(m_run, mx * a.scale_log2);
+      const bool need = m_new > m_run + kRescaleThreshold;
+      if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        const float alpha = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run - m_new);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] *= alpha;
+        l_run *= alpha;
+        m_run = m_new;
+      }
+      const float m_sub = (m_run == NEG_INF) ? 0.f : m_run;
+
+      float psum = 0.f;
+      bf16x8 pb[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        float pv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          pv[r] = fast_exp2(fmaf(s[kb][r], a.scale_log2, -m_sub));
+          psum += pv[r];
+        }
+        pb[kb][0] = to_bf16x8(pv);
+        pb[kb][1] = to_bf16x8(pv + 8);
+      }
+      l_run += psum;
+
+      // O^T[d][query] += V^T[d][key] P^T[key][query]
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const int n0 = 32 * db + 16 * (g16 & 1);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int k0 = 32 * kb + 16 * t + 4 * (g16 >> 1);
+            const __bf16* vp = &v_lds[buf][(k0 + (i16 >> 2)) * VP + n0 + 4 * (i16 & 3)];
+            const bf16x8 va = cat8(lds_read_tr4(vp), lds_read_tr4(vp + 8 * VP));
+            acc[db] = mfma32x32x16(va, pb[kb][t], acc[db]);
+          }
+      }
+
+      if (j + 1 < n_tiles) store_lds(buf ^ 1);
+      __syncthreads();
+    }
+
+    // epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
+    const float l_tot = xhalf_sum(l_run);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (row_ok) {
+      __bf16* op = BCAST ? a.o + (((int64_t)b * lq + my_row) * a.hq + h) * D
+                         : a.o + ((int64_t)(q_base + my_row) * a.hq + h) * D;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          bf16x4 ov;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) ov[x] = (__bf16)(acc[db][4 * r4 + x] * inv);
+          *(bf16x4*)(op + 32 * db + 8 * r4 + 4 * hh) = ov;
+        }
+      if (hh == 0) {
+        const float m_sub = (m_run == NEG_INF) ? 0.f : m_run;
+        const float lse = l_tot > 0.f ? (m_sub + __log2f(l_tot)) * kLn2 : NEG_INF;
+        const int64_t li = BCAST ? ((int64_t)b * a.hq + h) * lq + my_row
+                                 : (int64_t)h * a.total_q + q_base + my_row;
+        a.lse[li] = lse;
+      }
+    }
+    __syncthreads();   // s_item and the LDS buffers are reused by the next item
+  }
+}
+
+int fwd_block_rows() { return FwdTile<128>::BM; }
+int fwd_kv_tile() { return FwdTile<128>::BN; }
+int fwd_blocks_per_cu(int) { return 2; }
+
+template <int D>
+static hipError_t launch_fwd_d(const FwdArgs& a, int grid, hipStream_t stream) {
+  const dim3 g(grid), blk(FwdTile<D>::NT);
+  if (a.bcast_nq > 0)
+    hipLaunchKernelGGL((fwd_kernel<D, false, true>), g, blk, 0, stream, a);
+  else if (a.causal)
+    hipLaunchKernelGGL((fwd_kernel<D, true, false>), g, blk, 0, stream, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<D, false, false>), g, blk, 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_fwd_d<64>(a, grid, stream);
+    case 96: return launch_fwd_d<96>(a, grid, stream);
+    case 128: return launch_fwd_d<128>(a, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace jfa

@@ -1,0 +1,129 @@
+// Internal (host-side) interface between the C ABI layer and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace jfa {
+
+// One work-list entry: (sequence or item b, tile index t along the stationary axis).
+struct WorkEntry {
+  int32_t b;
+  int32_t t;
+};
+
+// Shape of the cost-sorted work list built on the device from the offsets.
+struct SchedArgs {
+  const int32_t* cu_q;      // [B+1] (unused in broadcast-Q mode)
+  const int32_t* cu_k;      // [B+1]
+  int32_t batch;
+  int32_t stat_tile;        // rows per tile on the stationary axis
+  int32_t loop_tile;        // rows per tile on the inner-loop axis
+  int32_t mode;             // 0: query-stationary (forward), 1: key-stationary (backward)
+  int32_t causal;
+  int32_t bcast_nq;         // > 0: broadcast-Q, every item has Lq = bcast_nq
+  int32_t n_buckets;        // cost buckets (costs above are clamped into the last one)
+  int32_t max_entries;      // capacity of `entries`
+  WorkEntry* entries;       // sorted by cost, longest first
+  int32_t* n_entries;       // number of valid entries
+  uint32_t* counter;        // reset to 0 for the persistent consumers
+};
+
+hipError_t launch_sched(const SchedArgs& a, hipStream_t stream);
+
+// Forward kernel arguments.
+struct FwdArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  __bf16* o;
+  float* lse;
+  const WorkEntry* entries;
+  const int32_t* n_entries;
+  uint32_t* counter;
+  int32_t hq, hkv, group;   // group = hq / hkv
+  int32_t bcast_nq;         // > 0: broadcast-Q
+  int32_t total_q;          // LSE row stride for self-attention
+  int32_t causal;
+  float scale_log2;         // softmax scale * log2(e)
+};
+
+hipError_t launch_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t stream);
+int fwd_block_rows();       // BM of the forward kernel
+int fwd_kv_tile();          // BN of the forward kernel
+int fwd_blocks_per_cu(int head_dim);
+
+// Backward.
+struct BwdPreArgs {
+  const __bf16* o;
+  const __bf16* dout;
+  float* delta;             // same layout as lse
+  float* dq_acc;            // fp32, same element count as dq; zeroed here
+  int64_t rows;             // rows of o / dout (self: total_q, broadcast: B * Nq)
+  int32_t hq;
+  int32_t head_dim;
+  int32_t lse_cols;         // self: total_q; broadcast: Nq
+  int32_t bcast;
+  int64_t dq_elems;
+};
+hipError_t launch_bwd_pre(const BwdPreArgs& a, hipStream_t stream);
+
+struct BwdArgs {
+  const __bf16* q;
+  const __bf16* k;
+  const __bf16* v;
+  const __bf16* dout;
+  const float* lse;
+  const float* delta;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  float* dq_acc;
+  __bf16* dk;
+  __bf16* dv;
+  const WorkEntry* entries;
+  const int32_t* n_entries;
+  uint32_t* counter;
+  int32_t hq, hkv, group;
+  int32_t bcast_nq;
+  int32_t total_q;
+  int32_t causal;
+  float scale;
+  float scale_log2;
+};
+hipError_t launch_bwd(const BwdArgs& a, int head_dim, int grid, hipStream_t stream);
+int bwd_block_rows();       // query rows per inner step
+int bwd_kv_tile();          // keys per workgroup
+int bwd_blocks_per_cu(int head_dim);
+
+struct DqConvertArgs {
+  const float* dq_acc;
+  __bf16* dq;
+  int64_t n;                // elements
+  float scale;
+};
+hipError_t launch_dq_convert(const DqConvertArgs& a, hipStream_t stream);
+
+// Decode.
+struct DecodeArgs {
+  const __bf16* q;
+  const __bf16* k_cache;
+  const __bf16* v_cache;
+  const int32_t* page_table;
+  const int32_t* seqlens;
+  __bf16* o;                // final output when splits == 1
+  float* lse;
+  float* o_part;            // [splits, B, Hq, d] when splits > 1
+  float* lse_part;          // [splits, B, Hq]
+  int32_t batch, hq, hkv, group;
+  int32_t page_size;
+  int32_t max_pages;
+  int32_t splits;
+  float scale_log2;
+};
+hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t stream);
+hipError_t launch_decode_combine(const DecodeArgs& a, int head_dim, hipStream_t stream);
+int decode_chunk_align();
+
+}  // namespace jfa

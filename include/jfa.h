@@ -1,0 +1,194 @@
+/*
+ * jfa.h -- C ABI of libjfa.so: exact jagged (packed variable-length) FlashAttention
+ * forward and backward, and split-KV paged decode, for AMD MI355X (gfx950).
+ *
+ * Sources of the operations (page title, then section):
+ *   - "Optimizing Jagged Flash Attention with TLX: The Road Toward SOTA FA4 on
+ *     Blackwell": attention over jagged user sequences packed contiguously with
+ *     their boundaries in an offsets tensor, no padded tokens materialised; the
+ *     broadcast-Q production case in which one dense Q serves the whole batch and
+ *     dQ is summed over the batch (third paragraph); persistent passes, load
+ *     balancing of jagged tiles, bulk + masked-tail KV loop (fourth and fifth).
+ *   - "Cutting edge isn't plug-and-play: customising FlashAttention-4 on B300":
+ *     the tiled forward with saved LSE and the backward that rebuilds P from the
+ *     saved LSE and uses delta, dP and dS (Flash Attention recap; Phase 2
+ *     chunked-backward pseudocode and buffer list); unsupported head dims must not
+ *     end in an assertion (the March 2026 head-dim support remark).
+ *   - "Optimizing FlashAttention-4 for Efficient Inference": decode with
+ *     parallelism over the KV dimension (PR 1940), arbitrary KV page sizes with a
+ *     page table (PR 1999 / PR 2104), only real query rows in the tile (PR 1993)
+ *     and GQA packing of the query heads that share a KV head (PR 2186).
+ *
+ * Conventions shared by every entry point
+ *   - Every tensor pointer is a DEVICE pointer to contiguous row-major memory in
+ *     the layout stated, aligned to 16 bytes.  bf16 tensors are passed as void*.
+ *   - The caller owns all memory (inputs, outputs, workspace).  The library
+ *     allocates no device memory and keeps no state beyond a per-device cache of
+ *     the compute-unit count.  Calls with distinct workspaces may run
+ *     concurrently on different streams.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
+ *     runs asynchronously: no call synchronises with the host.
+ *   - Outputs are fully overwritten, never accumulated into.
+ *   - Host-checkable errors are returned before anything is launched.  The
+ *     library never aborts, throws or prints.  A failed launch returns
+ *     JFA_ERR_HIP.
+ *   - Device contents are the caller's contract and are not checked: offsets
+ *     start at 0, do not decrease and end at the packed total; page ids are
+ *     < num_pages; seqlens_k[b] <= max_pages_per_seq * page_size.
+ *   - Sequences (or items) of length 0 are legal.  A query row that sees no key
+ *     gets O = 0 and LSE = -inf, and contributes no gradient.
+ */
+#ifndef JFA_H
+#define JFA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define JFA_ABI_VERSION 1
+
+/* Same type as hipStream_t, declared without including the HIP headers. */
+struct ihipStream_t;
+typedef struct ihipStream_t* jfa_stream_t;
+
+typedef enum {
+  JFA_OK = 0,
+  JFA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, Hq % Hkv != 0, ... */
+  JFA_ERR_UNSUPPORTED = 2,        /* head_dim outside {64, 96, 128}, causal broadcast-Q, ... */
+  JFA_ERR_WORKSPACE_TOO_SMALL = 3,
+  JFA_ERR_HIP = 4                 /* a HIP call or kernel launch failed */
+} jfa_status_t;
+
+/*
+ * Problem description for jfa_fwd / jfa_bwd.
+ *
+ * Self-attention (broadcast_q = 0), B = batch sequences:
+ *   q, o, dout, dq   [total_q, Hq, d]   bf16, sequence b owns rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1
+ *   k, v, dk, dv     [total_k, Hkv, d]  bf16, rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1
+ *   lse              [Hq, total_q]      fp32, natural-log log-sum-exp of the scaled scores
+ * Broadcast-Q (broadcast_q = 1), B = batch items sharing one dense Q of Nq = total_q rows:
+ *   q, dq            [Nq, Hq, d]        dq = sum over all B items
+ *   k, v, dk, dv     [total_k, Hkv, d]  jagged by cu_seqlens_k
+ *   o, dout          [B, Nq, Hq, d]
+ *   lse              [B, Hq, Nq]
+ *   cu_seqlens_q is ignored (may be NULL); causal must be 0.
+ * Query head h uses KV head h / (Hq / Hkv) (grouped-query attention).
+ * Scores: S = Q K^T * scale with scale = softmax_scale, or 1/sqrt(d) when
+ * softmax_scale <= 0.  Causal masking is aligned bottom-right: key j is visible
+ * to query i of a sequence iff j <= i + (Lk - Lq).
+ */
+typedef struct {
+  int32_t batch;          /* B >= 1 */
+  int32_t num_heads_q;    /* Hq >= 1 */
+  int32_t num_heads_kv;   /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;       /* d in {64, 96, 128}; anything else is JFA_ERR_UNSUPPORTED */
+  int32_t total_q;        /* packed query rows (broadcast-Q: Nq) */
+  int32_t total_k;        /* packed key rows */
+  int32_t max_seqlen_q;   /* upper bound on any Lq (broadcast-Q: ignored, Nq is used) */
+  int32_t max_seqlen_k;   /* upper bound on any Lk; sizes the scheduler's cost buckets */
+  int32_t causal;         /* 0 or 1 */
+  int32_t broadcast_q;    /* 0 or 1 */
+  float softmax_scale;    /* <= 0 selects 1/sqrt(d) */
+} jfa_attn_params_t;
+
+/* Bytes of workspace jfa_fwd needs for this problem (0 if the params are invalid). */
+size_t jfa_fwd_workspace_size(const jfa_attn_params_t* p);
+
+/*
+ * Forward: O = softmax(S) V per sequence and head, plus LSE, with no score
+ * matrix or padding ever written to memory.  Work items (sequence, query tile,
+ * head) are listed on the device from the offsets, sorted by their KV-tile count
+ * (longest first) and pulled by persistent workgroups from an atomic counter.
+ * workspace: device memory of at least jfa_fwd_workspace_size(p) bytes, used
+ * only during this call (stream-ordered).
+ */
+jfa_status_t jfa_fwd(const jfa_attn_params_t* p,
+                     const void* q, const void* k, const void* v,
+                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                     void* o, float* lse,
+                     void* workspace, size_t workspace_bytes, jfa_stream_t stream);
+
+/* Bytes of workspace jfa_bwd needs (holds delta, an fp32 dQ accumulator and the work list). */
+size_t jfa_bwd_workspace_size(const jfa_attn_params_t* p);
+
+/*
+ * Backward: given q, k, v, the forward's o and lse, and dout, writes dq, dk, dv.
+ * P is rebuilt from lse; delta = rowsum(dout * o); dP = dout V^T;
+ * dS = P * (dP - delta); dV = P^T dout; dK = scale dS^T Q; dQ = scale dS K.
+ * dK/dV of a KV head sum over the Hq/Hkv query heads of its group.  dQ is
+ * reduced in fp32 with atomic adds (so its low bits depend on timing); in
+ * broadcast-Q mode it is the sum over all items.  Keys that no query sees get
+ * dK = dV = 0.
+ */
+jfa_status_t jfa_bwd(const jfa_attn_params_t* p,
+                     const void* q, const void* k, const void* v,
+                     const void* o, const float* lse, const void* dout,
+                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                     void* dq, void* dk, void* dv,
+                     void* workspace, size_t workspace_bytes, jfa_stream_t stream);
+
+/*
+ * Split-KV paged decode: one query token per sequence.
+ *   q           [B, Hq, d]                            bf16
+ *   k_cache,
+ *   v_cache     [num_pages, page_size, Hkv, d]        bf16
+ *   page_table  [B, max_pages_per_seq]                int32, physical page of each logical page
+ *   seqlens_k   [B]                                   int32, KV length of each sequence
+ *   o           [B, Hq, d]                            bf16
+ *   lse         [B, Hq]                               fp32, natural log
+ * Token t of sequence b lives in slot t % page_size of page
+ * page_table[b][t / page_size].  The Hq/Hkv query heads that share a KV head are
+ * processed together so every KV byte is read once.  Each sequence's tokens are
+ * cut into num_splits contiguous chunks processed in parallel; every chunk
+ * leaves a normalised partial output and its LSE, and a final pass merges them
+ * with weights exp(LSE_s - LSE).  num_splits = 0 picks a count from the problem
+ * size; 1 writes o/lse directly.
+ */
+typedef struct {
+  int32_t batch;              /* B >= 1 */
+  int32_t num_heads_q;        /* Hq >= 1 */
+  int32_t num_heads_kv;       /* Hkv >= 1, Hq % Hkv == 0, Hq / Hkv <= 16 */
+  int32_t head_dim;           /* d in {64, 96, 128} */
+  int32_t page_size;          /* >= 1, any value */
+  int32_t num_pages;          /* pages in the cache, >= 1 */
+  int32_t max_pages_per_seq;  /* columns of page_table, >= 1 */
+  int32_t num_splits;         /* 0 = automatic, else 1 .. 128 */
+  float softmax_scale;        /* <= 0 selects 1/sqrt(d) */
+} jfa_decode_params_t;
+
+size_t jfa_decode_workspace_size(const jfa_decode_params_t* p);
+
+jfa_status_t jfa_decode_paged(const jfa_decode_params_t* p,
+                              const void* q, const void* k_cache, const void* v_cache,
+                              const int32_t* page_table, const int32_t* seqlens_k,
+                              void* o, float* lse,
+                              void* workspace, size_t workspace_bytes, jfa_stream_t stream);
+
+/* The split count jfa_decode_paged uses for p (resolves num_splits = 0). */
+int32_t jfa_decode_num_splits(const jfa_decode_params_t* p);
+
+/* Static string naming a status code. */
+const char* jfa_status_string(jfa_status_t s);
+
+/* JFA_ABI_VERSION of the built library. */
+int jfa_abi_version(void);
+
+/*
+ * Optional kernel timing.  While enabled, every call records a pair of HIP
+ * events on its stream around the launch of its main kernel (the attention
+ * kernel of jfa_fwd, the main backward kernel of jfa_bwd, the split kernel of
+ * jfa_decode_paged).  jfa_timing_collect() waits for the recorded events, adds
+ * their elapsed milliseconds per entry point into total_ms[0..2] (fwd, bwd,
+ * decode) and the number of launches into count[0..2], then releases them.
+ * Either output may be NULL.  Intended for benchmarks; off by default.
+ */
+jfa_status_t jfa_timing_enable(int enable);
+jfa_status_t jfa_timing_collect(double total_ms[3], int64_t count[3]);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* JFA_H */

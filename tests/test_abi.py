@@ -1,0 +1,122 @@
+"""C ABI checks that need no GPU: the library loads, exports every declared symbol,
+and rejects bad arguments with the documented status before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "jfa.h")
+
+
+def _lib():
+    from bwd_varlen_flashattention_amd import _lib as L
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libjfa.so is not built (run __graft_entry__.build())")
+    return L, L.load()
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(jfa_[a-z_0-9]+)\s*\(", text)) - {"jfa_status_t"})
+
+
+def test_header_declares_and_library_exports():
+    L, lib = _lib()
+    names = _declared()
+    assert "jfa_fwd" in names and "jfa_bwd" in names and "jfa_decode_paged" in names
+    for n in names:
+        assert hasattr(lib, n), f"missing export {n}"
+    assert set(names) == set(L.EXPORTS)
+    assert lib.jfa_abi_version() == 1
+
+
+def test_header_compiles_as_c(tmp_path):
+    src = tmp_path / "t.c"
+    src.write_text('#include "jfa.h"\nint main(void){ jfa_attn_params_t p; (void)p; return JFA_OK; }\n')
+    r = os.system(f"gcc -std=c99 -Wall -Werror -I {os.path.dirname(HEADER)} -c {src} -o {tmp_path / 't.o'}")
+    assert r == 0
+
+
+def _params(L, **kw):
+    base = dict(batch=2, num_heads_q=4, num_heads_kv=2, head_dim=128, total_q=10, total_k=10,
+                max_seqlen_q=5, max_seqlen_k=5, causal=0, broadcast_q=0, softmax_scale=0.0)
+    base.update(kw)
+    return L.AttnParams(**base)
+
+
+BAD = [
+    (dict(head_dim=80), 2), (dict(head_dim=256), 2), (dict(num_heads_q=3), 1), (dict(batch=0), 1),
+    (dict(total_q=-1), 1), (dict(causal=2), 1), (dict(broadcast_q=1, causal=1), 2),
+    (dict(softmax_scale=float("nan")), 1),
+]
+
+
+@pytest.mark.parametrize("kw,status", BAD)
+def test_invalid_attention_arguments(kw, status):
+    L, lib = _lib()
+    p = _params(L, **kw)
+    dummy = ctypes.c_void_p(16)
+    assert lib.jfa_fwd_workspace_size(ctypes.byref(p)) == 0
+    st = lib.jfa_fwd(ctypes.byref(p), dummy, dummy, dummy, dummy, dummy, dummy, dummy, dummy, 1 << 20, None)
+    assert st == status, L.status_string(st)
+    st = lib.jfa_bwd(ctypes.byref(p), dummy, dummy, dummy, dummy, dummy, dummy, dummy, dummy,
+                     dummy, dummy, dummy, dummy, 1 << 20, None)
+    assert st == status
+
+
+def test_null_pointers_and_small_workspace():
+    L, lib = _lib()
+    p = _params(L)
+    d = ctypes.c_void_p(16)
+    need = lib.jfa_fwd_workspace_size(ctypes.byref(p))
+    assert need > 0
+    assert lib.jfa_fwd(None, d, d, d, d, d, d, d, d, need, None) == L.JFA_ERR_INVALID_ARGUMENT
+    assert lib.jfa_fwd(ctypes.byref(p), None, d, d, d, d, d, d, d, need, None) == L.JFA_ERR_INVALID_ARGUMENT
+    assert lib.jfa_fwd(ctypes.byref(p), d, d, d, d, d, d, d, d, need - 1, None) == L.JFA_ERR_WORKSPACE_TOO_SMALL
+    nb = lib.jfa_bwd_workspace_size(ctypes.byref(p))
+    assert nb > 10 * 4 * 128 * 4      # holds at least the fp32 dQ accumulator
+    assert lib.jfa_bwd(ctypes.byref(p), d, d, d, d, d, d, d, d, d, d, d, d, nb - 1, None) == L.JFA_ERR_WORKSPACE_TOO_SMALL
+    assert lib.jfa_bwd(ctypes.byref(p), d, d, d, None, d, d, d, d, d, d, d, d, nb, None) == L.JFA_ERR_INVALID_ARGUMENT
+
+
+def test_empty_problem_is_a_no_op():
+    L, lib = _lib()
+    p = _params(L, total_q=0, total_k=0)
+    assert lib.jfa_fwd(ctypes.byref(p), None, None, None, None, None, None, None, None, 0, None) == L.JFA_OK
+
+
+DEC_BAD = [
+    (dict(page_size=0), 1), (dict(num_splits=129), 1), (dict(num_splits=-1), 1), (dict(head_dim=48), 2),
+    (dict(num_heads_q=34, num_heads_kv=2), 2), (dict(num_heads_q=30), 1), (dict(num_pages=0), 1),
+]
+
+
+@pytest.mark.parametrize("kw,status", DEC_BAD)
+def test_invalid_decode_arguments(kw, status):
+    L, lib = _lib()
+    base = dict(batch=2, num_heads_q=32, num_heads_kv=8, head_dim=128, page_size=16, num_pages=10,
+                max_pages_per_seq=5, num_splits=4, softmax_scale=0.0)
+    base.update(kw)
+    p = L.DecodeParams(**base)
+    d = ctypes.c_void_p(16)
+    assert lib.jfa_decode_paged(ctypes.byref(p), d, d, d, d, d, d, d, d, 1 << 20, None) == status
+
+
+def test_decode_workspace_query():
+    L, lib = _lib()
+    p = L.DecodeParams(batch=32, num_heads_q=32, num_heads_kv=8, head_dim=128, page_size=16, num_pages=100,
+                       max_pages_per_seq=1024, num_splits=4, softmax_scale=0.0)
+    assert lib.jfa_decode_workspace_size(ctypes.byref(p)) >= 4 * 32 * 32 * 129 * 4
+    p.num_splits = 1
+    assert lib.jfa_decode_workspace_size(ctypes.byref(p)) == 0
+    d = ctypes.c_void_p(16)
+    p.num_splits = 4
+    assert lib.jfa_decode_paged(ctypes.byref(p), d, d, d, d, d, d, d, d, 16, None) == L.JFA_ERR_WORKSPACE_TOO_SMALL
+
+
+def test_status_strings():
+    L, lib = _lib()
+    assert L.status_string(0) == "JFA_OK"
+    assert L.status_string(2) == "JFA_ERR_UNSUPPORTED"

@@ -1,0 +1,221 @@
+"""GPU parity: jagged forward and backward through the C ABI against the fp64 oracle."""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from parity import check_grad, check_lse, check_o, dev, host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def jfa():
+    import bwd_varlen_flashattention_amd as m
+    m.load()
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return m
+
+
+def _run_self(jfa, inp, scale=None):
+    q, k, v, do = (dev(x, torch) for x in (inp.q, inp.k, inp.v, inp.do))
+    cq, ck = dev(inp.cu_q, torch), dev(inp.cu_k, torch)
+    mq, mk = inp.max_len_q, inp.max_len_k
+    o, lse = jfa.jfa_fwd(q, k, v, cq, ck, mq, mk, inp.causal, scale)
+    dq, dk, dv = jfa.jfa_bwd(q, k, v, o, lse, do, cq, ck, mq, mk, inp.causal, scale)
+    torch.cuda.synchronize()
+    return host(o), host(lse), host(dq), host(dk), host(dv)
+
+
+def _oracle_self(inp, scale=None, seqs=None):
+    """Oracle outputs; with `seqs`, only for those sequences (a sample the oracle computes one by one)."""
+    q, k, v, do = inp.q, inp.k, inp.v, inp.do
+    if seqs is None:
+        f = lambda x: x.astype(np.float64)
+        o, lse = oracle.attention_forward(f(q), f(k), f(v), inp.cu_q, inp.cu_k, inp.causal, scale)
+        dq, dk, dv = oracle.attention_backward(f(q), f(k), f(v), f(do), inp.cu_q, inp.cu_k, inp.causal, scale)
+        return o, lse, dq, dk, dv
+    out = {}
+    for b in seqs:
+        qs, qe, ks, ke = inp.cu_q[b], inp.cu_q[b + 1], inp.cu_k[b], inp.cu_k[b + 1]
+        cq, ck = np.array([0, qe - qs]), np.array([0, ke - ks])
+        args = [x.astype(np.float64) for x in (q[qs:qe], k[ks:ke], v[ks:ke])]
+        o, lse = oracle.attention_forward(*args, cq, ck, inp.causal, scale)
+        dq, dk, dv = oracle.attention_backward(*args, do[qs:qe].astype(np.float64), cq, ck, inp.causal, scale)
+        out[b] = (o, lse, dq, dk, dv)
+    return out
+
+
+def _compare_full(got, ref):
+    o, lse, dq, dk, dv = got
+    ro, rl, rdq, rdk, rdv = ref
+    eo = check_o(o, ro)
+    el = check_lse(lse, rl)
+    e = [check_grad(dq, rdq, "dQ"), check_grad(dk, rdk, "dK"), check_grad(dv, rdv, "dV")]
+    _say(f"  O max-abs {eo:.2e}  LSE {el:.2e}  dQ/dK/dV rel-L2 {e[0]:.2e} {e[1]:.2e} {e[2]:.2e}")
+
+
+def _compare_sampled(inp, got, ref):
+    o, lse, dq, dk, dv = got
+    for b, (ro, rl, rdq, rdk, rdv) in ref.items():
+        qs, qe, ks, ke = inp.cu_q[b], inp.cu_q[b + 1], inp.cu_k[b], inp.cu_k[b + 1]
+        check_o(o[qs:qe], ro, f"O[seq {b}]")
+        check_lse(lse[:, qs:qe], rl, f"LSE[seq {b}]")
+        check_grad(dq[qs:qe], rdq, f"dQ[seq {b}]")
+        check_grad(dk[ks:ke], rdk, f"dK[seq {b}]")
+        check_grad(dv[ks:ke], rdv, f"dV[seq {b}]")
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tiny(jfa, seed):
+    inp = workloads.tiny(seed)
+    _say(f"tiny seed={seed} lengths={list(np.diff(inp.cu_q))}")
+    _compare_full(_run_self(jfa, inp), _oracle_self(inp))
+
+
+RAGGED = [1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200, 0, 257, 5]
+
+
+@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2), (3, 1)])
+def test_ragged(jfa, d, causal, hq, hkv):
+    inp = workloads.jagged(100 + d, RAGGED, None, hq, hkv, d, causal)
+    _say(f"ragged d={d} causal={causal} hq={hq} hkv={hkv}")
+    _compare_full(_run_self(jfa, inp), _oracle_self(inp))
+
+
+def test_cross_lengths_bottom_right_causal(jfa):
+    """Lq != Lk per sequence, causal aligned bottom-right (rows with no key get O=0, LSE=-inf)."""
+    lq = [5, 130, 64, 1, 77, 300]
+    lk = [9, 64, 200, 0, 77, 129]
+    for causal in (False, True):
+        inp = workloads.jagged(7, lq, lk, 4, 2, 128, causal)
+        _say(f"cross lengths causal={causal}")
+        _compare_full(_run_self(jfa, inp), _oracle_self(inp))
+
+
+def test_explicit_scale(jfa):
+    inp = workloads.jagged(8, [70, 129], None, 2, 2, 64, False)
+    _compare_full(_run_self(jfa, inp, 0.3), _oracle_self(inp, 0.3))
+
+
+def test_outputs_overwritten(jfa):
+    """Outputs pre-filled with NaN must be fully overwritten (catches unwritten rows)."""
+    inp = workloads.jagged(9, [3, 130, 64, 0, 1], None, 4, 2, 64, True)
+    q, k, v, do = (dev(x, torch) for x in (inp.q, inp.k, inp.v, inp.do))
+    cq, ck = dev(inp.cu_q, torch), dev(inp.cu_k, torch)
+    o = torch.full_like(q, float("nan"))
+    lse = torch.full((4, q.shape[0]), float("nan"), device="cuda")
+    jfa.jfa_fwd(q, k, v, cq, ck, 130, 130, True, out=o, lse=lse)
+    dq, dk, dv = (torch.full_like(x, float("nan")) for x in (q, k, v))
+    jfa.jfa_bwd(q, k, v, o, lse, do, cq, ck, 130, 130, True, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    _compare_full((host(o), host(lse), host(dq), host(dk), host(dv)), _oracle_self(inp))
+
+
+@pytest.mark.parametrize("s", [0.9, 0.5, 0.1])
+def test_gem_full_size_sampled(jfa, s):
+    """GEM config at full size (256 sequences, 8 heads, d=128); oracle on a sample of sequences."""
+    inp = workloads.gem(0, s)
+    _say(f"gem s={s} T={inp.q.shape[0]}")
+    got = _run_self(jfa, inp)
+    lens = np.diff(inp.cu_q)
+    order = np.argsort(lens)
+    seqs = sorted(set(order[:3].tolist() + order[-3:].tolist() + [0, 1, 128, 255]))
+    _compare_sampled(inp, got, _oracle_self(inp, seqs=seqs))
+    assert np.isfinite(got[0]).all() and np.isfinite(got[2]).all()
+
+
+@pytest.mark.parametrize("d", [128, 96])
+def test_dense_causal_full_size_sampled(jfa, d):
+    """4 x 8192 causal, 32 heads, at full size; oracle on sequence 0, heads {0, 17, 31}."""
+    inp = workloads.dense_causal(0, head_dim=d)
+    _say(f"dense causal d={d}")
+    got = _run_self(jfa, inp)
+    L = 8192
+    for h in (0, 17, 31):
+        args = [x[:L, h:h + 1].astype(np.float64) for x in (inp.q, inp.k, inp.v)]
+        cu = np.array([0, L])
+        ro, rl = oracle.attention_forward(*args, cu, cu, True)
+        rdq, rdk, rdv = oracle.attention_backward(*args, inp.do[:L, h:h + 1].astype(np.float64), cu, cu, True)
+        check_o(got[0][:L, h:h + 1], ro, f"O[h{h}]")
+        check_lse(got[1][h:h + 1, :L], rl, f"LSE[h{h}]")
+        check_grad(got[2][:L, h:h + 1], rdq, f"dQ[h{h}]")
+        check_grad(got[3][:L, h:h + 1], rdk, f"dK[h{h}]")
+        check_grad(got[4][:L, h:h + 1], rdv, f"dV[h{h}]")
+        _say(f"  head {h} ok")
+
+
+def _run_bcast(jfa, inp):
+    q, k, v, do = (dev(x, torch) for x in (inp.q, inp.k, inp.v, inp.do))
+    ck = dev(inp.cu_k, torch)
+    nq = inp.q.shape[0]
+    o, lse = jfa.jfa_fwd(q, k, v, None, ck, nq, inp.max_len_k, False, None, broadcast_q=True)
+    dq, dk, dv = jfa.jfa_bwd(q, k, v, o, lse, do, None, ck, nq, inp.max_len_k, False, None, broadcast_q=True)
+    torch.cuda.synchronize()
+    return host(o), host(lse), host(dq), host(dk), host(dv)
+
+
+def _oracle_bcast(inp):
+    f = lambda x: x.astype(np.float64)
+    o, lse = oracle.broadcast_q_forward(f(inp.q), f(inp.k), f(inp.v), inp.cu_k)
+    dq, dk, dv = oracle.broadcast_q_backward(f(inp.q), f(inp.k), f(inp.v), f(inp.do), inp.cu_k)
+    return o, lse, dq, dk, dv
+
+
+@pytest.mark.parametrize("nq,lengths,hq,hkv", [
+    (37, [5, 0, 64, 129, 1], 2, 2),
+    (256, [300, 17, 0, 128, 64, 1000, 3], 4, 4),
+    (130, [70, 70, 200], 4, 2),
+])
+def test_broadcast_q(jfa, nq, lengths, hq, hkv):
+    inp = workloads.broadcast(3, nq, lengths, hq, hkv, 128)
+    _say(f"broadcast nq={nq} lengths={lengths}")
+    _compare_full(_run_bcast(jfa, inp), _oracle_bcast(inp))
+
+
+def test_broadcast_q_config_s09(jfa):
+    """Broadcast-Q config (Nq=256, 512 items, 4 heads, d=128) at sparsity 0.9, full tensors."""
+    inp = workloads.broadcast_q(0, 0.9)
+    _say(f"broadcast config s=0.9 Tk={inp.k.shape[0]}")
+    _compare_full(_run_bcast(jfa, inp), _oracle_bcast(inp))
+
+
+def test_broadcast_dq_is_sum_of_items(jfa):
+    """dQ of a broadcast batch equals the sum of the single-item runs (GPU against GPU)."""
+    inp = workloads.broadcast(4, 64, [40, 130, 7], 2, 2, 64)
+    full = _run_bcast(jfa, inp)
+    acc = np.zeros_like(full[2])
+    for b in range(3):
+        ks, ke = inp.cu_k[b], inp.cu_k[b + 1]
+        one = workloads.BroadcastInputs(inp.q, inp.k[ks:ke], inp.v[ks:ke], inp.do[b:b + 1],
+                                        np.array([0, ke - ks], np.int32))
+        acc += _run_bcast(jfa, one)[2]
+    assert np.abs(full[2] - acc).max() <= 2e-2 * max(1.0, np.abs(acc).max())
+
+
+def test_repeatability(jfa):
+    """Ten runs agree within tolerance (dQ atomics make the last bits order-dependent)."""
+    inp = workloads.jagged(12, [300, 129, 64], None, 4, 4, 128, False)
+    ref = _oracle_self(inp)
+    first = None
+    for _ in range(10):
+        got = _run_self(jfa, inp)
+        check_grad(got[2], ref[2], "dQ")
+        if first is None:
+            first = got
+        else:
+            np.testing.assert_array_equal(got[0], first[0])    # forward is deterministic
+            np.testing.assert_array_equal(got[3], first[3])    # dK, dV have no atomics
+            np.testing.assert_array_equal(got[4], first[4])

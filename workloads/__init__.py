@@ -8,8 +8,10 @@ Recipe (one for every workload):
   1. ``rng = numpy.random.default_rng(seed)``
   2. draw the sequence lengths (jagged workloads) or KV lengths (decode)
   3. decode only: draw the physical page permutation
-  4. draw Q, K, V, dO in that order with ``rng.standard_normal(shape, float32)``
-     and round each to bf16 with round-to-nearest-even.
+  4. draw Q, K, V, dO in that order: each tensor takes one 64-bit integer from
+     ``rng`` to seed 16 PCG64 child streams that fill 16 equal contiguous
+     chunks with ``standard_normal(float32)``; values are then rounded to bf16
+     with round-to-nearest-even.
 
 Workloads follow the pages' statement of the problem: packed ``[total_tokens,
 heads, head_dim]`` tensors plus an int32 offsets array (Meta's Jagged Flash
@@ -24,6 +26,7 @@ its distribution.
 from __future__ import annotations
 
 import math
+import os
 from dataclasses import dataclass, field
 from typing import Optional
 
@@ -58,8 +61,41 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     return bits_to_f32(bf16_bits(x))
 
 
+_CHUNKS = 16
+_POOL = None
+
+
+def _pool():
+    global _POOL
+    if _POOL is None:
+        from concurrent.futures import ThreadPoolExecutor
+        _POOL = ThreadPoolExecutor(max_workers=min(_CHUNKS, os.cpu_count() or 1))
+    return _POOL
+
+
 def _normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
-    return bf16_round(rng.standard_normal(shape, dtype=np.float32))
+    """N(0,1) float32 rounded to bf16.
+
+    The tensor takes one 64-bit draw from ``rng`` as the entropy of its own
+    SeedSequence, spawns 16 child PCG64 streams and fills 16 equal contiguous
+    chunks from them (in parallel threads; the values do not depend on the
+    thread count).
+    """
+    n = int(np.prod(shape))
+    out = np.empty(n, dtype=np.float32)
+    kids = np.random.SeedSequence(int(rng.integers(0, 2**63))).spawn(_CHUNKS)
+    step = -(-n // _CHUNKS) if n else 0
+
+    def fill(i):
+        lo, hi = i * step, min(n, (i + 1) * step)
+        if lo < hi:
+            g = np.random.Generator(np.random.PCG64(kids[i]))
+            seg = out[lo:hi]
+            g.standard_normal(out=seg, dtype=np.float32)
+            seg[:] = bf16_round(seg)
+
+    list(_pool().map(fill, range(_CHUNKS)))
+    return out.reshape(shape)
 
 
 # ------------------------------------------------------------------------ lengths
