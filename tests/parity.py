@@ -5,7 +5,9 @@ Tolerances (bf16 inputs, fp32 accumulation):
         stored in bf16, whose rounding alone exceeds 1e-2 once |O| >= 4; the
         added half-ulp is that unavoidable rounding, nothing more.
   LSE   max-abs <= 1e-3, and -inf exactly where the reference is -inf.
-  dQ, dK, dV   relative L2 error (whole tensor) <= 1e-2.
+  dQ, dK, dV   relative L2 error (whole tensor) <= 1e-2.  Where the reference
+        is exactly zero (e.g. dQ of a one-key sequence, whose dS vanishes
+        analytically) a relative error is undefined; there max |x| <= 1e-3.
 """
 from __future__ import annotations
 
@@ -16,6 +18,7 @@ import numpy as np
 O_ATOL = 1e-2
 LSE_ATOL = 1e-3
 GRAD_REL_L2 = 1e-2
+ZERO_ATOL = 1e-3
 
 
 def dev(x, torch, dtype=None):
@@ -68,8 +71,10 @@ def check_grad(got, ref, what):
     got = np.asarray(got, np.float64)
     assert got.shape == np.shape(ref), (what, got.shape, np.shape(ref))
     assert np.isfinite(got).all(), f"{what}: non-finite values"
+    if np.linalg.norm(ref) == 0:
+        worst = float(np.abs(got).max(initial=0.0))
+        assert worst <= ZERO_ATOL, f"{what}: reference is zero, max |got| {worst:.3e} > {ZERO_ATOL}"
+        return worst
     e = rel_l2(got, ref)
     assert e <= GRAD_REL_L2, f"{what}: rel L2 error {e:.3e} > {GRAD_REL_L2}"
-    if np.linalg.norm(ref) == 0:
-        assert np.all(got == 0), f"{what}: expected exact zeros"
     return e

@@ -68,3 +68,12 @@ def test_config_shapes_small():
     assert g.q.shape[1:] == (8, 128) and g.batch == 256 and g.max_len_q <= 1024
     bq = workloads.broadcast_q(0, 0.9, batch=8)
     assert bq.q.shape == (256, 4, 128) and bq.do.shape == (8, 256, 4, 128)
+
+
+def test_repage_keeps_kv_and_moves_pages():
+    a = workloads.decode(3, [10, 1, 33], heads_q=4, heads_kv=2, head_dim=8, page_size=4)
+    b = workloads.repage(a, 5, seed=9)
+    np.testing.assert_array_equal(a.k, b.k)
+    for i, L in enumerate(b.seqlens_k):
+        for t in range(L):
+            np.testing.assert_array_equal(b.k_cache[b.page_table[i, t // 5], t % 5], b.k[b.cu_k[i] + t])

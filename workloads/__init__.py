@@ -36,7 +36,7 @@ __all__ = [
     "bf16_round", "bf16_bits", "bits_to_f32", "sparsity_lengths", "offsets",
     "JaggedInputs", "BroadcastInputs", "DecodeInputs",
     "jagged", "broadcast", "decode", "tiny", "gem", "broadcast_q", "dense_causal",
-    "decode_paged", "TINY_LENGTHS",
+    "decode_paged", "repage", "TINY_LENGTHS",
 ]
 
 TINY_LENGTHS = (37, 64, 1, 90)
@@ -289,12 +289,23 @@ def decode(seed: int, seqlens, heads_q: int = 32, heads_kv: int = 8, head_dim: i
     k = _normal_bf16(rng, (tk, heads_kv, head_dim))
     v = _normal_bf16(rng, (tk, heads_kv, head_dim))
 
+    page_table, k_cache, v_cache = _page(k, v, seqlens, cu_k, page_size, max_pages_per_seq, perm, tail_fill)
+    return DecodeInputs(q, k, v, cu_k, seqlens, page_size, page_table, k_cache, v_cache, name,
+                        {"num_pages": num_pages})
+
+
+def _page(k, v, seqlens, cu_k, page_size, max_pages_per_seq, perm, tail_fill):
+    """Scatter contiguous K/V rows into pages; physical ids come from `perm` in (sequence, page) order."""
+    b = len(seqlens)
+    tk, heads_kv, head_dim = k.shape
+    pages_per = -(-seqlens.astype(np.int64) // page_size)
+    num_pages = int(pages_per.sum())
     page_table = np.zeros((b, max_pages_per_seq), dtype=np.int32)
     first_page = np.zeros(b + 1, dtype=np.int64)
     np.cumsum(pages_per, out=first_page[1:])
     for i in range(b):
         page_table[i, :pages_per[i]] = perm[first_page[i]:first_page[i + 1]]
-    # scatter every token to (physical page, slot)
+    # every token goes to (physical page, slot)
     seq_of_token = np.repeat(np.arange(b), seqlens)
     pos = np.arange(tk, dtype=np.int64) - cu_k[seq_of_token].astype(np.int64)
     phys = page_table[seq_of_token, pos // page_size].astype(np.int64)
@@ -303,10 +314,19 @@ def decode(seed: int, seqlens, heads_q: int = 32, heads_kv: int = 8, head_dim: i
     v_cache = np.full((num_pages * page_size, heads_kv, head_dim), tail_fill, dtype=np.float32)
     k_cache[slot] = k
     v_cache[slot] = v
-    k_cache = k_cache.reshape(num_pages, page_size, heads_kv, head_dim)
-    v_cache = v_cache.reshape(num_pages, page_size, heads_kv, head_dim)
-    return DecodeInputs(q, k, v, cu_k, seqlens, page_size, page_table, k_cache, v_cache, name,
-                        {"num_pages": num_pages})
+    return (page_table, k_cache.reshape(num_pages, page_size, heads_kv, head_dim),
+            v_cache.reshape(num_pages, page_size, heads_kv, head_dim))
+
+
+def repage(inp: DecodeInputs, page_size: int, seed: int, tail_fill: float = float("nan")) -> DecodeInputs:
+    """The same q and contiguous K/V laid out in pages of another size under a fresh permutation."""
+    rng = np.random.default_rng(seed)
+    pages_per = -(-inp.seqlens_k.astype(np.int64) // page_size)
+    perm = rng.permutation(int(pages_per.sum())).astype(np.int32)
+    max_pages = int(pages_per.max(initial=1))
+    pt, kc, vc = _page(inp.k, inp.v, inp.seqlens_k, inp.cu_k, page_size, max_pages, perm, tail_fill)
+    return DecodeInputs(inp.q, inp.k, inp.v, inp.cu_k, inp.seqlens_k, page_size, pt, kc, vc,
+                        inp.name + f"_repaged{page_size}", {"num_pages": kc.shape[0]})
 
 
 def decode_paged(seed: int = 0, page_size: int = 16, batch: int = 32, heads_q: int = 32, heads_kv: int = 8,
