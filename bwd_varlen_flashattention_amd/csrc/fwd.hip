@@ -12,13 +12,18 @@
 //     the cost-sorted list built by sched.hip;
 //   * 4 waves, each owning 32 query rows whose Q fragment stays in VGPRs for the
 //     whole key loop;
+//   * two workgroups per CU (two waves per SIMD), so one wave's softmax VALU
+//     work overlaps the other's MFMAs;
 //   * K/V tiles of 64 keys are double-buffered in LDS: the global loads of tile
 //     j+1 are in flight while tile j is consumed;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 so each lane owns one query column:
 //     the row max/sum reductions are in-lane plus one permlane32 swap;
 //   * the S^T accumulator, rounded to bf16, is directly the B operand of
-//     O^T += V^T P^T, whose A operand comes from row-major V in LDS through the
-//     transposed read ds_read_b64_tr_b16;
+//     O^T += V^T P^T.  V is staged into LDS already transposed (each thread
+//     transposes a 4-key x 8-column block in registers with v_perm_b32), with
+//     the keys of every 16-key group stored in the order the accumulator hands
+//     them out, so every MFMA operand is one 16-byte ds_read_b128 -- on gfx950
+//     the transposed LDS read delivers about a third of the b128 bandwidth;
 //   * the key loop is split into a branch-free bulk and masked tail/diagonal tiles
 //     (loop peeling, TLX page fifth paragraph);
 //   * the running max is only moved (and the accumulator rescaled) when it grows
@@ -35,28 +40,34 @@ struct FwdTile {
   static constexpr int BM = 128;            // query rows per item (32 per wave)
   static constexpr int BN = 64;             // keys per KV tile
   static constexpr int KP = D + 8;          // K row pitch in LDS (elements): +16 B staggers banks
-  static constexpr int VP = D + 16;         // V row pitch: +32 B keeps the 4-row transposed reads apart
+  static constexpr int VTP = BN + 8;        // V^T row pitch (elements): 144 B rows
   static constexpr int CH = D / 8;          // 16-byte chunks per row
-  static constexpr int LOADS = BN * CH / NT;
+  static constexpr int KLOADS = BN * CH / NT;
+  static constexpr int VBLOCKS = (BN / 4) * (D / 8);   // 4-key x 8-column blocks of V
   static constexpr int KS = D / 16;         // k-steps of K Q^T
   static constexpr int DB = D / 32;         // 32-wide output column blocks
   static_assert(BN * CH % NT == 0, "tile load split");
+  static_assert(VBLOCKS <= NT, "one V block per thread");
 };
+
+// Position of a 4-key quarter inside its stored 16-key group: the S^T accumulator
+// gives lane half h the keys {4h..4h+3, 8+4h..8+4h+3} of each group as one
+// 8-slot MFMA operand, so quarters are stored in the order 0, 2, 1, 3.
+__device__ __forceinline__ int vt_quarter_pos(int q) { return ((q & 1) << 1) | (q >> 1); }
 
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 
 template <int D, bool CAUSAL, bool BCAST>
-__global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   using T = FwdTile<D>;
-  constexpr int BM = T::BM, BN = T::BN, KP = T::KP, VP = T::VP, KS = T::KS, DB = T::DB;
+  constexpr int BM = T::BM, BN = T::BN, KP = T::KP, VTP = T::VTP, KS = T::KS, DB = T::DB;
   __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][BN * KP];
-  __shared__ __attribute__((aligned(16))) __bf16 v_lds[2][BN * VP];
+  __shared__ __attribute__((aligned(16))) __bf16 vt_lds[2][D * VTP];
   __shared__ int s_item;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int g16 = lane >> 4, i16 = lane & 15;
   const int n_items = *a.n_entries * a.hq;
   const float NEG_INF = -__builtin_inff();
 
@@ -105,25 +116,46 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
     for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
     float m_run = NEG_INF, l_run = 0.f;
 
-    u32x4 kr[T::LOADS], vr[T::LOADS];
+    // staging: K row-major chunks; V as one 4-key x 8-column block per thread
+    u32x4 kr[T::KLOADS], vr[4];
+    const bool v_stager = tid < T::VBLOCKS;
+    const int vkb = tid % (BN / 4), vdb = tid / (BN / 4);
     auto load_regs = [&](int j) {
 #pragma unroll
-      for (int i = 0; i < T::LOADS; ++i) {
+      for (int i = 0; i < T::KLOADS; ++i) {
         const int id = tid + i * T::NT;
         const int r = id / T::CH, c = id % T::CH;
         const int key = min(j * BN + r, lk - 1);     // clamp: rows past the end are masked later
-        const int64_t goff = ((int64_t)(k_base + key) * a.hkv + g) * D + c * 8;
-        kr[i] = *(const u32x4*)(a.k + goff);
-        vr[i] = *(const u32x4*)(a.v + goff);
+        kr[i] = *(const u32x4*)(a.k + ((int64_t)(k_base + key) * a.hkv + g) * D + c * 8);
+      }
+      if (v_stager) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = min(j * BN + 4 * vkb + i, lk - 1);
+          vr[i] = *(const u32x4*)(a.v + ((int64_t)(k_base + key) * a.hkv + g) * D + vdb * 8);
+        }
       }
     };
     auto store_lds = [&](int buf) {
 #pragma unroll
-      for (int i = 0; i < T::LOADS; ++i) {
+      for (int i = 0; i < T::KLOADS; ++i) {
         const int id = tid + i * T::NT;
         const int r = id / T::CH, c = id % T::CH;
         *(u32x4*)&k_lds[buf][r * KP + c * 8] = kr[i];
-        *(u32x4*)&v_lds[buf][r * VP + c * 8] = vr[i];
+      }
+      if (v_stager) {
+        // 4 keys x 8 columns -> 8 rows of V^T holding 4 keys each
+        const int col = 16 * (vkb >> 2) + 4 * vt_quarter_pos(vkb & 3);
+        __bf16* dst = &vt_lds[buf][(8 * vdb) * VTP + col];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t lo01 = __builtin_amdgcn_perm(vr[1][c], vr[0][c], 0x05040100u);
+          const uint32_t lo23 = __builtin_amdgcn_perm(vr[3][c], vr[2][c], 0x05040100u);
+          const uint32_t hi01 = __builtin_amdgcn_perm(vr[1][c], vr[0][c], 0x07060302u);
+          const uint32_t hi23 = __builtin_amdgcn_perm(vr[3][c], vr[2][c], 0x07060302u);
+          *(uint2*)(dst + (2 * c) * VTP) = make_uint2(lo01, lo23);
+          *(uint2*)(dst + (2 * c + 1) * VTP) = make_uint2(hi01, hi23);
+        }
       }
     };
 
@@ -192,19 +224,15 @@ __global__ __launch_bounds__(256) void fwd_kernel(FwdArgs a) {
       }
       l_run += psum;
 
-      // O^T[d][query] += V^T[d][key] P^T[key][query]
+      // O^T[d][query] += V^T[d][key] P^T[key][query]; one b128 read per operand
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int n0 = 32 * db + 16 * (g16 & 1);
+        const __bf16* vp = &vt_lds[buf][(32 * db + l32) * VTP + 8 * hh];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int k0 = 32 * kb + 16 * t + 4 * (g16 >> 1);
-            const __bf16* vp = &v_lds[buf][(k0 + (i16 >> 2)) * VP + n0 + 4 * (i16 & 3)];
-            const bf16x8 va = cat8(lds_read_tr4(vp), lds_read_tr4(vp + 8 * VP));
-            acc[db] = mfma32x32x16(va, pb[kb][t], acc[db]);
-          }
+          for (int t = 0; t < 2; ++t)
+            acc[db] = mfma32x32x16(*(const bf16x8*)(vp + 16 * (2 * kb + t)), pb[kb][t], acc[db]);
       }
 
       if (j + 1 < n_tiles) store_lds(buf ^ 1);
