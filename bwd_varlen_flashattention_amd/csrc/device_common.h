@@ -28,6 +28,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #define JFA_LDS __attribute__((address_space(3)))
 
+// Word 3 of a raw buffer resource (32-bit data format, no swizzle); loads past
+// num_records return zero.
+constexpr int kBufferFlags = 0x00020000;
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

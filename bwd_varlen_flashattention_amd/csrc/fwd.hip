@@ -29,6 +29,8 @@
 //   * the running max is only moved (and the accumulator rescaled) when it grows
 //     by more than 2^8, which keeps the result exact because the final
 //     normalisation uses the same stale max.
+#include <type_traits>
+
 #include "jfa_internal.h"
 #include "device_common.h"
 
@@ -70,6 +72,19 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   const int l32 = lane & 31, hh = lane >> 5;
   const int n_items = *a.n_entries * a.hq;
   const float NEG_INF = -__builtin_inff();
+
+  // byte offsets of this thread's staging loads inside a KV tile (row stride rs elements)
+  const int rs = a.hkv * D;
+  const bool v_stager = tid < T::VBLOCKS;
+  const int vkb = tid % (BN / 4), vdb = tid / (BN / 4);
+  uint32_t koff[T::KLOADS], voff[4];
+#pragma unroll
+  for (int i = 0; i < T::KLOADS; ++i) {
+    const int id = tid + i * T::NT;
+    koff[i] = (uint32_t)(((id / T::CH) * rs + (id % T::CH) * 8) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)(((4 * vkb + i) * rs + vdb * 8) * 2);
 
   for (;;) {
     if (tid == 0) s_item = (int)atomicAdd(a.counter, 1u);
@@ -116,24 +131,25 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
     float m_run = NEG_INF, l_run = 0.f;
 
-    // staging: K row-major chunks; V as one 4-key x 8-column block per thread
+    // staging: K row-major chunks; V as one 4-key x 8-column block per thread.
+    // Raw buffer loads: the per-thread byte offsets are fixed (koff/voff), the
+    // tile base and its valid byte range live in the 4-SGPR resource, and rows
+    // past the sequence end fall outside the range and read as zero.
+    const __bf16* kbase = a.k + ((int64_t)k_base * a.hkv + g) * D;
+    const __bf16* vbase = a.v + ((int64_t)k_base * a.hkv + g) * D;
     u32x4 kr[T::KLOADS], vr[4];
-    const bool v_stager = tid < T::VBLOCKS;
-    const int vkb = tid % (BN / 4), vdb = tid / (BN / 4);
     auto load_regs = [&](int j) {
+      const int64_t tile_off = (int64_t)j * BN * rs;
+      const uint32_t nbytes = (uint32_t)(min(lk - j * BN, BN) * rs * 2);
+      const auto krs = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + tile_off), (short)0, nbytes, kBufferFlags);
+      const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + tile_off), (short)0, nbytes, kBufferFlags);
 #pragma unroll
-      for (int i = 0; i < T::KLOADS; ++i) {
-        const int id = tid + i * T::NT;
-        const int r = id / T::CH, c = id % T::CH;
-        const int key = min(j * BN + r, lk - 1);     // clamp: rows past the end are masked later
-        kr[i] = *(const u32x4*)(a.k + ((int64_t)(k_base + key) * a.hkv + g) * D + c * 8);
-      }
+      for (int i = 0; i < T::KLOADS; ++i)
+        kr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, koff[i], 0, 0));
       if (v_stager) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = min(j * BN + 4 * vkb + i, lk - 1);
-          vr[i] = *(const u32x4*)(a.v + ((int64_t)(k_base + key) * a.hkv + g) * D + vdb * 8);
-        }
+        for (int i = 0; i < 4; ++i)
+          vr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff[i], 0, 0));
       }
     };
     auto store_lds = [&](int buf) {
@@ -159,13 +175,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       }
     };
 
-    if (n_tiles > 0) {
-      load_regs(0);
-      store_lds(0);
-      __syncthreads();
-    }
-
-    for (int j = 0; j < n_tiles; ++j) {
+    // One KV tile.  MASK selects the tail / causal-diagonal variant; the bulk
+    // variant has no per-element masking at all (loop peeling).
+    auto tile = [&](int j, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
       const int buf = j & 1;
       if (j + 1 < n_tiles) load_regs(j + 1);
 
@@ -180,15 +193,14 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
           s[kb] = mfma32x32x16(*(const bf16x8*)(kp + 16 * ks), qf[ks], s[kb]);
       }
 
-      if (j >= n_bulk) {   // tail tile (keys past Lk) or causal diagonal tile
+      if constexpr (MASK) {
+        const int kmax_ok = CAUSAL ? min(lk - 1, my_row + off) : lk - 1;   // last visible key
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = j * BN + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            bool ok = key < lk;
-            if (CAUSAL) ok = ok && key <= my_row + off;
-            s[kb][r] = ok ? s[kb][r] : NEG_INF;
+            s[kb][r] = key <= kmax_ok ? s[kb][r] : NEG_INF;
           }
       }
 
@@ -201,6 +213,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       const float m_new = fmaxf(m_run, mx * a.scale_log2);
       const bool need = m_new > m_run + kRescaleThreshold;
       if (__builtin_amdgcn_ballot_w64(need) != 0) {
+        asm volatile("" ::: "memory");   // keep this a real branch: the rescale is rare
         const float alpha = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run - m_new);
 #pragma unroll
         for (int db = 0; db < DB; ++db) acc[db] *= alpha;
@@ -237,6 +250,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
       if (j + 1 < n_tiles) store_lds(buf ^ 1);
       __syncthreads();
+    };
+
+    // The loops are only reachable through the prologue, whose wait covers the
+    // Q-fragment loads; otherwise every tile would wait on all outstanding loads.
+    if (n_tiles > 0) {
+      load_regs(0);
+      store_lds(0);
+      __syncthreads();
+      for (int j = 0; j < n_bulk; ++j) tile(j, std::false_type{});
+      for (int j = n_bulk; j < n_tiles; ++j) tile(j, std::true_type{});
     }
 
     // epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
