@@ -145,7 +145,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--sparsity", type=float, default=0.5)
     ap.add_argument("--page-size", type=int, default=16)
-    ap.add_argument("--cpu-seqs", type=int, default=64, help="sequences in the oracle timing sample (0 = skip)")
+    ap.add_argument("--cpu-seqs", type=int, default=256, help="sequences in the oracle timing sample (0 = skip)")
     ap.add_argument("--sweep", action="store_true", help="one JSON line per workload (GEM s, broadcast-Q, dense, decode)")
     ap.add_argument("--copy-calibration-mib", type=int, default=1024,
                     help="run one device copy of this size after timing (reference for HBM byte counters)")
@@ -201,11 +201,17 @@ def main():
 
     tflops = (jc.fwd_flops + jc.bwd_flops) * args.steps / (fb_ms * 1e-3) / 1e12
     dec_tbs = dc.bytes * args.steps / (dec_ms * 1e-3) / 1e12
-    fwd_ms, nf = kt["fwd"]
-    bwd_ms, nb = kt["bwd"]
-    dk_ms, nd = kt["decode"]
-    fwd_avg, bwd_avg, dk_avg = fwd_ms / max(nf, 1), bwd_ms / max(nb, 1), dk_ms / max(nd, 1)
-    bwd_ach = jc.bwd_flops / (bwd_avg * 1e-3) / 1e12
+    avg = {k: (ms / n if n else 0.0) for k, (ms, n) in kt.items()}
+    # Algorithmic flops per launch of each main kernel (per query-key pair, times Hq):
+    #   fwd       4d  (S = Q K^T, O = P V)
+    #   bwd_dkdv  8d  (S recomputed, dP, dV, dK: the backward's contractions except dQ)
+    #   bwd_dq    2d  (dQ = dS K; its own S/dP recomputation is not counted)
+    d, hq = 128, 8
+    alg = {"fwd": 4.0 * d * hq * jc.pairs, "bwd_dkdv": 8.0 * d * hq * jc.pairs, "bwd_dq": 2.0 * d * hq * jc.pairs}
+    dominant = max(alg, key=lambda k: avg[k])
+    ach = alg[dominant] / (avg[dominant] * 1e-3) / 1e12
+    names = {"fwd": "fwd_kernel (jagged forward)", "bwd_dkdv": "bwd_dkdv_kernel (key-stationary dK/dV)",
+             "bwd_dq": "bwd_dq_kernel (query-stationary dQ)"}
 
     # plain device copy of known size: reference for FETCH_SIZE / WRITE_SIZE scaling
     if args.copy_calibration_mib > 0:
@@ -247,10 +253,11 @@ def main():
         "fwd_bwd_ms": round(fb_ms / args.steps, 4),
         "decode": {"value": round(dec_tbs, 3), "unit": "TB/s", "pct_hbm_peak": round(100 * dec_tbs * 1e3 / HBM_PEAK_GBS, 2),
                    "ms": round(dec_ms / args.steps, 4)},
-        "kernels_ms": {"fwd": round(fwd_avg, 4), "bwd_main": round(bwd_avg, 4), "decode_split": round(dk_avg, 4)},
-        "roofline": {"kernel": "bwd_kernel (key-stationary backward main loop)", "bound": "mfma",
-                     "achieved": round(bwd_ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(bwd_ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None},
+        "kernels_ms": {k: round(v, 4) for k, v in avg.items()},
+        "roofline": {"kernel": names[dominant], "bound": "mfma",
+                     "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flop_per_launch": alg[dominant]},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

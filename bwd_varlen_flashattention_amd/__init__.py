@@ -148,13 +148,17 @@ class timing:
     def enable(on: bool = True) -> None:
         _lib.check(load().jfa_timing_enable(int(on)), "jfa_timing_enable")
 
+    SLOTS = ("fwd", "bwd_dq", "bwd_dkdv", "decode")
+
     @staticmethod
     def collect():
-        """Returns {'fwd': (total_ms, count), 'bwd': ..., 'decode': ...} and clears the record."""
-        ms = (ctypes.c_double * 3)()
-        cnt = (ctypes.c_int64 * 3)()
+        """Returns {'fwd': (total_ms, launches), 'bwd_dq': ..., 'bwd_dkdv': ..., 'decode': ...}
+        and clears the record."""
+        n = len(timing.SLOTS)
+        ms = (ctypes.c_double * n)()
+        cnt = (ctypes.c_int64 * n)()
         _lib.check(load().jfa_timing_collect(ms, cnt), "jfa_timing_collect")
-        return {name: (ms[i], cnt[i]) for i, name in enumerate(("fwd", "bwd", "decode"))}
+        return {name: (ms[i], cnt[i]) for i, name in enumerate(timing.SLOTS)}
 
 
 def default_scale(head_dim: int, softmax_scale: Optional[float] = None) -> float:

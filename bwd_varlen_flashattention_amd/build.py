@@ -19,6 +19,10 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libjfa.so")
 SOURCES = ["api.cpp", "sched.hip", "fwd.hip", "bwd.hip", "decode.hip"]
 ARCH = "gfx950"
+# Per-source code-generation options.  The backward's key-stationary kernel runs
+# one wave per SIMD, so its LDS reads must be issued well ahead of the MFMAs that
+# consume them; LLVM's iterative ILP scheduler does that (about 20% faster there).
+EXTRA_FLAGS = {"bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 
 def _hipcc() -> str:
@@ -39,7 +43,7 @@ def common_flags() -> list[str]:
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *common_flags(), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [_hipcc(), *common_flags(), *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

@@ -44,7 +44,7 @@ bool supported_dim(int d) { return d == 64 || d == 96 || d == 128; }
 struct Timing {
   std::mutex mu;
   bool enabled = false;
-  std::vector<hipEvent_t> start[3], stop[3];
+  std::vector<hipEvent_t> start[JFA_TIMING_SLOTS], stop[JFA_TIMING_SLOTS];
 };
 Timing& timing() {
   static Timing t;
@@ -112,8 +112,13 @@ int64_t fwd_max_entries(const jfa_attn_params_t* p) {
   return cdiv_i(p->total_q, bm) + (int64_t)p->batch;
 }
 
-int64_t bwd_max_entries(const jfa_attn_params_t* p) {
-  return cdiv_i(p->total_k, bwd_kv_tile()) + (int64_t)p->batch;
+int64_t dkdv_max_entries(const jfa_attn_params_t* p) {
+  return cdiv_i(p->total_k, bwd_dkdv_tile()) + (int64_t)p->batch;
+}
+
+int64_t dq_max_entries(const jfa_attn_params_t* p) {
+  if (p->broadcast_q) return 0;   // broadcast-Q dQ work is indexed directly
+  return cdiv_i(p->total_q, bwd_dq_rows()) + (int64_t)p->batch;
 }
 
 int64_t lse_elems(const jfa_attn_params_t* p) {
@@ -122,17 +127,21 @@ int64_t lse_elems(const jfa_attn_params_t* p) {
 
 struct BwdLayout {
   size_t delta = 0, dq_acc = 0;
-  SchedLayout sched;
+  SchedLayout dq_list, dkdv_list;
   size_t end = 0;
 };
 
 BwdLayout bwd_layout(const jfa_attn_params_t* p) {
   BwdLayout l;
   l.delta = 0;
-  l.dq_acc = align_up(l.delta + (size_t)lse_elems(p) * sizeof(float));
-  const size_t dq_elems = (size_t)p->total_q * p->num_heads_q * p->head_dim;
-  l.sched = sched_layout(align_up(l.dq_acc + dq_elems * sizeof(float)), bwd_max_entries(p));
-  l.end = l.sched.end;
+  size_t next = align_up((size_t)lse_elems(p) * sizeof(float));
+  if (p->broadcast_q) {
+    l.dq_acc = next;
+    next = align_up(next + (size_t)p->total_q * p->num_heads_q * p->head_dim * sizeof(float));
+  }
+  l.dq_list = sched_layout(next, dq_max_entries(p));
+  l.dkdv_list = sched_layout(l.dq_list.end, dkdv_max_entries(p));
+  l.end = l.dkdv_list.end;
   return l;
 }
 
@@ -248,7 +257,7 @@ jfa_status_t jfa_fwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   fa.scale_log2 = eff_scale(p->softmax_scale, p->head_dim) * 1.4426950408889634f;
   const int64_t max_items = (int64_t)L.max_entries * p->num_heads_q;
   const int grid = (int)std::min<int64_t>((int64_t)cu_count() * fwd_blocks_per_cu(p->head_dim), max_items);
-  TimedRegion tr(0, stream);
+  TimedRegion tr(JFA_TIMING_FWD, stream);
   e = launch_fwd(fa, p->head_dim, std::max(grid, 1), stream);
   tr.finish();
   return hip_status(e);
@@ -275,11 +284,36 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   hipStream_t stream = (hipStream_t)stream_;
   const float scale = eff_scale(p->softmax_scale, p->head_dim);
   float* delta = at<float>(workspace, L.delta);
-  float* dq_acc = at<float>(workspace, L.dq_acc);
+  float* dq_acc = p->broadcast_q ? at<float>(workspace, L.dq_acc) : nullptr;
   const int64_t dq_elems = (int64_t)p->total_q * p->num_heads_q * p->head_dim;
+  const int cus = cu_count();
+
+  BwdArgs ba{};
+  ba.q = (const __bf16*)q;
+  ba.k = (const __bf16*)k;
+  ba.v = (const __bf16*)v;
+  ba.dout = (const __bf16*)dout;
+  ba.lse = lse;
+  ba.delta = delta;
+  ba.cu_q = cu_seqlens_q;
+  ba.cu_k = cu_seqlens_k;
+  ba.dq = (__bf16*)dq;
+  ba.dq_acc = dq_acc;
+  ba.dk = (__bf16*)dk;
+  ba.dv = (__bf16*)dv;
+  ba.batch = p->batch;
+  ba.hq = p->num_heads_q;
+  ba.hkv = p->num_heads_kv;
+  ba.group = p->num_heads_q / p->num_heads_kv;
+  ba.bcast_nq = p->broadcast_q ? p->total_q : 0;
+  ba.total_q = p->total_q;
+  ba.causal = p->causal;
+  ba.scale = scale;
+  ba.scale_log2 = scale * 1.4426950408889634f;
 
   hipError_t e;
   if (p->total_q > 0) {
+    // delta = rowsum(dO * O); for broadcast-Q also zero the fp32 dQ accumulator
     BwdPreArgs pa{};
     pa.o = (const __bf16*)o;
     pa.dout = (const __bf16*)dout;
@@ -293,59 +327,77 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
     pa.dq_elems = dq_elems;
     e = launch_bwd_pre(pa, stream);
     if (e != hipSuccess) return JFA_ERR_HIP;
+
+    // dQ: query-stationary
+    if (p->broadcast_q) {
+      const int qtiles = cdiv_i(p->total_q, bwd_dq_rows());
+      const int64_t tiles_heads = (int64_t)qtiles * p->num_heads_q;
+      int chunks = (int)std::min<int64_t>(p->batch, std::max<int64_t>(1, (2LL * cus + tiles_heads - 1) / tiles_heads));
+      ba.bcast_chunk = cdiv_i(p->batch, chunks);
+      ba.bcast_chunks = cdiv_i(p->batch, ba.bcast_chunk);
+      ba.bcast_units = (int)(tiles_heads * ba.bcast_chunks);
+      TimedRegion tr(JFA_TIMING_BWD_DQ, stream);
+      e = launch_bwd_dq(ba, p->head_dim, std::max(1, std::min(ba.bcast_units, 2 * cus)), stream);
+      tr.finish();
+      if (e != hipSuccess) return JFA_ERR_HIP;
+    } else {
+      SchedArgs sa{};
+      sa.cu_q = cu_seqlens_q;
+      sa.cu_k = cu_seqlens_k;
+      sa.batch = p->batch;
+      sa.stat_tile = bwd_dq_rows();
+      sa.loop_tile = bwd_dq_tile();
+      sa.mode = 0;
+      sa.causal = p->causal;
+      sa.bcast_nq = 0;
+      sa.n_buckets = std::min(kMaxBuckets, cdiv_i(p->max_seqlen_k, bwd_dq_tile()) + 1);
+      sa.max_entries = L.dq_list.max_entries;
+      sa.entries = at<WorkEntry>(workspace, L.dq_list.entries);
+      sa.n_entries = at<int32_t>(workspace, L.dq_list.n_entries);
+      sa.counter = at<uint32_t>(workspace, L.dq_list.counter);
+      e = launch_sched(sa, stream);
+      if (e != hipSuccess) return JFA_ERR_HIP;
+      ba.entries = sa.entries;
+      ba.n_entries = sa.n_entries;
+      ba.counter = sa.counter;
+      const int64_t max_items = (int64_t)L.dq_list.max_entries * p->num_heads_q;
+      TimedRegion tr(JFA_TIMING_BWD_DQ, stream);
+      e = launch_bwd_dq(ba, p->head_dim, (int)std::max<int64_t>(1, std::min<int64_t>(2LL * cus, max_items)), stream);
+      tr.finish();
+      if (e != hipSuccess) return JFA_ERR_HIP;
+    }
   }
 
   if (p->total_k > 0) {
+    // dK, dV: key-stationary
     SchedArgs sa{};
     sa.cu_q = cu_seqlens_q;
     sa.cu_k = cu_seqlens_k;
     sa.batch = p->batch;
-    sa.stat_tile = bwd_kv_tile();
-    sa.loop_tile = bwd_block_rows();
+    sa.stat_tile = bwd_dkdv_tile();
+    sa.loop_tile = bwd_dkdv_rows();
     sa.mode = 1;
     sa.causal = p->causal;
     sa.bcast_nq = p->broadcast_q ? p->total_q : 0;
     const int maxq = p->broadcast_q ? p->total_q : p->max_seqlen_q;
-    sa.n_buckets = std::min(kMaxBuckets, cdiv_i(maxq, bwd_block_rows()) + 1);
-    sa.max_entries = L.sched.max_entries;
-    sa.entries = at<WorkEntry>(workspace, L.sched.entries);
-    sa.n_entries = at<int32_t>(workspace, L.sched.n_entries);
-    sa.counter = at<uint32_t>(workspace, L.sched.counter);
+    sa.n_buckets = std::min(kMaxBuckets, cdiv_i(maxq, bwd_dkdv_rows()) + 1);
+    sa.max_entries = L.dkdv_list.max_entries;
+    sa.entries = at<WorkEntry>(workspace, L.dkdv_list.entries);
+    sa.n_entries = at<int32_t>(workspace, L.dkdv_list.n_entries);
+    sa.counter = at<uint32_t>(workspace, L.dkdv_list.counter);
     e = launch_sched(sa, stream);
     if (e != hipSuccess) return JFA_ERR_HIP;
-
-    BwdArgs ba{};
-    ba.q = (const __bf16*)q;
-    ba.k = (const __bf16*)k;
-    ba.v = (const __bf16*)v;
-    ba.dout = (const __bf16*)dout;
-    ba.lse = lse;
-    ba.delta = delta;
-    ba.cu_q = cu_seqlens_q;
-    ba.cu_k = cu_seqlens_k;
-    ba.dq_acc = dq_acc;
-    ba.dk = (__bf16*)dk;
-    ba.dv = (__bf16*)dv;
     ba.entries = sa.entries;
     ba.n_entries = sa.n_entries;
     ba.counter = sa.counter;
-    ba.hq = p->num_heads_q;
-    ba.hkv = p->num_heads_kv;
-    ba.group = p->num_heads_q / p->num_heads_kv;
-    ba.bcast_nq = sa.bcast_nq;
-    ba.total_q = p->total_q;
-    ba.causal = p->causal;
-    ba.scale = scale;
-    ba.scale_log2 = scale * 1.4426950408889634f;
-    const int64_t max_items = (int64_t)L.sched.max_entries * p->num_heads_kv;
-    const int grid = (int)std::min<int64_t>((int64_t)cu_count() * bwd_blocks_per_cu(p->head_dim), max_items);
-    TimedRegion tr(1, stream);
-    e = launch_bwd(ba, p->head_dim, std::max(grid, 1), stream);
+    const int64_t max_items = (int64_t)L.dkdv_list.max_entries * p->num_heads_kv;
+    TimedRegion tr(JFA_TIMING_BWD_DKDV, stream);
+    e = launch_bwd_dkdv(ba, p->head_dim, (int)std::max<int64_t>(1, std::min<int64_t>(cus, max_items)), stream);
     tr.finish();
     if (e != hipSuccess) return JFA_ERR_HIP;
   }
 
-  if (p->total_q > 0) {
+  if (p->broadcast_q && p->total_q > 0) {
     DqConvertArgs ca{};
     ca.dq_acc = dq_acc;
     ca.dq = (__bf16*)dq;
@@ -399,7 +451,7 @@ jfa_status_t jfa_decode_paged(const jfa_decode_params_t* p, const void* q, const
   a.max_pages = p->max_pages_per_seq;
   a.splits = splits;
   a.scale_log2 = eff_scale(p->softmax_scale, p->head_dim) * 1.4426950408889634f;
-  TimedRegion tr(2, stream);
+  TimedRegion tr(JFA_TIMING_DECODE, stream);
   hipError_t e = launch_decode(a, p->head_dim, stream);
   tr.finish();
   if (e != hipSuccess) return JFA_ERR_HIP;
@@ -417,11 +469,11 @@ jfa_status_t jfa_timing_enable(int enable) {
   return JFA_OK;
 }
 
-jfa_status_t jfa_timing_collect(double total_ms[3], int64_t count[3]) {
+jfa_status_t jfa_timing_collect(double total_ms[JFA_TIMING_SLOTS], int64_t count[JFA_TIMING_SLOTS]) {
   Timing& t = timing();
   std::lock_guard<std::mutex> g(t.mu);
   jfa_status_t st = JFA_OK;
-  for (int w = 0; w < 3; ++w) {
+  for (int w = 0; w < JFA_TIMING_SLOTS; ++w) {
     double ms_sum = 0.0;
     int64_t n = 0;
     for (size_t i = 0; i < t.start[w].size(); ++i) {

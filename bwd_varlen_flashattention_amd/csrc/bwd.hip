@@ -2,7 +2,7 @@
 //
 // What is computed ("Cutting edge isn't plug-and-play: customising
 // FlashAttention-4 on B300", Phase 2 chunked-backward pseudocode and its buffer
-// list, restated without the head-dim chunking because d <= 128 fits on chip):
+// list, restated without head-dim chunking because d <= 128 fits on chip):
 //   P = exp(S - LSE) rebuilt from the forward's saved LSE, S = Q K^T * scale,
 //   delta = rowsum(dO * O), dP = dO V^T, dS = P * (dP - delta),
 //   dV = P^T dO, dK = scale dS^T Q, dQ = scale dS K.
@@ -10,19 +10,33 @@
 // every item adds its dQ into the one shared dQ.
 //
 // Kernels:
-//   bwd_pre_kernel   delta (fp32, laid out like LSE) and a zeroed fp32 dQ accumulator
-//   bwd_kernel       persistent, key-stationary: a workgroup owns 128 keys of one
-//                    KV head, keeps K/V fragments in VGPRs and the dK/dV
-//                    accumulators in AGPR/VGPRs across all query tiles and all
-//                    query heads of the GQA group, and streams 64-row Q/dO tiles
-//                    through double-buffered LDS.  dQ partials (dS K) are
-//                    atomically added in fp32 to the accumulator.
-//   dq_convert       dQ = scale * accumulator -> bf16
+//   bwd_pre_kernel   delta (fp32, laid out like LSE); zeroes the fp32 dQ
+//                    accumulator used only by broadcast-Q
+//   bwd_dkdv_kernel  persistent, key-stationary: a workgroup owns 128 keys of one
+//                    KV head; K/V fragments stay in VGPRs and the dK^T/dV^T
+//                    accumulators in registers across all query tiles and all
+//                    query heads of the GQA group.  64-row Q/dO tiles are staged
+//                    into double-buffered LDS both row-major (A operands of
+//                    S = Q K^T and dP = dO V^T) and transposed (A operands of
+//                    dV^T += dO^T P and dK^T += Q^T dS, with P and dS taken
+//                    straight from the S/dP accumulators), so every MFMA operand
+//                    is a single ds_read_b128.
+//   bwd_dq_kernel    persistent, query-stationary (the forward's structure):
+//                    recomputes S^T = K Q^T and dP^T = V dO^T per 64-key tile
+//                    and accumulates dQ^T += K^T dS^T in registers, with dS^T
+//                    straight from the accumulators and K^T staged transposed.
+//                    dQ is written once per query tile: no atomics, so dQ is
+//                    deterministic.  Broadcast-Q splits the items into chunks
+//                    whose partial dQ are added in fp32 (then dq_convert).
 //
-// The K tile stays in LDS for the whole item: K is consumed twice per query
-// tile, by S = Q K^T and again by dQ = dS K after dS exists, so no stage that
-// holds K is refilled before its last reader (the single-stage K-buffer hazard
-// described in the bug-hunting section of the B300 page).
+// The dQ kernel repeats S and dP (4d of the 14d flops per query-key pair); the
+// alternative -- dS K accumulated with fp32 atomics from the key-stationary
+// kernel -- measured ~1.2 ms of atomic traffic on the GEM s=0.5 workload,
+// more than the repeated MFMA work.  Neither kernel refills an LDS stage while
+// any reader of it is unfinished (one barrier per stage), the single-buffer
+// K hazard described in the bug-hunting section of the B300 page.
+#include <type_traits>
+
 #include "jfa_internal.h"
 #include "device_common.h"
 
@@ -60,23 +74,25 @@ __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(BwdPreArgs a) {
     }
     a.delta[di] = acc;
   }
-  // zero the dQ accumulator (grid-stride over float4)
-  const int64_t n4 = a.dq_elems / 4;
-  const int64_t stride = (int64_t)gridDim.x * kPreThreads;
-  for (int64_t i = gtid; i < n4; i += stride) ((f32x4*)a.dq_acc)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int64_t i = n4 * 4 + gtid; i < a.dq_elems; i += stride) a.dq_acc[i] = 0.f;
+  if (a.dq_acc) {   // broadcast-Q only: zero the fp32 dQ accumulator (grid-stride over float4)
+    const int64_t n4 = a.dq_elems / 4;
+    const int64_t stride = (int64_t)gridDim.x * kPreThreads;
+    for (int64_t i = gtid; i < n4; i += stride) ((f32x4*)a.dq_acc)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int64_t i = n4 * 4 + gtid; i < a.dq_elems; i += stride) a.dq_acc[i] = 0.f;
+  }
 }
 
 hipError_t launch_bwd_pre(const BwdPreArgs& a, hipStream_t stream) {
   const int64_t threads = a.rows * a.hq * 16;
   int64_t blocks = (threads + kPreThreads - 1) / kPreThreads;
-  if (blocks < 1024) blocks = 1024;                 // enough waves for the zero fill
+  if (a.dq_acc && blocks < 256) blocks = 256;
+  if (blocks < 1) blocks = 1;
   if (blocks > (1 << 30)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)blocks), dim3(kPreThreads), 0, stream, a);
   return hipGetLastError();
 }
 
-// ----------------------------------------------------------------------------- dQ convert
+// ----------------------------------------------------------------------------- dQ convert (broadcast-Q)
 __global__ __launch_bounds__(256) void dq_convert_kernel(DqConvertArgs a) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i + 3 < a.n) {
@@ -97,31 +113,47 @@ hipError_t launch_dq_convert(const DqConvertArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// ----------------------------------------------------------------------------- main kernel
+// Stored order of the four 4-row quarters of a 16-row group in a transposed
+// tile: an S/dP accumulator hands lane half h the rows {4h..4h+3, 8+4h..8+4h+3}
+// of each group as one 8-slot MFMA operand, so quarters go in the order 0, 2, 1, 3.
+__device__ __forceinline__ int quarter_pos(int q) { return ((q & 1) << 1) | (q >> 1); }
+
+// Transpose a 4-row x 8-column bf16 block held as four 16-byte rows and write it
+// as 8 rows of 4 values (8 bytes each) at dst, dst + pitch, ... (pitch in elements).
+__device__ __forceinline__ void store_transposed_4x8(__bf16* dst, int pitch, const u32x4 (&r)[4]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const uint32_t lo01 = __builtin_amdgcn_perm(r[1][c], r[0][c], 0x05040100u);
+    const uint32_t lo23 = __builtin_amdgcn_perm(r[3][c], r[2][c], 0x05040100u);
+    const uint32_t hi01 = __builtin_amdgcn_perm(r[1][c], r[0][c], 0x07060302u);
+    const uint32_t hi23 = __builtin_amdgcn_perm(r[3][c], r[2][c], 0x07060302u);
+    *(uint2*)(dst + (2 * c) * pitch) = make_uint2(lo01, lo23);
+    *(uint2*)(dst + (2 * c + 1) * pitch) = make_uint2(hi01, hi23);
+  }
+}
+
+// ============================================================================= dK / dV
 template <int D>
-struct BwdTile {
-  static constexpr int NT = 256;           // 4 waves, 32 keys each
-  static constexpr int BN = 128;           // keys per item
-  static constexpr int BM = 64;            // query rows per inner step
-  static constexpr int P = D + 16;         // LDS row pitch of Q, dO and K (elements)
-  static constexpr int SP = BM + 16;       // LDS row pitch of the dS^T tile
-  static constexpr int CH = D / 8;
-  static constexpr int QLOADS = BM * CH / NT;
-  static constexpr int KLOADS = BN * CH / NT;
+struct DkvTile {
+  static constexpr int NT = 256;             // 4 waves, 32 keys each
+  static constexpr int BN = 128;             // keys per item
+  static constexpr int BM = 64;              // query rows per step
+  static constexpr int QP = D + 8;           // row pitch of Q / dO tiles (elements)
+  static constexpr int QTP = BM + 8;         // row pitch of Q^T / dO^T tiles
+  static constexpr int QBLOCKS = (BM / 4) * (D / 8);   // 4-row x 8-column staging blocks
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
-  static constexpr int DQB = (2 * DB + 3) / 4;   // dQ output blocks per wave
-  static_assert(BM * CH % NT == 0 && BN * CH % NT == 0, "tile load split");
+  static_assert(QBLOCKS <= NT, "one Q block per thread");
 };
 
 template <int D, bool CAUSAL, bool BCAST>
-__global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
-  using T = BwdTile<D>;
-  constexpr int BN = T::BN, BM = T::BM, P = T::P, SP = T::SP, KS = T::KS, DB = T::DB;
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[BN * P];
-  __shared__ __attribute__((aligned(16))) __bf16 q_lds[2][BM * P];
-  __shared__ __attribute__((aligned(16))) __bf16 do_lds[2][BM * P];
-  __shared__ __attribute__((aligned(16))) __bf16 dst_lds[BN * SP];
+__global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
+  using T = DkvTile<D>;
+  constexpr int BN = T::BN, BM = T::BM, QP = T::QP, QTP = T::QTP, KS = T::KS, DB = T::DB;
+  __shared__ __attribute__((aligned(16))) __bf16 q_lds[2][BM * QP];
+  __shared__ __attribute__((aligned(16))) __bf16 do_lds[2][BM * QP];
+  __shared__ __attribute__((aligned(16))) __bf16 qt_lds[2][D * QTP];
+  __shared__ __attribute__((aligned(16))) __bf16 dot_lds[2][D * QTP];
   __shared__ __attribute__((aligned(16))) float lse_lds[2][BM];
   __shared__ __attribute__((aligned(16))) float dlt_lds[2][BM];
   __shared__ int s_item;
@@ -129,9 +161,16 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int g16 = lane >> 4, i16 = lane & 15;
   const int n_items = *a.n_entries * a.hkv;
   const float INF = __builtin_inff();
+
+  // staging: thread owns rows 4*sq..4*sq+3, columns 8*sd..8*sd+7 of the Q and dO tiles
+  const bool stager = tid < T::QBLOCKS;
+  const int sq = tid % (BM / 4), sd = tid / (BM / 4);
+  const int qrs = a.hq * D;                           // elements between query rows
+  uint32_t qoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) qoff[i] = (uint32_t)(((4 * sq + i) * qrs + 8 * sd) * 2);
 
   for (;;) {
     if (tid == 0) s_item = (int)atomicAdd(a.counter, 1u);
@@ -167,48 +206,36 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
         vf[ks] = key_ok ? *(const bf16x8*)(a.v + base + 16 * ks) : zero_bf16x8();
       }
     }
-    f32x16 dkT[DB], dvT[DB];
+    f32x16 dkt[DB], dvt[DB];
 #pragma unroll
-    for (int db = 0; db < DB; ++db) { dkT[db] = f32x16{}; dvT[db] = f32x16{}; }
+    for (int db = 0; db < DB; ++db) { dkt[db] = f32x16{}; dvt[db] = f32x16{}; }
 
-    if (n_steps > 0) {
-      // stage the K tile (row-major, zero past the end) for the dQ contraction
-#pragma unroll
-      for (int i = 0; i < T::KLOADS; ++i) {
-        const int id = tid + i * T::NT;
-        const int r = id / T::CH, c = id % T::CH;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (kt0 + r < lk) v = *(const u32x4*)(a.k + ((int64_t)(k_base + kt0 + r) * a.hkv + g) * D + c * 8);
-        *(u32x4*)&k_lds[r * P + c * 8] = v;
-      }
-    }
-
-    // step s -> (query head, query tile)
-    u32x4 qr[T::QLOADS], dr[T::QLOADS];
+    // step s -> (query head, query tile); rows past Lq read as zero (buffer range)
+    u32x4 qr[4], dr[4];
     float lse_r = 0.f, dlt_r = 0.f;
     auto load_regs = [&](int s) {
       const int h = g * a.group + s / n_qt;
       const int qt = i_first + s % n_qt;
+      const int row0 = qt * BM;
+      const uint32_t nbytes = (uint32_t)(min(lq - row0, BM) * qrs * 2);
+      const __bf16* qb = a.q + ((int64_t)(q_base + row0) * a.hq + h) * D;
+      const int64_t orow0 = BCAST ? (int64_t)b * lq + row0 : (int64_t)(q_base + row0);
+      const __bf16* ob = a.dout + (orow0 * a.hq + h) * D;
+      const auto qrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)qb, (short)0, nbytes, kBufferFlags);
+      const auto orsrc = __builtin_amdgcn_make_buffer_rsrc((void*)ob, (short)0, nbytes, kBufferFlags);
+      if (stager) {
 #pragma unroll
-      for (int i = 0; i < T::QLOADS; ++i) {
-        const int id = tid + i * T::NT;
-        const int r = id / T::CH, c = id % T::CH;
-        const int row = qt * BM + r;
-        u32x4 qv = {0u, 0u, 0u, 0u}, dv = {0u, 0u, 0u, 0u};
-        if (row < lq) {
-          qv = *(const u32x4*)(a.q + ((int64_t)(q_base + row) * a.hq + h) * D + c * 8);
-          const int64_t orow = BCAST ? (int64_t)b * lq + row : (int64_t)(q_base + row);
-          dv = *(const u32x4*)(a.dout + (orow * a.hq + h) * D + c * 8);
+        for (int i = 0; i < 4; ++i) {
+          qr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrsrc, qoff[i], 0, 0));
+          dr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(orsrc, qoff[i], 0, 0));
         }
-        qr[i] = qv;
-        dr[i] = dv;
       }
       if (tid < BM) {
-        const int row = qt * BM + tid;
+        const int row = row0 + tid;
         if (row < lq) {
           const int64_t li = BCAST ? ((int64_t)b * a.hq + h) * lq + row : (int64_t)h * a.total_q + q_base + row;
           const float l = a.lse[li];
-          lse_r = (l == -INF) ? INF : l * kLog2e;   // rows that saw no key get P = 0
+          lse_r = (l == -INF) ? INF : l * kLog2e;     // rows that saw no key get P = 0
           dlt_r = a.delta[li];
         } else {
           lse_r = INF;
@@ -217,49 +244,36 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
       }
     };
     auto store_lds = [&](int buf) {
+      if (stager) {
 #pragma unroll
-      for (int i = 0; i < T::QLOADS; ++i) {
-        const int id = tid + i * T::NT;
-        const int r = id / T::CH, c = id % T::CH;
-        *(u32x4*)&q_lds[buf][r * P + c * 8] = qr[i];
-        *(u32x4*)&do_lds[buf][r * P + c * 8] = dr[i];
+        for (int i = 0; i < 4; ++i) {
+          *(u32x4*)&q_lds[buf][(4 * sq + i) * QP + 8 * sd] = qr[i];
+          *(u32x4*)&do_lds[buf][(4 * sq + i) * QP + 8 * sd] = dr[i];
+        }
+        const int col = 16 * (sq >> 2) + 4 * quarter_pos(sq & 3);
+        store_transposed_4x8(&qt_lds[buf][(8 * sd) * QTP + col], QTP, qr);
+        store_transposed_4x8(&dot_lds[buf][(8 * sd) * QTP + col], QTP, dr);
       }
       if (tid < BM) { lse_lds[buf][tid] = lse_r; dlt_lds[buf][tid] = dlt_r; }
     };
 
-    if (n_steps > 0) {
-      load_regs(0);
-      store_lds(0);
-      __syncthreads();
-    }
-
-    for (int s = 0; s < n_steps; ++s) {
+    auto step = [&](int s, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
       const int buf = s & 1;
-      const int h = g * a.group + s / n_qt;
       const int qt = i_first + s % n_qt;
       if (s + 1 < n_steps) load_regs(s + 1);
-      const __bf16* qt_lds = q_lds[buf];
-      const __bf16* dot_lds = do_lds[buf];
-
-      // S[q][key] and dP[q][key] for two 32-row query blocks
-      f32x16 sacc[2], pacc[2];
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
-        sacc[qb] = f32x16{};
-        pacc[qb] = f32x16{};
-        const __bf16* qp = qt_lds + (32 * qb + l32) * P + 8 * hh;
-        const __bf16* dp = dot_lds + (32 * qb + l32) * P + 8 * hh;
+        // S[q][key], dP[q][key]: A = Q / dO rows, B = K / V fragments
+        f32x16 sacc = f32x16{}, pacc = f32x16{};
+        const __bf16* qp = &q_lds[buf][(32 * qb + l32) * QP + 8 * hh];
+        const __bf16* dp = &do_lds[buf][(32 * qb + l32) * QP + 8 * hh];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          sacc[qb] = mfma32x32x16(*(const bf16x8*)(qp + 16 * ks), kf[ks], sacc[qb]);
-          pacc[qb] = mfma32x32x16(*(const bf16x8*)(dp + 16 * ks), vf[ks], pacc[qb]);
+          sacc = mfma32x32x16(*(const bf16x8*)(qp + 16 * ks), kf[ks], sacc);
+          pacc = mfma32x32x16(*(const bf16x8*)(dp + 16 * ks), vf[ks], pacc);
         }
-      }
-
-      // P = exp2(S*c - LSE*log2e), masked; dS = P * (dP - delta)
-      bf16x8 pb[2][2], sb[2][2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+        // P = exp2(S*c - LSE*log2e); dS = P * (dP - delta)
         float pv[16], dsv[16];
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
@@ -269,75 +283,39 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
             const int r = 4 * r4 + x;
-            bool ok = key_ok;
-            if (CAUSAL) ok = ok && (my_key <= qt * BM + q0 + x + off);
-            const float p = ok ? fast_exp2(fmaf(sacc[qb][r], a.scale_log2, -l4[x])) : 0.f;
+            float p = fast_exp2(fmaf(sacc[r], a.scale_log2, -l4[x]));
+            if constexpr (MASK) p = (my_key <= qt * BM + q0 + x + off) ? p : 0.f;
             pv[r] = p;
-            dsv[r] = p * (pacc[qb][r] - d4[x]);
+            dsv[r] = p * (pacc[r] - d4[x]);
           }
         }
-        pb[qb][0] = to_bf16x8(pv);
-        pb[qb][1] = to_bf16x8(pv + 8);
-        sb[qb][0] = to_bf16x8(dsv);
-        sb[qb][1] = to_bf16x8(dsv + 8);
-      }
-
-      // dV^T[d][key] += dO^T P ; dK^T[d][key] += Q^T dS   (A operands: transposed LDS reads)
+        const bf16x8 pb0 = to_bf16x8(pv), pb1 = to_bf16x8(pv + 8);
+        const bf16x8 sb0 = to_bf16x8(dsv), sb1 = to_bf16x8(dsv + 8);
+        // dV^T[d][key] += dO^T P ; dK^T[d][key] += Q^T dS  (A operands from the transposed tiles)
 #pragma unroll
-      for (int db = 0; db < DB; ++db) {
-        const int c0 = 32 * db + 16 * (g16 & 1) + 4 * (i16 & 3);
-#pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const int r0 = 32 * qb + 16 * t + 4 * (g16 >> 1) + (i16 >> 2);
-            const __bf16* dp = dot_lds + r0 * P + c0;
-            const __bf16* qp = qt_lds + r0 * P + c0;
-            const bf16x8 doT = cat8(lds_read_tr4(dp), lds_read_tr4(dp + 8 * P));
-            const bf16x8 qT = cat8(lds_read_tr4(qp), lds_read_tr4(qp + 8 * P));
-            dvT[db] = mfma32x32x16(doT, pb[qb][t], dvT[db]);
-            dkT[db] = mfma32x32x16(qT, sb[qb][t], dkT[db]);
-          }
-      }
-
-      // dS^T[key][q] -> LDS (4 consecutive queries per 8-byte write)
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          bf16x4 v4;
-#pragma unroll
-          for (int x = 0; x < 4; ++x) v4[x] = sb[qb][r4 >> 1][4 * (r4 & 1) + x];
-          *(bf16x4*)&dst_lds[(32 * w + l32) * SP + 32 * qb + 8 * r4 + 4 * hh] = v4;
-        }
-      __syncthreads();
-
-      // dQ[q][d] = dS[q][key] K[key][d] over all 128 keys; this wave takes output blocks w, w+4, ...
-#pragma unroll
-      for (int bi = 0; bi < T::DQB; ++bi) {
-        const int blk = w + 4 * bi;
-        if (blk < 2 * DB) {
-          const int qb = blk / DB, db = blk % DB;
-          f32x16 dq = f32x16{};
-          const __bf16* sp = dst_lds + (4 * (g16 >> 1) + (i16 >> 2)) * SP + 32 * qb + 16 * (g16 & 1) + 4 * (i16 & 3);
-          const __bf16* kp = k_lds + (4 * (g16 >> 1) + (i16 >> 2)) * P + 32 * db + 16 * (g16 & 1) + 4 * (i16 & 3);
-#pragma unroll
-          for (int ks = 0; ks < BN / 16; ++ks) {
-            const bf16x8 sa = cat8(lds_read_tr4(sp + 16 * ks * SP), lds_read_tr4(sp + (16 * ks + 8) * SP));
-            const bf16x8 kb = cat8(lds_read_tr4(kp + 16 * ks * P), lds_read_tr4(kp + (16 * ks + 8) * P));
-            dq = mfma32x32x16(sa, kb, dq);
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = qt * BM + 32 * qb + 8 * (r >> 2) + 4 * hh + (r & 3);
-            if (row < lq)
-              unsafeAtomicAdd(a.dq_acc + ((int64_t)(q_base + row) * a.hq + h) * D + 32 * db + l32, dq[r]);
-          }
+        for (int db = 0; db < DB; ++db) {
+          const __bf16* dtp = &dot_lds[buf][(32 * db + l32) * QTP + 32 * qb + 8 * hh];
+          const __bf16* qtp = &qt_lds[buf][(32 * db + l32) * QTP + 32 * qb + 8 * hh];
+          dvt[db] = mfma32x32x16(*(const bf16x8*)(dtp), pb0, dvt[db]);
+          dvt[db] = mfma32x32x16(*(const bf16x8*)(dtp + 16), pb1, dvt[db]);
+          dkt[db] = mfma32x32x16(*(const bf16x8*)(qtp), sb0, dkt[db]);
+          dkt[db] = mfma32x32x16(*(const bf16x8*)(qtp + 16), sb1, dkt[db]);
         }
       }
-
       if (s + 1 < n_steps) store_lds(buf ^ 1);
       __syncthreads();
+    };
+
+    if (n_steps > 0) {
+      load_regs(0);
+      store_lds(0);
+      __syncthreads();
+      for (int s = 0; s < n_steps; ++s) {
+        bool mask = false;
+        if (CAUSAL) mask = kt0 + BN - 1 > (i_first + s % n_qt) * BM + off;   // some key above the diagonal
+        if (mask) step(s, std::true_type{});
+        else step(s, std::false_type{});
+      }
     }
 
     // epilogue: dK = scale * dK^T, dV = dV^T, 4 consecutive d per 8-byte store
@@ -350,39 +328,276 @@ __global__ __launch_bounds__(256) void bwd_kernel(BwdArgs a) {
           bf16x4 kv4, vv4;
 #pragma unroll
           for (int x = 0; x < 4; ++x) {
-            kv4[x] = (__bf16)(dkT[db][4 * r4 + x] * a.scale);
-            vv4[x] = (__bf16)(dvT[db][4 * r4 + x]);
+            kv4[x] = (__bf16)(dkt[db][4 * r4 + x] * a.scale);
+            vv4[x] = (__bf16)(dvt[db][4 * r4 + x]);
           }
           const int d0 = 32 * db + 8 * r4 + 4 * hh;
           *(bf16x4*)(a.dk + base + d0) = kv4;
           *(bf16x4*)(a.dv + base + d0) = vv4;
         }
     }
-    __syncthreads();   // s_item and LDS reuse
+    __syncthreads();   // s_item and the LDS buffers are reused by the next item
   }
 }
 
-int bwd_block_rows() { return BwdTile<128>::BM; }
-int bwd_kv_tile() { return BwdTile<128>::BN; }
-int bwd_blocks_per_cu(int) { return 1; }
+// ============================================================================= dQ
+template <int D>
+struct DqTile {
+  static constexpr int NT = 256;             // 4 waves, 32 query rows each
+  static constexpr int BM = 128;             // query rows per item
+  static constexpr int BN = 64;              // keys per tile
+  static constexpr int KP = D + 8;           // row pitch of K / V tiles
+  static constexpr int KTP = BN + 8;         // row pitch of the K^T tile
+  static constexpr int CH = D / 8;
+  static constexpr int VLOADS = BN * CH / NT;
+  static constexpr int KBLOCKS = (BN / 4) * (D / 8);
+  static constexpr int KS = D / 16;
+  static constexpr int DB = D / 32;
+  static_assert(BN * CH % NT == 0 && KBLOCKS <= NT, "tile load split");
+};
+
+template <int D, bool CAUSAL, bool BCAST>
+__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+  using T = DqTile<D>;
+  constexpr int BM = T::BM, BN = T::BN, KP = T::KP, KTP = T::KTP, KS = T::KS, DB = T::DB;
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds[BN * KP];
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds[BN * KP];
+  __shared__ __attribute__((aligned(16))) __bf16 kt_lds[D * KTP];
+  __shared__ int s_item;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hh = lane >> 5;
+  const float NEG_INF = -__builtin_inff(), INF = __builtin_inff();
+
+  // staging: K as one 4-key x 8-column block per thread (written row-major and
+  // transposed); V as row-major 16-byte chunks
+  const int rs = a.hkv * D;
+  const bool k_stager = tid < T::KBLOCKS;
+  const int skb = tid % (BN / 4), skd = tid / (BN / 4);
+  uint32_t koff[4], voff[T::VLOADS];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) koff[i] = (uint32_t)(((4 * skb + i) * rs + 8 * skd) * 2);
+#pragma unroll
+  for (int i = 0; i < T::VLOADS; ++i) {
+    const int id = tid + i * T::NT;
+    voff[i] = (uint32_t)(((id / T::CH) * rs + (id % T::CH) * 8) * 2);
+  }
+
+  // Work: self-attention pulls (sequence, 128-row query tile, head) items from the
+  // cost-sorted list; broadcast-Q owns (query tile, head, chunk of items) by block index.
+  const int n_items = BCAST ? 0 : *a.n_entries * a.hq;
+  int bcast_item = blockIdx.x;
+  for (;;) {
+    int b_lo, b_hi, h, qtile;
+    if (BCAST) {
+      if (bcast_item >= a.bcast_units) break;
+      const int per_tile = a.hq * a.bcast_chunks;
+      qtile = bcast_item / per_tile;
+      const int rem = bcast_item % per_tile;
+      h = rem / a.bcast_chunks;
+      const int c = rem % a.bcast_chunks;
+      b_lo = c * a.bcast_chunk;
+      b_hi = min(a.batch, b_lo + a.bcast_chunk);
+      bcast_item += gridDim.x;
+    } else {
+      if (tid == 0) s_item = (int)atomicAdd(a.counter, 1u);
+      __syncthreads();
+      const int item = s_item;
+      if (item >= n_items) break;
+      const WorkEntry e = a.entries[item / a.hq];
+      h = item % a.hq;
+      b_lo = e.b;
+      b_hi = e.b + 1;
+      qtile = e.t;
+    }
+    const int g = h / a.group;
+    const int row0 = qtile * BM;
+    const int my_row = row0 + w * 32 + l32;
+
+    f32x16 dqt[DB];
+#pragma unroll
+    for (int db = 0; db < DB; ++db) dqt[db] = f32x16{};
+
+    for (int b = b_lo; b < b_hi; ++b) {
+      int lq, q_base;
+      if (BCAST) { lq = a.bcast_nq; q_base = 0; }
+      else { q_base = a.cu_q[b]; lq = a.cu_q[b + 1] - q_base; }
+      const int k_base = a.cu_k[b];
+      const int lk = a.cu_k[b + 1] - k_base;
+      const bool row_ok = my_row < lq;
+      const int off = lk - lq;
+
+      int n_tiles, n_bulk;
+      if (CAUSAL) {
+        const int kmax = min(lk, row0 + BM + off);
+        n_tiles = kmax > 0 ? cdiv(kmax, BN) : 0;
+        const int full = min(lk, row0 + off + 1);
+        n_bulk = full > 0 ? full / BN : 0;
+      } else {
+        n_tiles = cdiv(lk, BN);
+        n_bulk = lk / BN;
+      }
+      if (n_tiles == 0) continue;   // uniform
+
+      // per-row state: Q and dO fragments (B operands of S^T = K Q^T, dP^T = V dO^T), LSE, delta
+      bf16x8 qf[KS], df[KS];
+      float lse2 = INF, dlt = 0.f;
+      {
+        const __bf16* qp = a.q + ((int64_t)(q_base + my_row) * a.hq + h) * D + 8 * hh;
+        const int64_t orow = BCAST ? (int64_t)b * lq + my_row : (int64_t)(q_base + my_row);
+        const __bf16* op = a.dout + (orow * a.hq + h) * D + 8 * hh;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          qf[ks] = row_ok ? *(const bf16x8*)(qp + 16 * ks) : zero_bf16x8();
+          df[ks] = row_ok ? *(const bf16x8*)(op + 16 * ks) : zero_bf16x8();
+        }
+        if (row_ok) {
+          const int64_t li = BCAST ? ((int64_t)b * a.hq + h) * lq + my_row : (int64_t)h * a.total_q + q_base + my_row;
+          const float l = a.lse[li];
+          lse2 = (l == NEG_INF) ? INF : l * kLog2e;
+          dlt = a.delta[li];
+        }
+      }
+
+      const __bf16* kbase = a.k + ((int64_t)k_base * a.hkv + g) * D;
+      const __bf16* vbase = a.v + ((int64_t)k_base * a.hkv + g) * D;
+      u32x4 kr[4], vr[T::VLOADS];
+      auto load_regs = [&](int j) {
+        const int64_t tile_off = (int64_t)j * BN * rs;
+        const uint32_t nbytes = (uint32_t)(min(lk - j * BN, BN) * rs * 2);
+        const auto krs = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + tile_off), (short)0, nbytes, kBufferFlags);
+        const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + tile_off), (short)0, nbytes, kBufferFlags);
+        if (k_stager) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            kr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, koff[i], 0, 0));
+        }
+#pragma unroll
+        for (int i = 0; i < T::VLOADS; ++i)
+          vr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff[i], 0, 0));
+      };
+      auto store_lds = [&]() {
+        if (k_stager) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) *(u32x4*)&k_lds[(4 * skb + i) * KP + 8 * skd] = kr[i];
+          store_transposed_4x8(&kt_lds[(8 * skd) * KTP + 16 * (skb >> 2) + 4 * quarter_pos(skb & 3)], KTP, kr);
+        }
+#pragma unroll
+        for (int i = 0; i < T::VLOADS; ++i) {
+          const int id = tid + i * T::NT;
+          *(u32x4*)&v_lds[(id / T::CH) * KP + (id % T::CH) * 8] = vr[i];
+        }
+      };
+
+      auto tile = [&](int j, auto mask_tag) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+        store_lds();
+        __syncthreads();
+        if (j + 1 < n_tiles) load_regs(j + 1);
+        const int kmax_ok = CAUSAL ? min(lk - 1, my_row + off) : lk - 1;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          // S^T[key][q] = K Q^T and dP^T[key][q] = V dO^T for 32 keys
+          f32x16 st = f32x16{}, pt = f32x16{};
+          const __bf16* kp = &k_lds[(32 * kb + l32) * KP + 8 * hh];
+          const __bf16* vp = &v_lds[(32 * kb + l32) * KP + 8 * hh];
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            st = mfma32x32x16(*(const bf16x8*)(kp + 16 * ks), qf[ks], st);
+            pt = mfma32x32x16(*(const bf16x8*)(vp + 16 * ks), df[ks], pt);
+          }
+          float dsv[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float p = fast_exp2(fmaf(st[r], a.scale_log2, -lse2));
+            if constexpr (MASK) {
+              const int key = j * BN + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
+              p = key <= kmax_ok ? p : 0.f;
+            }
+            dsv[r] = p * (pt[r] - dlt);
+          }
+          const bf16x8 sb0 = to_bf16x8(dsv), sb1 = to_bf16x8(dsv + 8);
+          // dQ^T[d][q] += K^T[d][key] dS^T[key][q]
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const __bf16* ktp = &kt_lds[(32 * db + l32) * KTP + 32 * kb + 8 * hh];
+            dqt[db] = mfma32x32x16(*(const bf16x8*)(ktp), sb0, dqt[db]);
+            dqt[db] = mfma32x32x16(*(const bf16x8*)(ktp + 16), sb1, dqt[db]);
+          }
+        }
+        __syncthreads();   // the single LDS stage is refilled by the next tile
+      };
+
+      load_regs(0);
+      for (int j = 0; j < n_bulk; ++j) tile(j, std::false_type{});
+      for (int j = n_bulk; j < n_tiles; ++j) tile(j, std::true_type{});
+    }
+
+    // epilogue: dQ = scale * dQ^T; 4 consecutive d per store
+    const int lq_e = BCAST ? a.bcast_nq : a.cu_q[b_lo + 1] - a.cu_q[b_lo];
+    if (my_row < lq_e) {
+      if (BCAST) {
+        float* dst = a.dq_acc + ((int64_t)my_row * a.hq + h) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            unsafeAtomicAdd(dst + 32 * db + 8 * (r >> 2) + 4 * hh + (r & 3), dqt[db][r]);
+      } else {
+        __bf16* dst = a.dq + ((int64_t)(a.cu_q[b_lo] + my_row) * a.hq + h) * D;
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            bf16x4 v4;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) v4[x] = (__bf16)(dqt[db][4 * r4 + x] * a.scale);
+            *(bf16x4*)(dst + 32 * db + 8 * r4 + 4 * hh) = v4;
+          }
+      }
+    }
+    if (!BCAST) __syncthreads();   // s_item is rewritten by the next pull
+  }
+}
+
+int bwd_dkdv_tile() { return DkvTile<128>::BN; }
+int bwd_dkdv_rows() { return DkvTile<128>::BM; }
+int bwd_dq_rows() { return DqTile<128>::BM; }
+int bwd_dq_tile() { return DqTile<128>::BN; }
 
 template <int D>
-static hipError_t launch_bwd_d(const BwdArgs& a, int grid, hipStream_t stream) {
-  const dim3 g(grid), blk(BwdTile<D>::NT);
-  if (a.bcast_nq > 0)
-    hipLaunchKernelGGL((bwd_kernel<D, false, true>), g, blk, 0, stream, a);
-  else if (a.causal)
-    hipLaunchKernelGGL((bwd_kernel<D, true, false>), g, blk, 0, stream, a);
-  else
-    hipLaunchKernelGGL((bwd_kernel<D, false, false>), g, blk, 0, stream, a);
+static hipError_t launch_dkdv_d(const BwdArgs& a, int grid, hipStream_t stream) {
+  const dim3 g(grid), blk(DkvTile<D>::NT);
+  if (a.bcast_nq > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true>), g, blk, 0, stream, a);
+  else if (a.causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false>), g, blk, 0, stream, a);
+  else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false>), g, blk, 0, stream, a);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdArgs& a, int head_dim, int grid, hipStream_t stream) {
+template <int D>
+static hipError_t launch_dq_d(const BwdArgs& a, int grid, hipStream_t stream) {
+  const dim3 g(grid), blk(DqTile<D>::NT);
+  if (a.bcast_nq > 0) hipLaunchKernelGGL((bwd_dq_kernel<D, false, true>), g, blk, 0, stream, a);
+  else if (a.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true, false>), g, blk, 0, stream, a);
+  else hipLaunchKernelGGL((bwd_dq_kernel<D, false, false>), g, blk, 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int grid, hipStream_t stream) {
   switch (head_dim) {
-    case 64: return launch_bwd_d<64>(a, grid, stream);
-    case 96: return launch_bwd_d<96>(a, grid, stream);
-    case 128: return launch_bwd_d<128>(a, grid, stream);
+    case 64: return launch_dkdv_d<64>(a, grid, stream);
+    case 96: return launch_dkdv_d<96>(a, grid, stream);
+    case 128: return launch_dkdv_d<128>(a, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int grid, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_dq_d<64>(a, grid, stream);
+    case 96: return launch_dq_d<96>(a, grid, stream);
+    case 128: return launch_dq_d<128>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -60,7 +60,7 @@ struct BwdPreArgs {
   const __bf16* o;
   const __bf16* dout;
   float* delta;             // same layout as lse
-  float* dq_acc;            // fp32, same element count as dq; zeroed here
+  float* dq_acc;            // broadcast-Q only (else null): fp32 accumulator, zeroed here
   int64_t rows;             // rows of o / dout (self: total_q, broadcast: B * Nq)
   int32_t hq;
   int32_t head_dim;
@@ -79,23 +79,30 @@ struct BwdArgs {
   const float* delta;
   const int32_t* cu_q;
   const int32_t* cu_k;
-  float* dq_acc;
+  __bf16* dq;
+  float* dq_acc;            // broadcast-Q dQ accumulator
   __bf16* dk;
   __bf16* dv;
-  const WorkEntry* entries;
+  const WorkEntry* entries; // cost-sorted list of the kernel being launched
   const int32_t* n_entries;
   uint32_t* counter;
+  int32_t batch;
   int32_t hq, hkv, group;
   int32_t bcast_nq;
+  int32_t bcast_chunk;      // broadcast-Q dQ: items per chunk
+  int32_t bcast_chunks;     // number of chunks
+  int32_t bcast_units;      // query tiles * heads * chunks
   int32_t total_q;
   int32_t causal;
   float scale;
   float scale_log2;
 };
-hipError_t launch_bwd(const BwdArgs& a, int head_dim, int grid, hipStream_t stream);
-int bwd_block_rows();       // query rows per inner step
-int bwd_kv_tile();          // keys per workgroup
-int bwd_blocks_per_cu(int head_dim);
+hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int grid, hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int grid, hipStream_t stream);
+int bwd_dkdv_tile();        // keys per dK/dV item
+int bwd_dkdv_rows();        // query rows per dK/dV step
+int bwd_dq_rows();          // query rows per dQ item
+int bwd_dq_tile();          // keys per dQ tile
 
 struct DqConvertArgs {
   const float* dq_acc;

@@ -111,17 +111,18 @@ jfa_status_t jfa_fwd(const jfa_attn_params_t* p,
                      void* o, float* lse,
                      void* workspace, size_t workspace_bytes, jfa_stream_t stream);
 
-/* Bytes of workspace jfa_bwd needs (holds delta, an fp32 dQ accumulator and the work list). */
+/* Bytes of workspace jfa_bwd needs (delta, the two work lists, and for broadcast-Q an fp32 dQ accumulator). */
 size_t jfa_bwd_workspace_size(const jfa_attn_params_t* p);
 
 /*
  * Backward: given q, k, v, the forward's o and lse, and dout, writes dq, dk, dv.
  * P is rebuilt from lse; delta = rowsum(dout * o); dP = dout V^T;
  * dS = P * (dP - delta); dV = P^T dout; dK = scale dS^T Q; dQ = scale dS K.
- * dK/dV of a KV head sum over the Hq/Hkv query heads of its group.  dQ is
- * reduced in fp32 with atomic adds (so its low bits depend on timing); in
- * broadcast-Q mode it is the sum over all items.  Keys that no query sees get
- * dK = dV = 0.
+ * dK/dV of a KV head sum over the Hq/Hkv query heads of its group.  Self-
+ * attention results are deterministic (no atomics).  In broadcast-Q mode dQ is
+ * the sum over all items, accumulated in fp32 with atomic adds across chunks
+ * of items, so its last bits may vary between runs.  Keys that no query sees
+ * get dK = dV = 0; queries that see no key get dQ = 0.
  */
 jfa_status_t jfa_bwd(const jfa_attn_params_t* p,
                      const void* q, const void* k, const void* v,
@@ -178,15 +179,18 @@ int jfa_abi_version(void);
 
 /*
  * Optional kernel timing.  While enabled, every call records a pair of HIP
- * events on its stream around the launch of its main kernel (the attention
- * kernel of jfa_fwd, the main backward kernel of jfa_bwd, the split kernel of
- * jfa_decode_paged).  jfa_timing_collect() waits for the recorded events, adds
- * their elapsed milliseconds per entry point into total_ms[0..2] (fwd, bwd,
- * decode) and the number of launches into count[0..2], then releases them.
- * Either output may be NULL.  Intended for benchmarks; off by default.
+ * events on its stream around the launch of each of its main kernels: the
+ * attention kernel of jfa_fwd (slot JFA_TIMING_FWD), the dQ and the dK/dV
+ * kernels of jfa_bwd (JFA_TIMING_BWD_DQ, JFA_TIMING_BWD_DKDV) and the split
+ * kernel of jfa_decode_paged (JFA_TIMING_DECODE).  jfa_timing_collect() waits
+ * for the recorded events, writes per slot the summed elapsed milliseconds into
+ * total_ms[slot] and the number of launches into count[slot], then releases
+ * them.  Either output may be NULL.  Intended for benchmarks; off by default.
  */
+enum { JFA_TIMING_FWD = 0, JFA_TIMING_BWD_DQ = 1, JFA_TIMING_BWD_DKDV = 2, JFA_TIMING_DECODE = 3,
+       JFA_TIMING_SLOTS = 4 };
 jfa_status_t jfa_timing_enable(int enable);
-jfa_status_t jfa_timing_collect(double total_ms[3], int64_t count[3]);
+jfa_status_t jfa_timing_collect(double total_ms[JFA_TIMING_SLOTS], int64_t count[JFA_TIMING_SLOTS]);
 
 #ifdef __cplusplus
 }
