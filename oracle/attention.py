@@ -1,6 +1,6 @@
 """fp64 CPU oracle for exact attention over jagged packed sequences.
 
-TEST INFRASTRUCTURE ONLY.  This module is the checker the GPU path is held to.
+TEST INFRASTRUCTURE ONLY.  This module is the reference the GPU path is held to.
 Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
 ``bench.py`` may import it; the product (the HIP library and its Python
 binding) never calls it and shares no code with it.
@@ -33,7 +33,7 @@ Definitions followed (notation of the pages):
             PR 1999/2104 and PR 2186 sections; paging and KV splitting change
             the memory layout and the order of reduction, not the result).
 
-Readings where the pages are silent (each also listed in the design notes):
+Readings where the pages are silent:
   * causal masking is bottom-right aligned: key j is visible to query i iff
     j <= i + (Lk - Lq); identical to top-left when Lq == Lk;
   * GQA: query head h uses kv head h // (Hq / Hkv);
