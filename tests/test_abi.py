@@ -76,7 +76,9 @@ def test_null_pointers_and_small_workspace():
     assert lib.jfa_fwd(ctypes.byref(p), None, d, d, d, d, d, d, d, need, None) == L.JFA_ERR_INVALID_ARGUMENT
     assert lib.jfa_fwd(ctypes.byref(p), d, d, d, d, d, d, d, d, need - 1, None) == L.JFA_ERR_WORKSPACE_TOO_SMALL
     nb = lib.jfa_bwd_workspace_size(ctypes.byref(p))
-    assert nb > 10 * 4 * 128 * 4      # holds at least the fp32 dQ accumulator
+    assert nb >= 4 * 10 * 4           # at least delta (fp32 per query row and head)
+    pb = _params(L, broadcast_q=1)
+    assert lib.jfa_bwd_workspace_size(ctypes.byref(pb)) >= 10 * 4 * 128 * 4   # + the fp32 dQ accumulator
     assert lib.jfa_bwd(ctypes.byref(p), d, d, d, d, d, d, d, d, d, d, d, d, nb - 1, None) == L.JFA_ERR_WORKSPACE_TOO_SMALL
     assert lib.jfa_bwd(ctypes.byref(p), d, d, d, None, d, d, d, d, d, d, d, d, nb, None) == L.JFA_ERR_INVALID_ARGUMENT
 
