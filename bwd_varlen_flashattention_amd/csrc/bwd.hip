@@ -257,8 +257,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       if (tid < BM) { lse_lds[buf][tid] = lse_r; dlt_lds[buf][tid] = dlt_r; }
     };
 
-    auto step = [&](int s, auto mask_tag) {
-      constexpr bool MASK = decltype(mask_tag)::value;
+    auto step = [&](int s) {
       const int buf = s & 1;
       const int qt = i_first + s % n_qt;
       if (s + 1 < n_steps) load_regs(s + 1);
@@ -284,7 +283,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
           for (int x = 0; x < 4; ++x) {
             const int r = 4 * r4 + x;
             float p = fast_exp2(fmaf(sacc[r], a.scale_log2, -l4[x]));
-            if constexpr (MASK) p = (my_key <= qt * BM + q0 + x + off) ? p : 0.f;
+            if constexpr (CAUSAL) p = (my_key <= qt * BM + q0 + x + off) ? p : 0.f;
             pv[r] = p;
             dsv[r] = p * (pacc[r] - d4[x]);
           }
@@ -310,12 +309,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       load_regs(0);
       store_lds(0);
       __syncthreads();
-      for (int s = 0; s < n_steps; ++s) {
-        bool mask = false;
-        if (CAUSAL) mask = kt0 + BN - 1 > (i_first + s % n_qt) * BM + off;   // some key above the diagonal
-        if (mask) step(s, std::true_type{});
-        else step(s, std::false_type{});
-      }
+      // causal masking is one compare per element in every step: a single step
+      // body keeps the register allocation of the causal kernel free of spills
+      for (int s = 0; s < n_steps; ++s) step(s);
     }
 
     // epilogue: dK = scale * dK^T, dV = dV^T, 4 consecutive d per 8-byte store
