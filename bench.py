@@ -117,6 +117,103 @@ class DecodeCase:
                                   workspace=self.ws)
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_gem_s0.5_bench_step.txt")
+KERNEL_SLOTS = (("bwd_dkdv_kernel", "bwd_dkdv"), ("bwd_dq_kernel", "bwd_dq"), ("fwd_kernel", "fwd"),
+                ("decode_kernel", "decode"))
+
+
+def source_digest() -> str:
+    """Digest of the kernel sources and build options: stored counter data is only
+    reported while it still describes the kernels that run."""
+    import hashlib
+    pkg = os.path.join(ROOT, "bwd_varlen_flashattention_amd")
+    files = [os.path.join(pkg, "csrc", f) for f in sorted(os.listdir(os.path.join(pkg, "csrc")))]
+    h = hashlib.sha256()
+    for f in files + [os.path.join(pkg, "build.py")]:
+        h.update(os.path.basename(f).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def stored_traffic(sparsity: float):
+    """HBM bytes per launch of each main kernel from the committed counter summary, or None."""
+    if abs(sparsity - 0.5) > 1e-9 or not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    for line in open(TRAFFIC_PROFILE):
+        if line.startswith('{"source_digest"'):
+            rec = json.loads(line)
+            return rec["bytes_per_launch"] if rec["source_digest"] == source_digest() else None
+    return None
+
+
+def pmc_summary(fetch_db: str, write_db: str, copy_mib: int, out: str):
+    """Turn two rocprofv3 --pmc databases of this benchmark (FETCH_SIZE, then WRITE_SIZE)
+    into per-launch byte counts, scaled by what the same counters read for the plain
+    device copy of copy_mib MiB that the benchmark runs after timing."""
+    import collections
+    import sqlite3
+
+    def per_dispatch(db, counter):
+        val, name = collections.defaultdict(float), {}
+        con = sqlite3.connect(db)
+        q = "select kernel_name, counter_name, value, dispatch_id from counters_collection"
+        for kname, cname, v, disp in con.execute(q):
+            if cname == counter:
+                val[disp] += v           # sum the per-XCD / per-channel instances of one dispatch
+                name[disp] = kname
+        return val, name
+
+    known = copy_mib * float(1 << 20)
+    res = {}
+    for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
+        val, name = per_dispatch(db, counter)
+        copies = [d for d in val if "copy" in name[d].lower()]
+        if not copies:
+            raise SystemExit(f"no copy kernel among the dispatches of {db}")
+        cal = max(copies, key=lambda d: val[d])
+        factor = known / (val[cal] * 1024.0)
+        kib = collections.defaultdict(list)
+        for d, v in val.items():
+            for key, slot in KERNEL_SLOTS:
+                if key in name[d]:
+                    kib[slot].append(v)
+        res[counter] = (factor, val[cal], {k: sum(v) / len(v) for k, v in kib.items()})
+    ff, fcal, fk = res["FETCH_SIZE"]
+    wf, wcal, wk = res["WRITE_SIZE"]
+    bytes_per = {s: fk.get(s, 0.0) * 1024.0 * ff + wk.get(s, 0.0) * 1024.0 * wf for _, s in KERNEL_SLOTS if s in fk}
+    lines = [
+        "# HBM traffic per launch: bench step (GEM jagged fwd+bwd, sparsity 0.5, + paged decode, page 16)",
+        "",
+        "Commands (repository root on the MI355X box = $REPO; one counter per run):",
+        "",
+        "```",
+        "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -d $REPO/gpurun_out/pmc_fetch -o fetch "
+        "-- python3 $REPO/bench.py --steps 2 --warmup 1 --cpu-seqs 0",
+        "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE -d $REPO/gpurun_out/pmc_write -o write "
+        "-- python3 $REPO/bench.py --steps 2 --warmup 1 --cpu-seqs 0",
+        "python3 bench.py --pmc-summary gpurun_out/pmc_fetch/fetch_results.db gpurun_out/pmc_write/write_results.db",
+        "```",
+        "",
+        f"Calibration: the benchmark's plain device copy of {copy_mib} MiB reads {fcal:.0f} KiB (FETCH_SIZE) and "
+        f"writes {wcal:.0f} KiB (WRITE_SIZE); scale factors {ff:.4f} (fetch) and {wf:.4f} (write) map the "
+        "counters to bytes.  FETCH_SIZE counts L2 misses served by the memory side, so reads that hit the "
+        "last-level MALL count too.",
+        "",
+        "| kernel | FETCH_SIZE (KiB/launch) | WRITE_SIZE (KiB/launch) | scaled bytes/launch |",
+        "|---|---|---|---|",
+    ]
+    for _, s in KERNEL_SLOTS:
+        if s in bytes_per:
+            lines.append(f"| {s} | {fk[s]:.0f} | {wk.get(s, 0.0):.0f} | {bytes_per[s]:.4g} |")
+    lines += ["", "Machine-readable line (the digest covers the kernel sources and build options):", ""]
+    lines.append(json.dumps({"source_digest": source_digest(), "workload": "gem_s0.5",
+                             "fetch_factor": ff, "write_factor": wf, "bytes_per_launch": bytes_per}))
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def cpu_baseline(inp, n_seq: int):
     """Time the fp64 oracle on the first n_seq sequences of the same workload (fwd + bwd)."""
     import oracle
@@ -149,7 +246,11 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="one JSON line per workload (GEM s, broadcast-Q, dense, decode)")
     ap.add_argument("--copy-calibration-mib", type=int, default=1024,
                     help="run one device copy of this size after timing (reference for HBM byte counters)")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
+                    help="summarise two rocprofv3 --pmc runs of this benchmark into the traffic profile and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        return pmc_summary(*args.pmc_summary, args.copy_calibration_mib, TRAFFIC_PROFILE)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -222,6 +323,9 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    stored = stored_traffic(args.sparsity)
+    traffic = round(stored[dominant]) if stored and dominant in stored else None
+
     cpu = None
     if args.cpu_seqs > 0:
         cpu = cpu_baseline(gem_inp, min(args.cpu_seqs, gem_inp.batch))
@@ -256,7 +360,7 @@ def main():
         "kernels_ms": {k: round(v, 4) for k, v in avg.items()},
         "roofline": {"kernel": names[dominant], "bound": "mfma",
                      "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
                      "algorithmic_flop_per_launch": alg[dominant]},
         "cpu_baseline": cpu,
     }
