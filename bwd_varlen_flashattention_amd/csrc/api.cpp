@@ -92,17 +92,19 @@ float eff_scale(float s, int d) { return s > 0.f ? s : 1.0f / sqrtf((float)d); }
 
 // ------------------------------------------------------------------ workspace layouts
 struct SchedLayout {
-  size_t entries = 0, n_entries = 0, counter = 0, end = 0;
-  int max_entries = 0;
+  size_t items = 0, scratch = 0, queues = 0, end = 0;
+  int max_items = 0;
 };
 
-SchedLayout sched_layout(size_t base, int64_t max_entries) {
+// Work list of one persistent kernel: max_items items, per-group scratch for
+// `groups` (sequence, KV head) groups, and the per-XCD queue descriptors.
+SchedLayout sched_layout(size_t base, int64_t max_items, int64_t groups) {
   SchedLayout l;
-  l.max_entries = (int)max_entries;
-  l.entries = base;
-  l.n_entries = align_up(l.entries + (size_t)max_entries * sizeof(WorkEntry));
-  l.counter = align_up(l.n_entries + sizeof(int32_t));
-  l.end = align_up(l.counter + sizeof(uint32_t));
+  l.max_items = (int)max_items;
+  l.items = align_up(base);
+  l.scratch = align_up(l.items + (size_t)max_items * sizeof(WorkItem));
+  l.queues = align_up(l.scratch + (size_t)groups * 4 * sizeof(int32_t));
+  l.end = align_up(l.queues + sizeof(WorkQueues));
   return l;
 }
 
@@ -119,6 +121,10 @@ int64_t dkdv_max_entries(const jfa_attn_params_t* p) {
 int64_t dq_max_entries(const jfa_attn_params_t* p) {
   if (p->broadcast_q) return 0;   // broadcast-Q dQ work is indexed directly
   return cdiv_i(p->total_q, bwd_dq_rows()) + (int64_t)p->batch;
+}
+
+SchedLayout fwd_list(const jfa_attn_params_t* p) {
+  return sched_layout(0, fwd_max_entries(p) * p->num_heads_q, (int64_t)p->batch * p->num_heads_kv);
 }
 
 int64_t lse_elems(const jfa_attn_params_t* p) {
@@ -139,14 +145,28 @@ BwdLayout bwd_layout(const jfa_attn_params_t* p) {
     l.dq_acc = next;
     next = align_up(next + (size_t)p->total_q * p->num_heads_q * p->head_dim * sizeof(float));
   }
-  l.dq_list = sched_layout(next, dq_max_entries(p));
-  l.dkdv_list = sched_layout(l.dq_list.end, dkdv_max_entries(p));
+  const int64_t groups = (int64_t)p->batch * p->num_heads_kv;
+  l.dq_list = sched_layout(next, dq_max_entries(p) * p->num_heads_q, p->broadcast_q ? 0 : groups);
+  l.dkdv_list = sched_layout(l.dq_list.end, dkdv_max_entries(p) * p->num_heads_kv, groups);
   l.end = l.dkdv_list.end;
   return l;
 }
 
 template <typename T>
 T* at(void* ws, size_t off) { return (T*)((char*)ws + off); }
+
+// Work-list fields of the scheduler arguments shared by every launch.
+void set_lists(SchedArgs& sa, const jfa_attn_params_t* p, void* ws, const SchedLayout& L) {
+  // one item group per (sequence, KV head); a query-stationary tile has one item
+  // per query head of the GQA group, a key-stationary tile one item
+  sa.groups_per_seq = p->num_heads_kv;
+  sa.per_tile = sa.mode == 0 ? p->num_heads_q / p->num_heads_kv : 1;
+  sa.n_buckets = kMaxBuckets;
+  sa.max_items = L.max_items;
+  sa.scratch = at<int32_t>(ws, L.scratch);
+  sa.items = at<WorkItem>(ws, L.items);
+  sa.queues = at<WorkQueues>(ws, L.queues);
+}
 
 jfa_status_t hip_status(hipError_t e) { return e == hipSuccess ? JFA_OK : JFA_ERR_HIP; }
 
@@ -202,7 +222,7 @@ const char* jfa_status_string(jfa_status_t s) {
 
 size_t jfa_fwd_workspace_size(const jfa_attn_params_t* p) {
   if (check_attn(p) != JFA_OK) return 0;
-  return sched_layout(0, fwd_max_entries(p)).end;
+  return fwd_list(p).end;
 }
 
 jfa_status_t jfa_fwd(const jfa_attn_params_t* p, const void* q, const void* k, const void* v,
@@ -214,8 +234,8 @@ jfa_status_t jfa_fwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   if (!q || !o || !lse || !cu_seqlens_k) return JFA_ERR_INVALID_ARGUMENT;
   if (!p->broadcast_q && !cu_seqlens_q) return JFA_ERR_INVALID_ARGUMENT;
   if (p->total_k > 0 && (!k || !v)) return JFA_ERR_INVALID_ARGUMENT;
-  const SchedLayout L = sched_layout(0, fwd_max_entries(p));
-  if (!workspace) return JFA_ERR_INVALID_ARGUMENT;
+  const SchedLayout L = fwd_list(p);
+  if (!workspace || ((uintptr_t)workspace % kAlign) != 0) return JFA_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < L.end) return JFA_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t stream = (hipStream_t)stream_;
 
@@ -229,11 +249,7 @@ jfa_status_t jfa_fwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   sa.mode = 0;
   sa.causal = p->causal;
   sa.bcast_nq = p->broadcast_q ? p->total_q : 0;
-  sa.n_buckets = std::min(kMaxBuckets, cdiv_i(p->max_seqlen_k, bn) + 1);
-  sa.max_entries = L.max_entries;
-  sa.entries = at<WorkEntry>(workspace, L.entries);
-  sa.n_entries = at<int32_t>(workspace, L.n_entries);
-  sa.counter = at<uint32_t>(workspace, L.counter);
+  set_lists(sa, p, workspace, L);
   hipError_t e = launch_sched(sa, stream);
   if (e != hipSuccess) return JFA_ERR_HIP;
 
@@ -245,9 +261,8 @@ jfa_status_t jfa_fwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   fa.cu_k = cu_seqlens_k;
   fa.o = (__bf16*)o;
   fa.lse = lse;
-  fa.entries = sa.entries;
-  fa.n_entries = sa.n_entries;
-  fa.counter = sa.counter;
+  fa.items = sa.items;
+  fa.queues = sa.queues;
   fa.hq = p->num_heads_q;
   fa.hkv = p->num_heads_kv;
   fa.group = p->num_heads_q / p->num_heads_kv;
@@ -255,7 +270,7 @@ jfa_status_t jfa_fwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   fa.total_q = p->total_q;
   fa.causal = p->causal;
   fa.scale_log2 = eff_scale(p->softmax_scale, p->head_dim) * 1.4426950408889634f;
-  const int64_t max_items = (int64_t)L.max_entries * p->num_heads_q;
+  const int64_t max_items = L.max_items;
   const int grid = (int)std::min<int64_t>((int64_t)cu_count() * fwd_blocks_per_cu(p->head_dim), max_items);
   TimedRegion tr(JFA_TIMING_FWD, stream);
   e = launch_fwd(fa, p->head_dim, std::max(grid, 1), stream);
@@ -279,7 +294,7 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   if (p->total_q > 0 && (!q || !o || !lse || !dout || !dq)) return JFA_ERR_INVALID_ARGUMENT;
   if (p->total_k > 0 && (!k || !v || !dk || !dv)) return JFA_ERR_INVALID_ARGUMENT;
   const BwdLayout L = bwd_layout(p);
-  if (!workspace) return JFA_ERR_INVALID_ARGUMENT;
+  if (!workspace || ((uintptr_t)workspace % kAlign) != 0) return JFA_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < L.end) return JFA_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t stream = (hipStream_t)stream_;
   const float scale = eff_scale(p->softmax_scale, p->head_dim);
@@ -350,17 +365,12 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
       sa.mode = 0;
       sa.causal = p->causal;
       sa.bcast_nq = 0;
-      sa.n_buckets = std::min(kMaxBuckets, cdiv_i(p->max_seqlen_k, bwd_dq_tile()) + 1);
-      sa.max_entries = L.dq_list.max_entries;
-      sa.entries = at<WorkEntry>(workspace, L.dq_list.entries);
-      sa.n_entries = at<int32_t>(workspace, L.dq_list.n_entries);
-      sa.counter = at<uint32_t>(workspace, L.dq_list.counter);
+      set_lists(sa, p, workspace, L.dq_list);
       e = launch_sched(sa, stream);
       if (e != hipSuccess) return JFA_ERR_HIP;
-      ba.entries = sa.entries;
-      ba.n_entries = sa.n_entries;
-      ba.counter = sa.counter;
-      const int64_t max_items = (int64_t)L.dq_list.max_entries * p->num_heads_q;
+      ba.items = sa.items;
+      ba.queues = sa.queues;
+      const int64_t max_items = L.dq_list.max_items;
       TimedRegion tr(JFA_TIMING_BWD_DQ, stream);
       e = launch_bwd_dq(ba, p->head_dim, (int)std::max<int64_t>(1, std::min<int64_t>(2LL * cus, max_items)), stream);
       tr.finish();
@@ -379,18 +389,12 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
     sa.mode = 1;
     sa.causal = p->causal;
     sa.bcast_nq = p->broadcast_q ? p->total_q : 0;
-    const int maxq = p->broadcast_q ? p->total_q : p->max_seqlen_q;
-    sa.n_buckets = std::min(kMaxBuckets, cdiv_i(maxq, bwd_dkdv_rows()) + 1);
-    sa.max_entries = L.dkdv_list.max_entries;
-    sa.entries = at<WorkEntry>(workspace, L.dkdv_list.entries);
-    sa.n_entries = at<int32_t>(workspace, L.dkdv_list.n_entries);
-    sa.counter = at<uint32_t>(workspace, L.dkdv_list.counter);
+    set_lists(sa, p, workspace, L.dkdv_list);
     e = launch_sched(sa, stream);
     if (e != hipSuccess) return JFA_ERR_HIP;
-    ba.entries = sa.entries;
-    ba.n_entries = sa.n_entries;
-    ba.counter = sa.counter;
-    const int64_t max_items = (int64_t)L.dkdv_list.max_entries * p->num_heads_kv;
+    ba.items = sa.items;
+    ba.queues = sa.queues;
+    const int64_t max_items = L.dkdv_list.max_items;
     TimedRegion tr(JFA_TIMING_BWD_DKDV, stream);
     e = launch_bwd_dkdv(ba, p->head_dim, (int)std::max<int64_t>(1, std::min<int64_t>(cus, max_items)), stream);
     tr.finish();
@@ -428,7 +432,7 @@ jfa_status_t jfa_decode_paged(const jfa_decode_params_t* p, const void* q, const
   if (!q || !k_cache || !v_cache || !page_table || !seqlens_k || !o || !lse) return JFA_ERR_INVALID_ARGUMENT;
   const int splits = resolve_splits(p);
   const size_t need = decode_ws(p, splits);
-  if (need > 0 && !workspace) return JFA_ERR_INVALID_ARGUMENT;
+  if (need > 0 && (!workspace || ((uintptr_t)workspace % kAlign) != 0)) return JFA_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < need) return JFA_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t stream = (hipStream_t)stream_;
 

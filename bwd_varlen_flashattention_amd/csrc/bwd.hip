@@ -157,11 +157,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) float lse_lds[2][BM];
   __shared__ __attribute__((aligned(16))) float dlt_lds[2][BM];
   __shared__ int s_item;
+  __shared__ int s_queue[2 * kQueues];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int n_items = *a.n_entries * a.hkv;
   const float INF = __builtin_inff();
 
   // staging: thread owns rows 4*sq..4*sq+3, columns 8*sd..8*sd+7 of the Q and dO tiles
@@ -172,13 +172,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) qoff[i] = (uint32_t)(((4 * sq + i) * qrs + 8 * sd) * 2);
 
+  int home_q = blockIdx.x % kQueues, drained = 0;   // work-queue state (thread 0)
+  load_queues(a.queues, s_queue);
+  __syncthreads();
   for (;;) {
-    if (tid == 0) s_item = (int)atomicAdd(a.counter, 1u);
+    if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
     __syncthreads();
     const int item = s_item;
-    if (item >= n_items) break;
-    const WorkEntry e = a.entries[item / a.hkv];
-    const int g = item % a.hkv;
+    if (item < 0) break;
+    const WorkItem e = a.items[item];
+    const int g = e.h;
     const int b = e.b;
     int lq, q_base;
     if (BCAST) { lq = a.bcast_nq; q_base = 0; }
@@ -210,12 +213,21 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) { dkt[db] = f32x16{}; dvt[db] = f32x16{}; }
 
-    // step s -> (query head, query tile); rows past Lq read as zero (buffer range)
+    // step s -> unit u -> (query head, query tile); rows past Lq read as zero
+    // (buffer range).  The units start at a rotation that differs between the key
+    // tiles of one (sequence, KV head): those run at the same time on one XCD and
+    // would otherwise request the same Q/dO lines at the same moment.
+    const int rot = n_steps > 1 ? (int)(((int64_t)e.t * n_steps) / cdiv(lk, BN)) % n_steps : 0;
+    auto unit_of = [&](int s) {
+      const int u = s + rot;
+      return u >= n_steps ? u - n_steps : u;
+    };
     u32x4 qr[4], dr[4];
     float lse_r = 0.f, dlt_r = 0.f;
     auto load_regs = [&](int s) {
-      const int h = g * a.group + s / n_qt;
-      const int qt = i_first + s % n_qt;
+      const int u = unit_of(s);
+      const int h = g * a.group + u / n_qt;
+      const int qt = i_first + u % n_qt;
       const int row0 = qt * BM;
       const uint32_t nbytes = (uint32_t)(min(lq - row0, BM) * qrs * 2);
       const __bf16* qb = a.q + ((int64_t)(q_base + row0) * a.hq + h) * D;
@@ -259,7 +271,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 
     auto step = [&](int s) {
       const int buf = s & 1;
-      const int qt = i_first + s % n_qt;
+      const int qt = i_first + unit_of(s) % n_qt;
       if (s + 1 < n_steps) load_regs(s + 1);
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
@@ -360,6 +372,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 v_lds[BN * KP];
   __shared__ __attribute__((aligned(16))) __bf16 kt_lds[D * KTP];
   __shared__ int s_item;
+  __shared__ int s_queue[2 * kQueues];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -381,9 +394,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
   }
 
   // Work: self-attention pulls (sequence, 128-row query tile, head) items from the
-  // cost-sorted list; broadcast-Q owns (query tile, head, chunk of items) by block index.
-  const int n_items = BCAST ? 0 : *a.n_entries * a.hq;
+  // per-XCD work queues; broadcast-Q owns (query tile, head, chunk of items) by block index.
   int bcast_item = blockIdx.x;
+  int home_q = blockIdx.x % kQueues, drained = 0;   // work-queue state (thread 0)
+  if (!BCAST) {   // broadcast-Q runs without a work list (a.queues is null)
+    load_queues(a.queues, s_queue);
+    __syncthreads();
+  }
   for (;;) {
     int b_lo, b_hi, h, qtile;
     if (BCAST) {
@@ -397,12 +414,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       b_hi = min(a.batch, b_lo + a.bcast_chunk);
       bcast_item += gridDim.x;
     } else {
-      if (tid == 0) s_item = (int)atomicAdd(a.counter, 1u);
+      if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
       __syncthreads();
       const int item = s_item;
-      if (item >= n_items) break;
-      const WorkEntry e = a.entries[item / a.hq];
-      h = item % a.hq;
+      if (item < 0) break;
+      const WorkItem e = a.items[item];
+      h = e.h;
       b_lo = e.b;
       b_hi = e.b + 1;
       qtile = e.t;
@@ -486,11 +503,23 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         }
       };
 
-      auto tile = [&](int j, auto mask_tag) {
+      // Key-tile order: bulk tiles rotated per (query tile, GQA head) so that the
+      // items sharing this K/V, which run together on one XCD, read different K/V
+      // lines at any moment; masked tiles last.
+      const int rot_cnt = cdiv(lq, BM) * a.group;
+      const int rot = n_bulk > 1 ? (int)(((int64_t)(qtile * a.group + h % a.group) * n_bulk) / rot_cnt) % n_bulk : 0;
+      auto tile_of = [&](int s) {
+        if (s >= n_bulk) return s;
+        const int j = s + rot;
+        return j >= n_bulk ? j - n_bulk : j;
+      };
+
+      auto tile = [&](int s, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
+        const int j = tile_of(s);
         store_lds();
         __syncthreads();
-        if (j + 1 < n_tiles) load_regs(j + 1);
+        if (s + 1 < n_tiles) load_regs(tile_of(s + 1));
         const int kmax_ok = CAUSAL ? min(lk - 1, my_row + off) : lk - 1;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
@@ -525,9 +554,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         __syncthreads();   // the single LDS stage is refilled by the next tile
       };
 
-      load_regs(0);
-      for (int j = 0; j < n_bulk; ++j) tile(j, std::false_type{});
-      for (int j = n_bulk; j < n_tiles; ++j) tile(j, std::true_type{});
+      load_regs(tile_of(0));
+      for (int s = 0; s < n_bulk; ++s) tile(s, std::false_type{});
+      for (int s = n_bulk; s < n_tiles; ++s) tile(s, std::true_type{});
     }
 
     // epilogue: dQ = scale * dQ^T; 4 consecutive d per store

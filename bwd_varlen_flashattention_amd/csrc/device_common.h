@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "jfa_internal.h"
+
 namespace jfa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -75,5 +77,25 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
 }
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Work-queue hand-out for persistent workgroups.  The queue starts and sizes
+// are copied into LDS once (load_queues, by all threads, followed by a barrier);
+// next_work_item is then called by one thread.  `q` starts at the block's home
+// queue, blockIdx.x % kQueues, and `drained` at 0; queues are visited
+// cyclically and a queue found empty stays empty, so after kQueues empty
+// visits every queue is drained and -1 is returned.
+__device__ __forceinline__ void load_queues(const WorkQueues* wq, int* s_queue) {
+  const int t = threadIdx.x;
+  if (t < 2 * kQueues) s_queue[t] = t < kQueues ? wq->start[t] : wq->size[t - kQueues];
+}
+__device__ __forceinline__ int next_work_item(WorkQueues* wq, const int* s_queue, int& q, int& drained) {
+  while (drained < kQueues) {
+    const uint32_t i = atomicAdd(&wq->next[q].value, 1u);
+    if (i < (uint32_t)s_queue[kQueues + q]) return s_queue[q] + (int)i;
+    q = (q + 1) & (kQueues - 1);
+    ++drained;
+  }
+  return -1;
+}
 
 }  // namespace jfa

@@ -9,7 +9,8 @@
 //
 // How it maps to CDNA4:
 //   * persistent workgroups pull (sequence, 128-row query tile, head) items from
-//     the cost-sorted list built by sched.hip;
+//     the per-XCD queues built by sched.hip, where the tiles sharing one K/V run
+//     back to back on one XCD and so share its L2;
 //   * 4 waves, each owning 32 query rows whose Q fragment stays in VGPRs for the
 //     whole key loop;
 //   * two workgroups per CU (two waves per SIMD), so one wave's softmax VALU
@@ -66,11 +67,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][BN * KP];
   __shared__ __attribute__((aligned(16))) __bf16 vt_lds[2][D * VTP];
   __shared__ int s_item;
+  __shared__ int s_queue[2 * kQueues];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hh = lane >> 5;
-  const int n_items = *a.n_entries * a.hq;
   const float NEG_INF = -__builtin_inff();
 
   // byte offsets of this thread's staging loads inside a KV tile (row stride rs elements)
@@ -86,13 +87,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)(((4 * vkb + i) * rs + vdb * 8) * 2);
 
+  int home_q = blockIdx.x % kQueues, drained = 0;   // work-queue state (thread 0)
+  load_queues(a.queues, s_queue);
+  __syncthreads();
   for (;;) {
-    if (tid == 0) s_item = (int)atomicAdd(a.counter, 1u);
+    if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
     __syncthreads();
     const int item = s_item;
-    if (item >= n_items) break;
-    const WorkEntry e = a.entries[item / a.hq];
-    const int h = item % a.hq;
+    if (item < 0) break;
+    const WorkItem e = a.items[item];
+    const int h = e.h;
     const int g = h / a.group;
     const int b = e.b;
 
@@ -175,12 +179,25 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       }
     };
 
-    // One KV tile.  MASK selects the tail / causal-diagonal variant; the bulk
-    // variant has no per-element masking at all (loop peeling).
-    auto tile = [&](int j, auto mask_tag) {
+    // Key-tile order: the bulk tiles start at a rotation that differs between the
+    // query tiles (and GQA heads) sharing this K/V, which run at the same time on
+    // one XCD and would otherwise request the same K/V lines at the same moment;
+    // the masked tiles come last.
+    const int rot_cnt = cdiv(lq, BM) * a.group;
+    const int rot = n_bulk > 1 ? (int)(((int64_t)(e.t * a.group + h % a.group) * n_bulk) / rot_cnt) % n_bulk : 0;
+    auto tile_of = [&](int s) {
+      if (s >= n_bulk) return s;
+      const int j = s + rot;
+      return j >= n_bulk ? j - n_bulk : j;
+    };
+
+    // Step s visits key tile j = tile_of(s).  MASK selects the tail / causal-diagonal
+    // variant; the bulk variant has no per-element masking at all (loop peeling).
+    auto tile = [&](int step, auto mask_tag) {
       constexpr bool MASK = decltype(mask_tag)::value;
-      const int buf = j & 1;
-      if (j + 1 < n_tiles) load_regs(j + 1);
+      const int buf = step & 1;
+      const int j = tile_of(step);
+      if (step + 1 < n_tiles) load_regs(tile_of(step + 1));
 
       // S^T[key][query] for two 32-key blocks
       f32x16 s[2];
@@ -248,18 +265,18 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
             acc[db] = mfma32x32x16(*(const bf16x8*)(vp + 16 * (2 * kb + t)), pb[kb][t], acc[db]);
       }
 
-      if (j + 1 < n_tiles) store_lds(buf ^ 1);
+      if (step + 1 < n_tiles) store_lds(buf ^ 1);
       __syncthreads();
     };
 
     // The loops are only reachable through the prologue, whose wait covers the
     // Q-fragment loads; otherwise every tile would wait on all outstanding loads.
     if (n_tiles > 0) {
-      load_regs(0);
+      load_regs(tile_of(0));
       store_lds(0);
       __syncthreads();
-      for (int j = 0; j < n_bulk; ++j) tile(j, std::false_type{});
-      for (int j = n_bulk; j < n_tiles; ++j) tile(j, std::true_type{});
+      for (int s = 0; s < n_bulk; ++s) tile(s, std::false_type{});
+      for (int s = n_bulk; s < n_tiles; ++s) tile(s, std::true_type{});
     }
 
     // epilogue: O = acc / l, LSE = (m + log2 l) * ln 2

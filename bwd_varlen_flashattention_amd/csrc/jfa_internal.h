@@ -6,27 +6,52 @@
 
 namespace jfa {
 
-// One work-list entry: (sequence or item b, tile index t along the stationary axis).
-struct WorkEntry {
+// Work queues: one per XCD.  Workgroups are dispatched to the XCDs round robin
+// by block index, so block i serves queue i % kQueues first and steals from the
+// others when its own queue runs dry.
+constexpr int kQueues = 8;
+
+// One work item: sequence (or broadcast item) b, tile t along the stationary
+// axis, head h (a query head for query-stationary kernels, a KV head for the
+// key-stationary one).
+struct WorkItem {
   int32_t b;
   int32_t t;
+  int32_t h;
+  int32_t pad;
 };
 
-// Shape of the cost-sorted work list built on the device from the offsets.
+// Queue descriptors.  start/size are read once per workgroup; each consumer
+// counter sits on a 256-byte line of its own, because every item hand-out is an
+// atomic on it and a shared line becomes the bottleneck of the whole grid.
+struct QueueCounter {
+  uint32_t value;
+  uint32_t pad[63];
+};
+struct WorkQueues {
+  int32_t start[kQueues];   // first item of each queue in the item array
+  int32_t size[kQueues];    // items in each queue
+  uint32_t pad[64 - 2 * kQueues];
+  QueueCounter next[kQueues];   // consumer counters (reset by the scheduler)
+};
+
+// Shape of the work list built on the device from the offsets.
 struct SchedArgs {
   const int32_t* cu_q;      // [B+1] (unused in broadcast-Q mode)
   const int32_t* cu_k;      // [B+1]
   int32_t batch;
+  int32_t groups_per_seq;   // item groups per sequence (the tiles of a group share K/V or Q/dO)
+  int32_t per_tile;         // items per tile of a group: head h = (group index) * per_tile + i
   int32_t stat_tile;        // rows per tile on the stationary axis
   int32_t loop_tile;        // rows per tile on the inner-loop axis
-  int32_t mode;             // 0: query-stationary (forward), 1: key-stationary (backward)
+  int32_t mode;             // 0: query-stationary (one item per query head), 1: key-stationary (per KV head)
   int32_t causal;
   int32_t bcast_nq;         // > 0: broadcast-Q, every item has Lq = bcast_nq
   int32_t n_buckets;        // cost buckets (costs above are clamped into the last one)
-  int32_t max_entries;      // capacity of `entries`
-  WorkEntry* entries;       // sorted by cost, longest first
-  int32_t* n_entries;       // number of valid entries
-  uint32_t* counter;        // reset to 0 for the persistent consumers
+  int32_t max_items;        // capacity of `items`
+  int32_t* scratch;         // 4 * batch * groups_per_seq ints
+  WorkItem* items;          // queue by queue
+  WorkQueues* queues;
 };
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t stream);
@@ -40,9 +65,8 @@ struct FwdArgs {
   const int32_t* cu_k;
   __bf16* o;
   float* lse;
-  const WorkEntry* entries;
-  const int32_t* n_entries;
-  uint32_t* counter;
+  const WorkItem* items;
+  WorkQueues* queues;
   int32_t hq, hkv, group;   // group = hq / hkv
   int32_t bcast_nq;         // > 0: broadcast-Q
   int32_t total_q;          // LSE row stride for self-attention
@@ -83,9 +107,8 @@ struct BwdArgs {
   float* dq_acc;            // broadcast-Q dQ accumulator
   __bf16* dk;
   __bf16* dv;
-  const WorkEntry* entries; // cost-sorted list of the kernel being launched
-  const int32_t* n_entries;
-  uint32_t* counter;
+  const WorkItem* items;    // work list of the kernel being launched
+  WorkQueues* queues;
   int32_t batch;
   int32_t hq, hkv, group;
   int32_t bcast_nq;

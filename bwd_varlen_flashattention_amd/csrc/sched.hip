@@ -1,14 +1,21 @@
-// Device-built, cost-sorted work list for the persistent attention kernels.
+// Device-built work list for the persistent attention kernels.
 //
 // Jagged batches give tiles of very different cost.  The list is built on the
-// device straight from the offsets (no host round trip): every (sequence, tile)
-// entry gets a cost equal to the number of inner-loop tiles it will visit
-// (causal tiles stop at the diagonal), entries are counting-sorted longest
-// first, and persistent workgroups then pull them in that order from an atomic
-// counter, which is a longest-processing-time-first greedy schedule.  This is
-// the software load balancing of jagged tiles and the persistent, on-demand
-// tile hand-out of "Optimizing Jagged Flash Attention with TLX" (fourth and
-// fifth paragraphs), done with a global atomic instead of Cluster Launch Control.
+// device straight from the offsets (no host round trip).  Every tile gets a cost
+// equal to the number of inner-loop tiles it will visit (causal tiles stop at the
+// diagonal).  This is the software load balancing of jagged tiles and the
+// persistent, on-demand tile hand-out of "Optimizing Jagged Flash Attention with
+// TLX" (fourth and fifth paragraphs), with global atomics in place of Cluster
+// Launch Control.
+//
+// The list is organised for the L2 caches as well as for balance.  All tiles of
+// one (sequence, KV head) read the same K/V (query-stationary kernels) or the
+// same Q/dO (key-stationary kernel), so they form a group that is kept together
+// in one queue and handed out back to back.  Groups are counting-sorted by cost,
+// longest first, and dealt to the kQueues per-XCD queues in snake order
+// (0..7, 7..0, ...), which balances the queues while each stays in descending
+// cost order.  Workgroup i serves queue i % kQueues (the XCD it is dispatched
+// to) and steals from the other queues once its own is empty.
 #include "jfa_internal.h"
 #include "device_common.h"
 
@@ -16,6 +23,7 @@ namespace jfa {
 
 constexpr int kSchedThreads = 1024;
 constexpr int kMaxBuckets = 4096;
+constexpr int kPerQueue = kSchedThreads / kQueues;
 
 __device__ __forceinline__ int entry_cost(const SchedArgs& a, int lq, int lk, int t) {
   if (a.mode == 0) {               // query tile t, loop over key tiles
@@ -30,69 +38,159 @@ __device__ __forceinline__ int entry_cost(const SchedArgs& a, int lq, int lk, in
   return first_q < lq ? ntq - first_q / a.loop_tile : 0;
 }
 
-__global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedArgs a) {
-  __shared__ int hist[kMaxBuckets];
-  __shared__ int part[kSchedThreads];
+// Rank r of the cost-sorted groups goes to queue snake(r) as that queue's group r / kQueues.
+__device__ __forceinline__ int snake_queue(int r) {
+  const int round = r / kQueues, pos = r % kQueues;
+  return (round & 1) ? kQueues - 1 - pos : pos;
+}
+__device__ __forceinline__ int snake_rank(int q, int j) {
+  return j * kQueues + ((j & 1) ? kQueues - 1 - q : q);
+}
+
+// Exclusive scan of one value per thread over segments of `seg` consecutive threads.
+// Returns the exclusive prefix; *seg_total receives the segment's total.
+__device__ int segmented_scan(int* part, int x, int seg, int* seg_total) {
   const int tid = threadIdx.x;
-  const int nb = a.n_buckets;
-  for (int i = tid; i < nb; i += kSchedThreads) hist[i] = 0;
+  part[tid] = x;
   __syncthreads();
-
-  // pass 1: histogram of costs (bucket index counts down so the scan sorts longest first)
-  for (int b = tid; b < a.batch; b += kSchedThreads) {
-    const int lq = a.bcast_nq > 0 ? a.bcast_nq : a.cu_q[b + 1] - a.cu_q[b];
-    const int lk = a.cu_k[b + 1] - a.cu_k[b];
-    const int stat_len = a.mode == 0 ? lq : lk;
-    const int nt = cdiv(stat_len, a.stat_tile);
-    for (int t = 0; t < nt; ++t) {
-      const int c = min(entry_cost(a, lq, lk, t), nb - 1);
-      atomicAdd(&hist[nb - 1 - c], 1);
-    }
-  }
-  __syncthreads();
-
-  // pass 2: exclusive scan of the histogram (each thread owns a contiguous run of buckets)
-  const int per = cdiv(nb, kSchedThreads);
-  const int lo = min(tid * per, nb), hi = min(lo + per, nb);
-  int run = 0;
-  for (int i = lo; i < hi; ++i) run += hist[i];
-  part[tid] = run;
-  __syncthreads();
-  for (int off = 1; off < kSchedThreads; off <<= 1) {
-    const int add = tid >= off ? part[tid - off] : 0;
+  for (int off = 1; off < seg; off <<= 1) {
+    const int add = (tid % seg) >= off ? part[tid - off] : 0;
     __syncthreads();
     part[tid] += add;
     __syncthreads();
   }
-  int base = part[tid] - run;            // exclusive prefix of this thread's run
-  for (int i = lo; i < hi; ++i) {
-    const int c = hist[i];
-    hist[i] = base;
-    base += c;
-  }
-  const int total = part[kSchedThreads - 1];
+  const int incl = part[tid];
+  *seg_total = part[(tid / seg) * seg + seg - 1];
+  __syncthreads();
+  return incl - x;
+}
+
+__global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedArgs a) {
+  __shared__ int hist[kMaxBuckets];
+  __shared__ int part[kSchedThreads];
+  __shared__ int q_start[kQueues], q_size[kQueues];
+  const int tid = threadIdx.x;
+  const int nb = a.n_buckets;
+  const int n_groups = a.batch * a.groups_per_seq;
+  const int per_tile = a.per_tile;
+  int* g_items = a.scratch;                   // [n_groups] items of each group
+  int* g_bucket = a.scratch + n_groups;       // [n_groups] cost bucket, -1 when empty
+  int* order = a.scratch + 2 * n_groups;      // [n_groups] group of each rank
+  int* r_off = a.scratch + 3 * n_groups;      // [n_groups] item offset of each rank in its queue
+
+  for (int i = tid; i < nb; i += kSchedThreads) hist[i] = 0;
   __syncthreads();
 
-  // pass 3: scatter the entries into their buckets
-  for (int b = tid; b < a.batch; b += kSchedThreads) {
+  // pass 1: cost and size of every group, histogram of costs (bucket index counts
+  // down so the scan sorts longest first)
+  for (int gi = tid; gi < n_groups; gi += kSchedThreads) {
+    const int b = gi / a.groups_per_seq;
     const int lq = a.bcast_nq > 0 ? a.bcast_nq : a.cu_q[b + 1] - a.cu_q[b];
     const int lk = a.cu_k[b + 1] - a.cu_k[b];
-    const int stat_len = a.mode == 0 ? lq : lk;
-    const int nt = cdiv(stat_len, a.stat_tile);
-    for (int t = 0; t < nt; ++t) {
-      const int c = min(entry_cost(a, lq, lk, t), nb - 1);
-      const int pos = atomicAdd(&hist[nb - 1 - c], 1);
-      if (pos < a.max_entries) a.entries[pos] = WorkEntry{b, t};
+    const int nt = cdiv(a.mode == 0 ? lq : lk, a.stat_tile);
+    int cost = 0;
+    for (int t = 0; t < nt; ++t) cost += entry_cost(a, lq, lk, t);
+    const int n = nt * per_tile;
+    g_items[gi] = n;
+    int bucket = -1;
+    if (n > 0) {
+      bucket = nb - 1 - min(cost * per_tile, nb - 1);
+      atomicAdd(&hist[bucket], 1);
+    }
+    g_bucket[gi] = bucket;
+  }
+  __syncthreads();
+
+  // pass 2: exclusive scan of the histogram (each thread owns a contiguous run of buckets)
+  {
+    const int per = cdiv(nb, kSchedThreads);
+    const int lo = min(tid * per, nb), hi = min(lo + per, nb);
+    int run = 0;
+    for (int i = lo; i < hi; ++i) run += hist[i];
+    int total;
+    int base = segmented_scan(part, run, kSchedThreads, &total);
+    for (int i = lo; i < hi; ++i) {
+      const int c = hist[i];
+      hist[i] = base;
+      base += c;
     }
   }
+  __syncthreads();
+
+  // pass 3: place the groups by rank
+  for (int gi = tid; gi < n_groups; gi += kSchedThreads) {
+    const int bucket = g_bucket[gi];
+    if (bucket >= 0) order[atomicAdd(&hist[bucket], 1)] = gi;
+  }
+  __syncthreads();
+  // after the scatter hist[nb - 1] is one past the last rank: the number of ranked groups
+  const int ranked = hist[nb - 1];
+
+  // pass 4: item offsets of the groups inside their queue (kPerQueue threads per
+  // queue, each owning a contiguous run of that queue's groups)
+  {
+    const int q = tid / kPerQueue, i = tid % kPerQueue;
+    const int per_q = cdiv(cdiv(ranked, kQueues), kPerQueue);
+    const int lo = i * per_q, hi = lo + per_q;
+    int run = 0;
+    for (int j = lo; j < hi; ++j) {
+      const int r = snake_rank(q, j);
+      if (r < ranked) run += g_items[order[r]];
+    }
+    int q_total;
+    int base = segmented_scan(part, run, kPerQueue, &q_total);
+    for (int j = lo; j < hi; ++j) {
+      const int r = snake_rank(q, j);
+      if (r < ranked) {
+        r_off[r] = base;
+        base += g_items[order[r]];
+      }
+    }
+    if (i == 0) q_size[q] = q_total;
+  }
+  __syncthreads();
   if (tid == 0) {
-    *a.n_entries = min(total, a.max_entries);
-    *a.counter = 0u;
+    int s = 0;
+    for (int q = 0; q < kQueues; ++q) {
+      const int n = max(0, min(q_size[q], a.max_items - s));
+      q_start[q] = s;
+      q_size[q] = n;
+      s += n;
+    }
+  }
+  __syncthreads();
+  if (tid < kQueues) {
+    a.queues->start[tid] = q_start[tid];
+    a.queues->size[tid] = q_size[tid];
+    a.queues->next[tid].value = 0u;
+  }
+
+  // pass 5: write the items of every group, tiles in descending cost order
+  // (query-stationary causal tiles grow with t, key-stationary ones shrink),
+  // the query heads of a tile next to each other
+  for (int r = tid; r < ranked; r += kSchedThreads) {
+    const int gi = order[r];
+    const int q = snake_queue(r);
+    const int b = gi / a.groups_per_seq, g = gi % a.groups_per_seq;
+    const int n = g_items[gi];
+    const int nt = n / per_tile;
+    const int base = q_start[q] + r_off[r];
+    const int end = min(q_start[q] + q_size[q], base + n);
+    for (int idx = 0; base + idx < end; ++idx) {
+      const int tt = idx / per_tile, hi = idx % per_tile;
+      WorkItem it;
+      it.b = b;
+      it.t = (a.causal && a.mode == 0) ? nt - 1 - tt : tt;
+      it.h = g * per_tile + hi;
+      it.pad = 0;
+      a.items[base + idx] = it;
+    }
   }
 }
 
 hipError_t launch_sched(const SchedArgs& a, hipStream_t stream) {
   if (a.n_buckets < 1 || a.n_buckets > kMaxBuckets) return hipErrorInvalidValue;
+  if (a.groups_per_seq < 1 || a.per_tile < 1 || a.batch < 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kSchedThreads), 0, stream, a);
   return hipGetLastError();
 }

@@ -22,6 +22,9 @@
  * Conventions shared by every entry point
  *   - Every tensor pointer is a DEVICE pointer to contiguous row-major memory in
  *     the layout stated, aligned to 16 bytes.  bf16 tensors are passed as void*.
+ *   - The workspace pointer must be aligned to 256 bytes (torch and hipMalloc
+ *     allocations are); a misaligned one is rejected with
+ *     JFA_ERR_INVALID_ARGUMENT.
  *   - The caller owns all memory (inputs, outputs, workspace).  The library
  *     allocates no device memory and keeps no state beyond a per-device cache of
  *     the compute-unit count.  Calls with distinct workspaces may run
@@ -100,8 +103,10 @@ size_t jfa_fwd_workspace_size(const jfa_attn_params_t* p);
 /*
  * Forward: O = softmax(S) V per sequence and head, plus LSE, with no score
  * matrix or padding ever written to memory.  Work items (sequence, query tile,
- * head) are listed on the device from the offsets, sorted by their KV-tile count
- * (longest first) and pulled by persistent workgroups from an atomic counter.
+ * head) are listed on the device from the offsets.  The tiles of one (sequence,
+ * KV head) form a group that shares its K/V; groups are sorted by cost (longest
+ * first) and dealt to one queue per XCD, and persistent workgroups pull from
+ * their XCD's queue, then from the others.
  * workspace: device memory of at least jfa_fwd_workspace_size(p) bytes, used
  * only during this call (stream-ordered).
  */

@@ -69,7 +69,7 @@ def test_invalid_attention_arguments(kw, status):
 def test_null_pointers_and_small_workspace():
     L, lib = _lib()
     p = _params(L)
-    d = ctypes.c_void_p(16)
+    d = ctypes.c_void_p(256)
     need = lib.jfa_fwd_workspace_size(ctypes.byref(p))
     assert need > 0
     assert lib.jfa_fwd(None, d, d, d, d, d, d, d, d, need, None) == L.JFA_ERR_INVALID_ARGUMENT
@@ -81,6 +81,19 @@ def test_null_pointers_and_small_workspace():
     assert lib.jfa_bwd_workspace_size(ctypes.byref(pb)) >= 10 * 4 * 128 * 4   # + the fp32 dQ accumulator
     assert lib.jfa_bwd(ctypes.byref(p), d, d, d, d, d, d, d, d, d, d, d, d, nb - 1, None) == L.JFA_ERR_WORKSPACE_TOO_SMALL
     assert lib.jfa_bwd(ctypes.byref(p), d, d, d, None, d, d, d, d, d, d, d, d, nb, None) == L.JFA_ERR_INVALID_ARGUMENT
+
+
+def test_misaligned_workspace_is_rejected():
+    L, lib = _lib()
+    p = _params(L)
+    d, mis = ctypes.c_void_p(256), ctypes.c_void_p(256 + 16)
+    nf, nb = lib.jfa_fwd_workspace_size(ctypes.byref(p)), lib.jfa_bwd_workspace_size(ctypes.byref(p))
+    assert lib.jfa_fwd(ctypes.byref(p), d, d, d, d, d, d, d, mis, nf, None) == L.JFA_ERR_INVALID_ARGUMENT
+    assert lib.jfa_bwd(ctypes.byref(p), d, d, d, d, d, d, d, d, d, d, d, mis, nb, None) == L.JFA_ERR_INVALID_ARGUMENT
+    pd = L.DecodeParams(batch=2, num_heads_q=32, num_heads_kv=8, head_dim=128, page_size=16, num_pages=10,
+                        max_pages_per_seq=5, num_splits=4, softmax_scale=0.0)
+    nd = lib.jfa_decode_workspace_size(ctypes.byref(pd))
+    assert lib.jfa_decode_paged(ctypes.byref(pd), d, d, d, d, d, d, d, mis, nd, None) == L.JFA_ERR_INVALID_ARGUMENT
 
 
 def test_empty_problem_is_a_no_op():
@@ -113,7 +126,7 @@ def test_decode_workspace_query():
     assert lib.jfa_decode_workspace_size(ctypes.byref(p)) >= 4 * 32 * 32 * 129 * 4
     p.num_splits = 1
     assert lib.jfa_decode_workspace_size(ctypes.byref(p)) == 0
-    d = ctypes.c_void_p(16)
+    d = ctypes.c_void_p(256)
     p.num_splits = 4
     assert lib.jfa_decode_paged(ctypes.byref(p), d, d, d, d, d, d, d, d, 16, None) == L.JFA_ERR_WORKSPACE_TOO_SMALL
 
