@@ -250,7 +250,7 @@ jfa_status_t jfa_fwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   sa.causal = p->causal;
   sa.bcast_nq = p->broadcast_q ? p->total_q : 0;
   set_lists(sa, p, workspace, L);
-  hipError_t e = launch_sched(sa, stream);
+  hipError_t e = launch_sched(&sa, 1, stream);
   if (e != hipSuccess) return JFA_ERR_HIP;
 
   FwdArgs fa{};
@@ -326,7 +326,42 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   ba.scale = scale;
   ba.scale_log2 = scale * 1.4426950408889634f;
 
+  // Both work lists (dQ: query-stationary, dK/dV: key-stationary) in one launch.
+  const bool dq_list = p->total_q > 0 && !p->broadcast_q;
+  const bool dkdv_list = p->total_k > 0;
+  SchedArgs lists[kMaxSchedLists];
+  int n_lists = 0;
+  SchedArgs dq_sa{}, dkdv_sa{};
+  if (dq_list) {
+    dq_sa.cu_q = cu_seqlens_q;
+    dq_sa.cu_k = cu_seqlens_k;
+    dq_sa.batch = p->batch;
+    dq_sa.stat_tile = bwd_dq_rows();
+    dq_sa.loop_tile = bwd_dq_tile();
+    dq_sa.mode = 0;
+    dq_sa.causal = p->causal;
+    dq_sa.bcast_nq = 0;
+    set_lists(dq_sa, p, workspace, L.dq_list);
+    lists[n_lists++] = dq_sa;
+  }
+  if (dkdv_list) {
+    dkdv_sa.cu_q = cu_seqlens_q;
+    dkdv_sa.cu_k = cu_seqlens_k;
+    dkdv_sa.batch = p->batch;
+    dkdv_sa.stat_tile = bwd_dkdv_tile();
+    dkdv_sa.loop_tile = bwd_dkdv_rows();
+    dkdv_sa.mode = 1;
+    dkdv_sa.causal = p->causal;
+    dkdv_sa.bcast_nq = p->broadcast_q ? p->total_q : 0;
+    set_lists(dkdv_sa, p, workspace, L.dkdv_list);
+    lists[n_lists++] = dkdv_sa;
+  }
   hipError_t e;
+  if (n_lists > 0) {
+    e = launch_sched(lists, n_lists, stream);
+    if (e != hipSuccess) return JFA_ERR_HIP;
+  }
+
   if (p->total_q > 0) {
     // delta = rowsum(dO * O); for broadcast-Q also zero the fp32 dQ accumulator
     BwdPreArgs pa{};
@@ -356,20 +391,8 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
       tr.finish();
       if (e != hipSuccess) return JFA_ERR_HIP;
     } else {
-      SchedArgs sa{};
-      sa.cu_q = cu_seqlens_q;
-      sa.cu_k = cu_seqlens_k;
-      sa.batch = p->batch;
-      sa.stat_tile = bwd_dq_rows();
-      sa.loop_tile = bwd_dq_tile();
-      sa.mode = 0;
-      sa.causal = p->causal;
-      sa.bcast_nq = 0;
-      set_lists(sa, p, workspace, L.dq_list);
-      e = launch_sched(sa, stream);
-      if (e != hipSuccess) return JFA_ERR_HIP;
-      ba.items = sa.items;
-      ba.queues = sa.queues;
+      ba.items = dq_sa.items;
+      ba.queues = dq_sa.queues;
       const int64_t max_items = L.dq_list.max_items;
       TimedRegion tr(JFA_TIMING_BWD_DQ, stream);
       e = launch_bwd_dq(ba, p->head_dim, (int)std::max<int64_t>(1, std::min<int64_t>(2LL * cus, max_items)), stream);
@@ -380,20 +403,8 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
 
   if (p->total_k > 0) {
     // dK, dV: key-stationary
-    SchedArgs sa{};
-    sa.cu_q = cu_seqlens_q;
-    sa.cu_k = cu_seqlens_k;
-    sa.batch = p->batch;
-    sa.stat_tile = bwd_dkdv_tile();
-    sa.loop_tile = bwd_dkdv_rows();
-    sa.mode = 1;
-    sa.causal = p->causal;
-    sa.bcast_nq = p->broadcast_q ? p->total_q : 0;
-    set_lists(sa, p, workspace, L.dkdv_list);
-    e = launch_sched(sa, stream);
-    if (e != hipSuccess) return JFA_ERR_HIP;
-    ba.items = sa.items;
-    ba.queues = sa.queues;
+    ba.items = dkdv_sa.items;
+    ba.queues = dkdv_sa.queues;
     const int64_t max_items = L.dkdv_list.max_items;
     TimedRegion tr(JFA_TIMING_BWD_DKDV, stream);
     e = launch_bwd_dkdv(ba, p->head_dim, (int)std::max<int64_t>(1, std::min<int64_t>(cus, max_items)), stream);

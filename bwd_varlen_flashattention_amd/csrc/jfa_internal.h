@@ -49,12 +49,17 @@ struct SchedArgs {
   int32_t bcast_nq;         // > 0: broadcast-Q, every item has Lq = bcast_nq
   int32_t n_buckets;        // cost buckets (costs above are clamped into the last one)
   int32_t max_items;        // capacity of `items`
-  int32_t* scratch;         // 4 * batch * groups_per_seq ints
+  int32_t* scratch;         // 4 * batch * groups_per_seq ints (used when they do not fit in LDS)
   WorkItem* items;          // queue by queue
   WorkQueues* queues;
 };
 
-hipError_t launch_sched(const SchedArgs& a, hipStream_t stream);
+// Several work lists built by one launch (one block each).
+constexpr int kMaxSchedLists = 2;
+struct SchedBatch {
+  SchedArgs list[kMaxSchedLists];
+};
+hipError_t launch_sched(const SchedArgs* lists, int n, hipStream_t stream);
 
 // Forward kernel arguments.
 struct FwdArgs {

@@ -16,6 +16,8 @@
 // (0..7, 7..0, ...), which balances the queues while each stays in descending
 // cost order.  Workgroup i serves queue i % kQueues (the XCD it is dispatched
 // to) and steals from the other queues once its own is empty.
+#include <algorithm>
+
 #include "jfa_internal.h"
 #include "device_common.h"
 
@@ -24,6 +26,7 @@ namespace jfa {
 constexpr int kSchedThreads = 1024;
 constexpr int kMaxBuckets = 4096;
 constexpr int kPerQueue = kSchedThreads / kQueues;
+constexpr int kLdsGroups = 6144;              // per-group arrays in LDS up to this many groups (96 KB)
 
 __device__ __forceinline__ int entry_cost(const SchedArgs& a, int lq, int lk, int t) {
   if (a.mode == 0) {               // query tile t, loop over key tiles
@@ -65,18 +68,33 @@ __device__ int segmented_scan(int* part, int x, int seg, int* seg_total) {
   return incl - x;
 }
 
-__global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedArgs a) {
+// Total cost of the nt tiles of one group member.
+__device__ __forceinline__ int tiles_cost(const SchedArgs& a, int lq, int lk, int nt) {
+  if (!a.causal) return nt * (a.mode == 0 ? cdiv(lk, a.loop_tile) : cdiv(lq, a.loop_tile));
+  int cost = 0;
+  for (int t = 0; t < nt; ++t) cost += entry_cost(a, lq, lk, t);
+  return cost;
+}
+
+// One block builds one work list (block i: list i).  LDS_SCRATCH keeps the
+// per-group arrays in LDS (up to kLdsGroups groups), otherwise they live in the
+// list's global scratch.
+template <bool LDS_SCRATCH>
+__global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedBatch batch) {
   __shared__ int hist[kMaxBuckets];
   __shared__ int part[kSchedThreads];
   __shared__ int q_start[kQueues], q_size[kQueues];
+  __shared__ int lds_scratch[LDS_SCRATCH ? 4 * kLdsGroups : 1];
+  const SchedArgs a = batch.list[blockIdx.x];
   const int tid = threadIdx.x;
   const int nb = a.n_buckets;
   const int n_groups = a.batch * a.groups_per_seq;
   const int per_tile = a.per_tile;
-  int* g_items = a.scratch;                   // [n_groups] items of each group
-  int* g_bucket = a.scratch + n_groups;       // [n_groups] cost bucket, -1 when empty
-  int* order = a.scratch + 2 * n_groups;      // [n_groups] group of each rank
-  int* r_off = a.scratch + 3 * n_groups;      // [n_groups] item offset of each rank in its queue
+  int* scratch = LDS_SCRATCH ? lds_scratch : a.scratch;
+  int* g_items = scratch;                     // [n_groups] items of each group
+  int* g_bucket = scratch + n_groups;         // [n_groups] cost bucket, -1 when empty
+  int* order = scratch + 2 * n_groups;        // [n_groups] group of each rank
+  int* r_off = scratch + 3 * n_groups;        // [n_groups] item offset of each rank in its queue
 
   for (int i = tid; i < nb; i += kSchedThreads) hist[i] = 0;
   __syncthreads();
@@ -88,8 +106,7 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedArgs a) {
     const int lq = a.bcast_nq > 0 ? a.bcast_nq : a.cu_q[b + 1] - a.cu_q[b];
     const int lk = a.cu_k[b + 1] - a.cu_k[b];
     const int nt = cdiv(a.mode == 0 ? lq : lk, a.stat_tile);
-    int cost = 0;
-    for (int t = 0; t < nt; ++t) cost += entry_cost(a, lq, lk, t);
+    const int cost = tiles_cost(a, lq, lk, nt);
     const int n = nt * per_tile;
     g_items[gi] = n;
     int bucket = -1;
@@ -188,10 +205,21 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedArgs a) {
   }
 }
 
-hipError_t launch_sched(const SchedArgs& a, hipStream_t stream) {
-  if (a.n_buckets < 1 || a.n_buckets > kMaxBuckets) return hipErrorInvalidValue;
-  if (a.groups_per_seq < 1 || a.per_tile < 1 || a.batch < 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(sched_kernel, dim3(1), dim3(kSchedThreads), 0, stream, a);
+hipError_t launch_sched(const SchedArgs* lists, int n, hipStream_t stream) {
+  if (n < 1 || n > kMaxSchedLists) return hipErrorInvalidValue;
+  SchedBatch batch{};
+  int64_t max_groups = 0;
+  for (int i = 0; i < n; ++i) {
+    const SchedArgs& a = lists[i];
+    if (a.n_buckets < 1 || a.n_buckets > kMaxBuckets) return hipErrorInvalidValue;
+    if (a.groups_per_seq < 1 || a.per_tile < 1 || a.batch < 0) return hipErrorInvalidValue;
+    batch.list[i] = a;
+    max_groups = std::max<int64_t>(max_groups, (int64_t)a.batch * a.groups_per_seq);
+  }
+  if (max_groups <= kLdsGroups)
+    hipLaunchKernelGGL(sched_kernel<true>, dim3(n), dim3(kSchedThreads), 0, stream, batch);
+  else
+    hipLaunchKernelGGL(sched_kernel<false>, dim3(n), dim3(kSchedThreads), 0, stream, batch);
   return hipGetLastError();
 }
 

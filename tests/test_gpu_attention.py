@@ -105,6 +105,17 @@ def test_cross_lengths_bottom_right_causal(jfa):
         _compare_full(_run_self(jfa, inp), _oracle_self(inp))
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_many_sequences(jfa, causal):
+    """More (sequence, KV head) groups than the scheduler keeps on chip (its per-group
+    arrays then live in the workspace), many of them empty or one token long."""
+    rng = np.random.default_rng(31)
+    lengths = rng.integers(0, 40, 1600).tolist()
+    inp = workloads.jagged(11, lengths, None, 8, 4, 64, causal)
+    _say(f"many sequences: batch {len(lengths)}, groups {len(lengths) * 4}, causal={causal}")
+    _compare_full(_run_self(jfa, inp), _oracle_self(inp))
+
+
 def test_explicit_scale(jfa):
     inp = workloads.jagged(8, [70, 129], None, 2, 2, 64, False)
     _compare_full(_run_self(jfa, inp, 0.3), _oracle_self(inp, 0.3))
