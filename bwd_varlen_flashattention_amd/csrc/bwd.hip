@@ -208,6 +208,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         kf[ks] = key_ok ? *(const bf16x8*)(a.k + base + 16 * ks) : zero_bf16x8();
         vf[ks] = key_ok ? *(const bf16x8*)(a.v + base + 16 * ks) : zero_bf16x8();
       }
+      wait_vmem_all();
     }
     f32x16 dkt[DB], dvt[DB];
 #pragma unroll
@@ -223,13 +224,26 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       return u >= n_steps ? u - n_steps : u;
     };
     u32x4 qr[4], dr[4];
-    float lse_r = 0.f, dlt_r = 0.f;
+    // LSE and delta travel raw (range-checked buffer loads) and are only looked
+    // at when they are written to LDS: consuming them right after the load would
+    // make the in-order vmcnt wait cover this step's Q/dO prefetch as well.
+    // Rows past Lq read LSE = delta = 0 with zero Q and dO rows, so they add
+    // nothing to dK or dV.
+    float lse_raw = 0.f, dlt_raw = 0.f;
     auto load_regs = [&](int s) {
       const int u = unit_of(s);
       const int h = g * a.group + u / n_qt;
       const int qt = i_first + u % n_qt;
       const int row0 = qt * BM;
-      const uint32_t nbytes = (uint32_t)(min(lq - row0, BM) * qrs * 2);
+      const int rows = min(lq - row0, BM);
+      if (tid < BM) {
+        const int64_t li0 = BCAST ? ((int64_t)b * a.hq + h) * lq + row0 : (int64_t)h * a.total_q + q_base + row0;
+        const auto lrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.lse + li0), (short)0, (uint32_t)(rows * 4), kBufferFlags);
+        const auto drsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.delta + li0), (short)0, (uint32_t)(rows * 4), kBufferFlags);
+        lse_raw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrsrc, tid * 4, 0, 0));
+        dlt_raw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(drsrc, tid * 4, 0, 0));
+      }
+      const uint32_t nbytes = (uint32_t)(rows * qrs * 2);
       const __bf16* qb = a.q + ((int64_t)(q_base + row0) * a.hq + h) * D;
       const int64_t orow0 = BCAST ? (int64_t)b * lq + row0 : (int64_t)(q_base + row0);
       const __bf16* ob = a.dout + (orow0 * a.hq + h) * D;
@@ -240,18 +254,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         for (int i = 0; i < 4; ++i) {
           qr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrsrc, qoff[i], 0, 0));
           dr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(orsrc, qoff[i], 0, 0));
-        }
-      }
-      if (tid < BM) {
-        const int row = row0 + tid;
-        if (row < lq) {
-          const int64_t li = BCAST ? ((int64_t)b * a.hq + h) * lq + row : (int64_t)h * a.total_q + q_base + row;
-          const float l = a.lse[li];
-          lse_r = (l == -INF) ? INF : l * kLog2e;     // rows that saw no key get P = 0
-          dlt_r = a.delta[li];
-        } else {
-          lse_r = INF;
-          dlt_r = 0.f;
         }
       }
     };
@@ -266,7 +268,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         store_transposed_4x8(&qt_lds[buf][(8 * sd) * QTP + col], QTP, qr);
         store_transposed_4x8(&dot_lds[buf][(8 * sd) * QTP + col], QTP, dr);
       }
-      if (tid < BM) { lse_lds[buf][tid] = lse_r; dlt_lds[buf][tid] = dlt_r; }
+      if (tid < BM) {
+        lse_lds[buf][tid] = (lse_raw == -INF) ? INF : lse_raw * kLog2e;   // rows that saw no key get P = 0
+        dlt_lds[buf][tid] = dlt_raw;
+      }
     };
 
     auto step = [&](int s) {

@@ -78,6 +78,13 @@ __device__ __forceinline__ bf16x8 zero_bf16x8() {
 
 __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 
+// s_waitcnt vmcnt(0): every vector-memory load of this wave has returned.  Used
+// after loads made under a branch whose results feed a loop: on the path that
+// skips the branch the waitcnt pass cannot prove those loads retired, and would
+// otherwise wait for all outstanding loads, this iteration's prefetch included,
+// inside the loop.  (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15.)
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // Work-queue hand-out for persistent workgroups.  The queue starts and sizes
 // are copied into LDS once (load_queues, by all threads, followed by a barrier);
 // next_work_item is then called by one thread.  `q` starts at the block's home
