@@ -186,8 +186,10 @@ jfa_status_t check_decode(const jfa_decode_params_t* p) {
 
 int resolve_splits(const jfa_decode_params_t* p) {
   if (p->num_splits > 0) return p->num_splits;
+  // about two workgroups per resident slot: the later ones fill in behind units
+  // of short sequences, which balances mixed lengths
   const int64_t units = (int64_t)p->batch * p->num_heads_kv;
-  int s = cdiv_i(4 * (int64_t)cu_count(), units);
+  int s = cdiv_i(2 * (int64_t)cu_count() * decode_blocks_per_cu(), units);
   const int64_t max_len = (int64_t)p->max_pages_per_seq * p->page_size;
   const int cap = (int)std::max<int64_t>(1, (max_len + 1023) / 1024);   // at least ~1k keys per split
   if (s > cap) s = cap;

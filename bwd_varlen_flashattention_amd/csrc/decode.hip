@@ -47,7 +47,7 @@ __device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
 }
 
 template <int D>
-__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, 4) void decode_kernel(DecodeArgs a) {
   using T = DecTile<D>;
   constexpr int BN = T::BN, KP = T::KP, VP = T::VP, KK = T::KK, DB = T::DB;
   constexpr int KV_BYTES = BN * (KP + VP) * 2;
@@ -62,11 +62,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
   const int l16 = lane & 15, g16 = lane >> 4;
   const float NEG_INF = -__builtin_inff();
 
+  // unit = (b, s, g) with g fastest: the KV heads of one chunk are neighbouring
+  // workgroups, dispatched together, so the token rows they share are read from
+  // DRAM at about the same time
   const int unit = blockIdx.x;
-  const int s = unit % a.splits;
-  const int bg = unit / a.splits;
-  const int g = bg % a.hkv;
-  const int b = bg / a.hkv;
+  const int g = unit % a.hkv;
+  const int bs = unit / a.hkv;
+  const int s = bs % a.splits;
+  const int b = bs / a.splits;
   const int L = a.seqlens[b];
   const int chunk = cdiv(cdiv(L, a.splits), BN) * BN;
   const int k_lo = s * chunk;
@@ -221,6 +224,7 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
 }
 
 int decode_chunk_align() { return DecTile<128>::BN; }
+int decode_blocks_per_cu() { return 4; }   // LDS and registers of the d = 128 kernel allow four
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t stream) {
   const int64_t grid = (int64_t)a.batch * a.hkv * a.splits;

@@ -160,5 +160,6 @@ struct DecodeArgs {
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeArgs& a, int head_dim, hipStream_t stream);
 int decode_chunk_align();
+int decode_blocks_per_cu();   // decode workgroups resident per CU
 
 }  // namespace jfa
