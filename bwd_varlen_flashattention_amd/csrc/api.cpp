@@ -310,6 +310,7 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   ba.k = (const __bf16*)k;
   ba.v = (const __bf16*)v;
   ba.dout = (const __bf16*)dout;
+  ba.o = (const __bf16*)o;
   ba.lse = lse;
   ba.delta = delta;
   ba.cu_q = cu_seqlens_q;
@@ -365,7 +366,9 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   }
 
   if (p->total_q > 0) {
-    // delta = rowsum(dO * O); for broadcast-Q also zero the fp32 dQ accumulator
+    // Broadcast-Q: delta = rowsum(dO * O) for every item and zero the fp32 dQ
+    // accumulator.  Self-attention computes delta inside the dQ kernel.
+    if (p->broadcast_q) {
     BwdPreArgs pa{};
     pa.o = (const __bf16*)o;
     pa.dout = (const __bf16*)dout;
@@ -379,6 +382,7 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
     pa.dq_elems = dq_elems;
     e = launch_bwd_pre(pa, stream);
     if (e != hipSuccess) return JFA_ERR_HIP;
+    }
 
     // dQ: query-stationary
     if (p->broadcast_q) {

@@ -456,7 +456,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         n_tiles = cdiv(lk, BN);
         n_bulk = lk / BN;
       }
-      if (n_tiles == 0) continue;   // uniform
+      if (BCAST && n_tiles == 0) continue;   // uniform
 
       // per-row state: Q and dO fragments (B operands of S^T = K Q^T, dP^T = V dO^T), LSE, delta
       bf16x8 qf[KS], df[KS];
@@ -470,13 +470,29 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
           qf[ks] = row_ok ? *(const bf16x8*)(qp + 16 * ks) : zero_bf16x8();
           df[ks] = row_ok ? *(const bf16x8*)(op + 16 * ks) : zero_bf16x8();
         }
+        const int64_t li = BCAST ? ((int64_t)b * a.hq + h) * lq + my_row : (int64_t)h * a.total_q + q_base + my_row;
+        if (BCAST) {
+          if (row_ok) dlt = a.delta[li];   // written by bwd_pre_kernel
+        } else {
+          // delta = rowsum(dO * O): each lane holds half of the row, its partner lane the other half.
+          // Written for every row, also of tiles that see no key, for the dK/dV kernel.
+          const __bf16* orp = a.o + ((int64_t)(q_base + my_row) * a.hq + h) * D + 8 * hh;
+          float part = 0.f;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 ov = row_ok ? *(const bf16x8*)(orp + 16 * ks) : zero_bf16x8();
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part = fmaf((float)ov[e], (float)df[ks][e], part);
+          }
+          dlt = xhalf_sum(part);
+          if (row_ok && hh == 0) a.delta[li] = dlt;
+        }
         if (row_ok) {
-          const int64_t li = BCAST ? ((int64_t)b * a.hq + h) * lq + my_row : (int64_t)h * a.total_q + q_base + my_row;
           const float l = a.lse[li];
           lse2 = (l == NEG_INF) ? INF : l * kLog2e;
-          dlt = a.delta[li];
         }
       }
+      if (!BCAST && n_tiles == 0) continue;   // uniform; delta is written
 
       const __bf16* kbase = a.k + ((int64_t)k_base * a.hkv + g) * D;
       const __bf16* vbase = a.v + ((int64_t)k_base * a.hkv + g) * D;

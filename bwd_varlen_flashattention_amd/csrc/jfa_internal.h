@@ -104,8 +104,9 @@ struct BwdArgs {
   const __bf16* k;
   const __bf16* v;
   const __bf16* dout;
+  const __bf16* o;          // forward output: the self-attention dQ kernel computes delta from it
   const float* lse;
-  const float* delta;
+  float* delta;             // broadcast-Q: written by bwd_pre_kernel; self-attention: by the dQ kernel
   const int32_t* cu_q;
   const int32_t* cu_k;
   __bf16* dq;
