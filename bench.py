@@ -48,11 +48,13 @@ def pairs_of(cu_q, cu_k, causal, nq=None):
 
 
 def decode_bytes(inp):
+    """Algorithmic bytes: K+V once, q and o, lse, page-table entries, lengths."""
     hkv, d = inp.k.shape[1], inp.k.shape[2]
     kv = int(inp.seqlens_k.astype(np.int64).sum()) * hkv * d * 2 * 2
-    b, hq = inp.q.shape[0], inp.q.shape[1]
+    b = inp.q.shape[0]
+    rows = int(np.prod(inp.q.shape[:-1]))          # B * q_len * Hq
     pages = int(sum(-(-int(L) // inp.page_size) for L in inp.seqlens_k))
-    return kv + b * hq * d * 2 * 2 + b * hq * 4 + pages * 4 + b * 4
+    return kv + rows * d * 2 * 2 + rows * 4 + pages * 4 + b * 4
 
 
 def dev(x, torch):
@@ -98,23 +100,24 @@ class JaggedCase:
 
 
 class DecodeCase:
-    def __init__(self, torch, jfa, inp, splits=0):
+    def __init__(self, torch, jfa, inp, splits=0, causal=False):
         self.torch, self.jfa, self.inp = torch, jfa, inp
+        self.causal = causal
         self.q, self.kc, self.vc = dev(inp.q, torch), dev(inp.k_cache, torch), dev(inp.v_cache, torch)
         self.pt, self.sl = dev(inp.page_table, torch), dev(inp.seqlens_k, torch)
         self.splits = splits
         self.nsplits = jfa.jfa_decode_num_splits(self.q, self.kc, self.pt, splits)
         self.bytes = decode_bytes(inp)
-        self.o, self.lse = jfa.jfa_decode_paged(self.q, self.kc, self.vc, self.pt, self.sl, splits)
+        self.o, self.lse = jfa.jfa_decode_paged(self.q, self.kc, self.vc, self.pt, self.sl, splits, causal=causal)
         import ctypes
         from bwd_varlen_flashattention_amd import _lib
-        p = jfa._decode_params(self.q, self.kc, self.pt, splits, None)
+        p = jfa._decode_params(self.q, self.kc, self.pt, splits, None, causal)
         n = _lib.load().jfa_decode_workspace_size(ctypes.byref(p))
         self.ws = torch.empty(max(1, n), dtype=torch.uint8, device="cuda")
 
     def step(self):
         self.jfa.jfa_decode_paged(self.q, self.kc, self.vc, self.pt, self.sl, self.splits, out=self.o, lse=self.lse,
-                                  workspace=self.ws)
+                                  workspace=self.ws, causal=self.causal)
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_gem_s0.5_bench_step.txt")
@@ -412,6 +415,18 @@ def sweep(torch, jfa, workloads, args, log):
             del dc
         del inp
         torch.cuda.empty_cache()
+    # a few new tokens per sequence (speculative decode): 4 tokens, causal, page 16
+    rng = np.random.default_rng(0)
+    lens = rng.integers(4096, 16385, size=32)
+    inp = workloads.decode(0, lens, 32, 8, 128, 16, max_pages_per_seq=1024, tail_fill=0.0, q_len=4)
+    for splits in (4, 8, 0):
+        dc = DecodeCase(torch, jfa, inp, splits, causal=True)
+        ms = timeit(dc.step)
+        print(json.dumps({"workload": "decode_ps16_q4_causal", "splits": dc.nsplits, "ms": round(ms, 4),
+                          "tb_s": round(dc.bytes / ms / 1e9, 3)}), flush=True)
+        del dc
+    del inp
+    torch.cuda.empty_cache()
 
 
 if __name__ == "__main__":

@@ -111,11 +111,14 @@ def jfa_bwd(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int
     return dq, dk, dv
 
 
-def _decode_params(q, k_cache, page_table, num_splits, scale):
+def _decode_params(q, k_cache, page_table, num_splits, scale, causal=False):
+    """q is [B, Hq, d] (one token per sequence) or [B, q_len, Hq, d]."""
+    q_len = 1 if q.dim() == 3 else q.shape[1]
     return DecodeParams(
-        batch=q.shape[0], num_heads_q=q.shape[1], num_heads_kv=k_cache.shape[2], head_dim=q.shape[2],
+        batch=q.shape[0], num_heads_q=q.shape[-2], num_heads_kv=k_cache.shape[2], head_dim=q.shape[-1],
         page_size=k_cache.shape[1], num_pages=k_cache.shape[0], max_pages_per_seq=page_table.shape[1],
-        num_splits=int(num_splits), softmax_scale=float(scale) if scale is not None else 0.0)
+        num_splits=int(num_splits), softmax_scale=float(scale) if scale is not None else 0.0,
+        q_len=int(q_len), causal=int(bool(causal)))
 
 
 def jfa_decode_num_splits(q, k_cache, page_table, num_splits: int = 0) -> int:
@@ -124,15 +127,23 @@ def jfa_decode_num_splits(q, k_cache, page_table, num_splits: int = 0) -> int:
 
 
 def jfa_decode_paged(q, k_cache, v_cache, page_table, seqlens_k, num_splits: int = 0,
-                     softmax_scale: Optional[float] = None, out=None, lse=None, workspace=None):
-    """Paged decode: q [B,Hq,d], caches [num_pages,page_size,Hkv,d] -> o [B,Hq,d], lse [B,Hq]."""
+                     softmax_scale: Optional[float] = None, out=None, lse=None, workspace=None,
+                     causal: bool = False):
+    """Paged decode of q_len new tokens per sequence against a paged KV cache.
+
+    q [B, Hq, d] (one token) or [B, q_len, Hq, d] (q_len <= 16); caches
+    [num_pages, page_size, Hkv, d] -> o shaped like q, lse [B, Hq] or [B, q_len, Hq].
+    causal: the q_len tokens are the last ones of each sequence (bottom-right mask).
+    """
     torch = _torch()
     lib = load()
-    _check_bf16("q", q, 3); _check_bf16("k_cache", k_cache, 4); _check_bf16("v_cache", v_cache, 4)
+    if q.dim() not in (3, 4):
+        raise ValueError("q must be [B, Hq, d] or [B, q_len, Hq, d]")
+    _check_bf16("q", q, q.dim()); _check_bf16("k_cache", k_cache, 4); _check_bf16("v_cache", v_cache, 4)
     _check_i32("page_table", page_table); _check_i32("seqlens_k", seqlens_k)
-    p = _decode_params(q, k_cache, page_table, num_splits, softmax_scale)
+    p = _decode_params(q, k_cache, page_table, num_splits, softmax_scale, causal)
     o = out if out is not None else torch.empty_like(q)
-    l = lse if lse is not None else torch.empty((q.shape[0], q.shape[1]), dtype=torch.float32, device=q.device)
+    l = lse if lse is not None else torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
     need = lib.jfa_decode_workspace_size(ctypes.byref(p))
     ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     st = lib.jfa_decode_paged(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),

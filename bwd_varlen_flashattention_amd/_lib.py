@@ -53,6 +53,8 @@ class DecodeParams(ctypes.Structure):
         ("max_pages_per_seq", ctypes.c_int32),
         ("num_splits", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
+        ("q_len", ctypes.c_int32),
+        ("causal", ctypes.c_int32),
     ]
 
 

@@ -179,7 +179,8 @@ jfa_status_t check_decode(const jfa_decode_params_t* p) {
   if (p->num_splits < 0 || p->num_splits > 128) return JFA_ERR_INVALID_ARGUMENT;
   if (!(p->softmax_scale == p->softmax_scale) || isinf(p->softmax_scale)) return JFA_ERR_INVALID_ARGUMENT;
   if (!supported_dim(p->head_dim)) return JFA_ERR_UNSUPPORTED;
-  if (p->num_heads_q / p->num_heads_kv > 16) return JFA_ERR_UNSUPPORTED;
+  if (p->q_len < 1 || p->q_len > 16 || (p->causal != 0 && p->causal != 1)) return JFA_ERR_INVALID_ARGUMENT;
+  if ((int64_t)(p->num_heads_q / p->num_heads_kv) * p->q_len > 256) return JFA_ERR_UNSUPPORTED;
   if ((int64_t)p->num_pages * p->page_size * p->num_heads_kv * p->head_dim > ((int64_t)1 << 40)) return JFA_ERR_INVALID_ARGUMENT;
   return JFA_OK;
 }
@@ -188,8 +189,10 @@ int resolve_splits(const jfa_decode_params_t* p) {
   if (p->num_splits > 0) return p->num_splits;
   // about two workgroups per resident slot: the later ones fill in behind units
   // of short sequences, which balances mixed lengths
-  const int64_t units = (int64_t)p->batch * p->num_heads_kv;
-  int s = cdiv_i(2 * (int64_t)cu_count() * decode_blocks_per_cu(), units);
+  const int cols = p->num_heads_q / p->num_heads_kv * p->q_len;
+  const int64_t col_units = cdiv_i(cdiv_i(cols, 16), decode_col_groups(cols));
+  const int64_t units = (int64_t)p->batch * p->num_heads_kv * col_units;
+  int s = cdiv_i(2 * (int64_t)cu_count() * decode_blocks_per_cu(cols), units);
   const int64_t max_len = (int64_t)p->max_pages_per_seq * p->page_size;
   const int cap = (int)std::max<int64_t>(1, (max_len + 1023) / 1024);   // at least ~1k keys per split
   if (s > cap) s = cap;
@@ -200,7 +203,7 @@ int resolve_splits(const jfa_decode_params_t* p) {
 
 size_t decode_ws(const jfa_decode_params_t* p, int splits) {
   if (splits <= 1) return 0;
-  const size_t plane = (size_t)p->batch * p->num_heads_q;
+  const size_t plane = (size_t)p->batch * p->q_len * p->num_heads_q;
   return align_up(plane * splits * p->head_dim * sizeof(float)) + align_up(plane * splits * sizeof(float));
 }
 
@@ -461,7 +464,7 @@ jfa_status_t jfa_decode_paged(const jfa_decode_params_t* p, const void* q, const
   a.seqlens = seqlens_k;
   a.o = (__bf16*)o;
   a.lse = lse;
-  const size_t plane = (size_t)p->batch * p->num_heads_q;
+  const size_t plane = (size_t)p->batch * p->q_len * p->num_heads_q;
   a.o_part = splits > 1 ? (float*)workspace : nullptr;
   a.lse_part = splits > 1 ? (float*)((char*)workspace + align_up(plane * splits * p->head_dim * sizeof(float))) : nullptr;
   a.batch = p->batch;
@@ -471,6 +474,8 @@ jfa_status_t jfa_decode_paged(const jfa_decode_params_t* p, const void* q, const
   a.page_size = p->page_size;
   a.max_pages = p->max_pages_per_seq;
   a.splits = splits;
+  a.q_len = p->q_len;
+  a.causal = p->causal;
   a.scale_log2 = eff_scale(p->softmax_scale, p->head_dim) * 1.4426950408889634f;
   TimedRegion tr(JFA_TIMING_DECODE, stream);
   hipError_t e = launch_decode(a, p->head_dim, stream);

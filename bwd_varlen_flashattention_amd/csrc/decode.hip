@@ -46,8 +46,11 @@ __device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
-template <int D>
-__global__ __launch_bounds__(256, 4) void decode_kernel(DecodeArgs a) {
+// NCG: 16-column query groups per workgroup (1 or 2).  A workgroup handles up to 16*NCG
+// query columns (token, query head of the GQA group) of one (sequence, KV head,
+// split); every K and V fragment it reads from LDS feeds all of its groups.
+template <int D, int NCG>
+__global__ __launch_bounds__(256, NCG == 1 ? 4 : 2) void decode_kernel(DecodeArgs a) {
   using T = DecTile<D>;
   constexpr int BN = T::BN, KP = T::KP, VP = T::VP, KK = T::KK, DB = T::DB;
   constexpr int KV_BYTES = BN * (KP + VP) * 2;
@@ -62,33 +65,51 @@ __global__ __launch_bounds__(256, 4) void decode_kernel(DecodeArgs a) {
   const int l16 = lane & 15, g16 = lane >> 4;
   const float NEG_INF = -__builtin_inff();
 
-  // unit = (b, s, g) with g fastest: the KV heads of one chunk are neighbouring
-  // workgroups, dispatched together, so the token rows they share are read from
-  // DRAM at about the same time
-  const int unit = blockIdx.x;
+  // unit = (b, s, column unit, g) with g fastest: the KV heads of one chunk are
+  // neighbouring workgroups, dispatched together, so the token rows they share
+  // are read from DRAM at about the same time
+  const int cols = a.group * a.q_len;               // query columns of one (sequence, KV head)
+  const int n_cu = cdiv(cdiv(cols, 16), NCG);
+  int unit = blockIdx.x;
   const int g = unit % a.hkv;
-  const int bs = unit / a.hkv;
-  const int s = bs % a.splits;
-  const int b = bs / a.splits;
+  unit /= a.hkv;
+  const int cu = unit % n_cu;
+  unit /= n_cu;
+  const int s = unit % a.splits;
+  const int b = unit / a.splits;
   const int L = a.seqlens[b];
   const int chunk = cdiv(cdiv(L, a.splits), BN) * BN;
   const int k_lo = s * chunk;
   const int k_hi = min(L, k_lo + chunk);
   const int n_tiles = k_hi > k_lo ? cdiv(k_hi - k_lo, BN) : 0;
 
-  // query fragment: column q = l16 is query head g*group + q (zero when q >= group)
-  bf16x8 qf[KK];
-  {
-    const bool q_ok = l16 < a.group;
-    const __bf16* qp = a.q + ((int64_t)b * a.hq + g * a.group + (q_ok ? l16 : 0)) * D + 8 * g16;
+  // Query fragments.  Column c = (cu*NCG + cg)*16 + l16 is token t = c / group of
+  // query head g*group + c % group; columns past the last one are zero.  With a
+  // causal mask (bottom-right: the q_len tokens are the last ones of the
+  // sequence) token t sees keys up to t + L - q_len.
+  bf16x8 qf[NCG][KK];
+  int kmax[NCG];
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qf[kk] = q_ok ? *(const bf16x8*)(qp + 32 * kk) : zero_bf16x8();
+  for (int cg = 0; cg < NCG; ++cg) {
+    const int c = (cu * NCG + cg) * 16 + l16;
+    const bool ok = c < cols;
+    const int t = ok ? c / a.group : 0;
+    const int h = g * a.group + (ok ? c % a.group : 0);
+    const __bf16* qp = a.q + (((int64_t)b * a.q_len + t) * a.hq + h) * D + 8 * g16;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) qf[cg][kk] = ok ? *(const bf16x8*)(qp + 32 * kk) : zero_bf16x8();
+    kmax[cg] = min(k_hi - 1, a.causal ? t + L - a.q_len : L - 1);
   }
 
-  f32x4 acc[DB];
+  f32x4 acc[NCG][DB];
+  float m_run[NCG], l_run[NCG];
 #pragma unroll
-  for (int db = 0; db < DB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = NEG_INF, l_run = 0.f;
+  for (int cg = 0; cg < NCG; ++cg) {
+#pragma unroll
+    for (int db = 0; db < DB; ++db) acc[cg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[cg] = NEG_INF;
+    l_run[cg] = 0.f;
+  }
 
   const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
   u32x4 kr[T::LOADS], vr[T::LOADS];
@@ -121,82 +142,106 @@ __global__ __launch_bounds__(256, 4) void decode_kernel(DecodeArgs a) {
     __syncthreads();
     if (j + 1 < n_tiles) load_regs(j + 1);
 
-    f32x4 st = f32x4{0.f, 0.f, 0.f, 0.f};
+    // S^T[key][column] for this wave's 16 keys and every column group
+    f32x4 st[NCG];
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg) st[cg] = f32x4{0.f, 0.f, 0.f, 0.f};
     const __bf16* kp = k_lds + (16 * w + l16) * KP + 8 * g16;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) st = mfma16x16x32(*(const bf16x8*)(kp + 32 * kk), qf[kk], st);
+    for (int kk = 0; kk < KK; ++kk) {
+      const bf16x8 kfrag = *(const bf16x8*)(kp + 32 * kk);
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) st[cg] = mfma16x16x32(kfrag, qf[cg][kk], st[cg]);
+    }
 
-    float mx = NEG_INF;
+    bf16x4 pb[NCG];
+    float alpha[NCG];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int key = k_lo + j * BN + 16 * w + 4 * g16 + r;
-      st[r] = key < k_hi ? st[r] : NEG_INF;
-      mx = fmaxf(mx, st[r]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = xhalf_max(mx);
-    const float m_new = fmaxf(m_run, mx * a.scale_log2);
-    const float alpha = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run - m_new);
-    const float m_sub = (m_new == NEG_INF) ? 0.f : m_new;
-    bf16x4 pb;
-    float psum = 0.f;
+    for (int cg = 0; cg < NCG; ++cg) {
+      float mx = NEG_INF;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float p = fast_exp2(fmaf(st[r], a.scale_log2, -m_sub));
-      psum += p;
-      pb[r] = (__bf16)p;
+      for (int r = 0; r < 4; ++r) {
+        const int key = k_lo + j * BN + 16 * w + 4 * g16 + r;
+        st[cg][r] = key <= kmax[cg] ? st[cg][r] : NEG_INF;
+        mx = fmaxf(mx, st[cg][r]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = xhalf_max(mx);
+      const float m_new = fmaxf(m_run[cg], mx * a.scale_log2);
+      alpha[cg] = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run[cg] - m_new);
+      const float m_sub = (m_new == NEG_INF) ? 0.f : m_new;
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = fast_exp2(fmaf(st[cg][r], a.scale_log2, -m_sub));
+        psum += p;
+        pb[cg][r] = (__bf16)p;
+      }
+      l_run[cg] = l_run[cg] * alpha[cg] + psum;
+      m_run[cg] = m_new;
     }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
 #pragma unroll
     for (int db = 0; db < DB; ++db) {
       const __bf16* vp = v_lds + (16 * w + 4 * g16 + (l16 >> 2)) * VP + 16 * db + 4 * (l16 & 3);
-      acc[db] = mfma16x16x16(lds_read_tr4(vp), pb, acc[db] * alpha);
+      const bf16x4 vfrag = lds_read_tr4(vp);
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) acc[cg][db] = mfma16x16x16(vfrag, pb[cg], acc[cg][db] * alpha[cg]);
     }
     __syncthreads();   // the tile buffer is refilled at the top of the next iteration
   }
 
-  // merge the four waves: lanes of one query column share m_run; sum l over the 4 row groups
-  l_run += __shfl_xor(l_run, 16);
-  l_run = xhalf_sum(l_run);
+  // merge the four waves, one column group at a time: lanes of one column share
+  // m_run; l sums over the 4 row groups
   float* o_s = (float*)smem;                       // [4][16][D]
   float* m_s = o_s + 4 * 16 * D;                   // [4][16]
   float* l_s = m_s + 4 * 16;                       // [4][16]
   if (n_tiles > 0) __syncthreads();
 #pragma unroll
-  for (int db = 0; db < DB; ++db)
+  for (int cg = 0; cg < NCG; ++cg) {
+    float lr = l_run[cg];
+    lr += __shfl_xor(lr, 16);
+    lr = xhalf_sum(lr);
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o_s[(w * 16 + l16) * D + 16 * db + 4 * g16 + r] = acc[db][r];
-  if (g16 == 0) {
-    m_s[w * 16 + l16] = m_run;
-    l_s[w * 16 + l16] = l_run;
-  }
-  __syncthreads();
+    for (int db = 0; db < DB; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o_s[(w * 16 + l16) * D + 16 * db + 4 * g16 + r] = acc[cg][db][r];
+    if (g16 == 0) {
+      m_s[w * 16 + l16] = m_run[cg];
+      l_s[w * 16 + l16] = lr;
+    }
+    __syncthreads();
 
-  for (int e = tid; e < a.group * D; e += T::NT) {
-    const int q = e / D, d = e % D;
-    float M = NEG_INF;
+    const int c0 = (cu * NCG + cg) * 16;
+    const int ncol = min(16, cols - c0);
+    for (int e = tid; e < ncol * D; e += T::NT) {
+      const int q = e / D, d = e % D;
+      float M = NEG_INF;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, m_s[ww * 16 + q]);
-    float Lsum = 0.f, O = 0.f;
+      for (int ww = 0; ww < 4; ++ww) M = fmaxf(M, m_s[ww * 16 + q]);
+      float Lsum = 0.f, O = 0.f;
 #pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
-      const float mw = m_s[ww * 16 + q];
-      const float wt = (mw == NEG_INF) ? 0.f : fast_exp2(mw - M);
-      Lsum += wt * l_s[ww * 16 + q];
-      O += wt * o_s[(ww * 16 + q) * D + d];
+      for (int ww = 0; ww < 4; ++ww) {
+        const float mw = m_s[ww * 16 + q];
+        const float wt = (mw == NEG_INF) ? 0.f : fast_exp2(mw - M);
+        Lsum += wt * l_s[ww * 16 + q];
+        O += wt * o_s[(ww * 16 + q) * D + d];
+      }
+      const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+      const float lse = Lsum > 0.f ? (M + __log2f(Lsum)) * kLn2 : NEG_INF;
+      const int c = c0 + q;
+      const int t = c / a.group;
+      const int h = g * a.group + c % a.group;
+      const int64_t row = ((int64_t)b * a.q_len + t) * a.hq + h;     // [B, q_len, Hq]
+      if (a.splits == 1) {
+        a.o[row * D + d] = (__bf16)(O * inv);
+        if (d == 0) a.lse[row] = lse;
+      } else {
+        const int64_t pi = (int64_t)s * a.batch * a.q_len * a.hq + row;
+        a.o_part[pi * D + d] = O * inv;
+        if (d == 0) a.lse_part[pi] = lse;
+      }
     }
-    const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
-    const float lse = Lsum > 0.f ? (M + __log2f(Lsum)) * kLn2 : NEG_INF;
-    const int h = g * a.group + q;
-    if (a.splits == 1) {
-      a.o[((int64_t)b * a.hq + h) * D + d] = (__bf16)(O * inv);
-      if (d == 0) a.lse[(int64_t)b * a.hq + h] = lse;
-    } else {
-      const int64_t pi = ((int64_t)s * a.batch + b) * a.hq + h;
-      a.o_part[pi * D + d] = O * inv;
-      if (d == 0) a.lse_part[pi] = lse;
-    }
+    if (cg + 1 < NCG) __syncthreads();   // the merge buffers are rewritten by the next group
   }
 }
 
@@ -204,9 +249,9 @@ __global__ __launch_bounds__(256, 4) void decode_kernel(DecodeArgs a) {
 // O = sum_s exp(LSE_s - LSE) O_s.  Splits with LSE_s = -inf (no keys) weigh 0.
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
-  const int bh = blockIdx.x;            // b * hq + h
+  const int bh = blockIdx.x;            // (b * q_len + t) * hq + h
   const int d = threadIdx.x;
-  const int64_t plane = (int64_t)a.batch * a.hq;
+  const int64_t plane = (int64_t)a.batch * a.q_len * a.hq;
   const float NEG_INF = -__builtin_inff();
   float M = NEG_INF;
   for (int s = 0; s < a.splits; ++s) M = fmaxf(M, a.lse_part[s * plane + bh]);
@@ -224,22 +269,38 @@ __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
 }
 
 int decode_chunk_align() { return DecTile<128>::BN; }
-int decode_blocks_per_cu() { return 4; }   // LDS and registers of the d = 128 kernel allow four
+
+// Two 16-column groups at most: four would spill at d = 128 with two waves per
+// SIMD; wider query tiles use more column units (the KV chunk is then read once
+// per unit).
+int decode_col_groups(int columns) { return columns <= 16 ? 1 : 2; }
+int decode_blocks_per_cu(int columns) { return decode_col_groups(columns) == 1 ? 4 : 2; }
+
+template <int D>
+static void launch_decode_d(const DecodeArgs& a, int ncg, unsigned grid, hipStream_t stream) {
+  if (ncg == 1)
+    hipLaunchKernelGGL((decode_kernel<D, 1>), dim3(grid), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((decode_kernel<D, 2>), dim3(grid), dim3(256), 0, stream, a);
+}
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t stream) {
-  const int64_t grid = (int64_t)a.batch * a.hkv * a.splits;
+  const int cols = a.group * a.q_len;
+  const int ncg = decode_col_groups(cols);
+  const int n_cu = ((cols + 15) / 16 + ncg - 1) / ncg;
+  const int64_t grid = (int64_t)a.batch * a.hkv * a.splits * n_cu;
   if (grid <= 0 || grid > (1ll << 31) - 1) return hipErrorInvalidValue;
   switch (head_dim) {
-    case 64: hipLaunchKernelGGL(decode_kernel<64>, dim3((unsigned)grid), dim3(256), 0, stream, a); break;
-    case 96: hipLaunchKernelGGL(decode_kernel<96>, dim3((unsigned)grid), dim3(256), 0, stream, a); break;
-    case 128: hipLaunchKernelGGL(decode_kernel<128>, dim3((unsigned)grid), dim3(256), 0, stream, a); break;
+    case 64: launch_decode_d<64>(a, ncg, (unsigned)grid, stream); break;
+    case 96: launch_decode_d<96>(a, ncg, (unsigned)grid, stream); break;
+    case 128: launch_decode_d<128>(a, ncg, (unsigned)grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
 hipError_t launch_decode_combine(const DecodeArgs& a, int head_dim, hipStream_t stream) {
-  const int64_t grid = (int64_t)a.batch * a.hq;
+  const int64_t grid = (int64_t)a.batch * a.q_len * a.hq;
   switch (head_dim) {
     case 64: hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((unsigned)grid), dim3(64), 0, stream, a); break;
     case 96: hipLaunchKernelGGL(decode_combine_kernel<96>, dim3((unsigned)grid), dim3(96), 0, stream, a); break;

@@ -156,11 +156,14 @@ struct DecodeArgs {
   int32_t page_size;
   int32_t max_pages;
   int32_t splits;
+  int32_t q_len;            // query tokens per sequence (1 = single-token decode)
+  int32_t causal;           // bottom-right mask over the q_len tokens
   float scale_log2;
 };
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeArgs& a, int head_dim, hipStream_t stream);
 int decode_chunk_align();
-int decode_blocks_per_cu();   // decode workgroups resident per CU
+int decode_col_groups(int columns);      // 16-column query groups per decode workgroup
+int decode_blocks_per_cu(int columns);   // decode workgroups resident per CU
 
 }  // namespace jfa

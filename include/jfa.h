@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define JFA_ABI_VERSION 1
+#define JFA_ABI_VERSION 2
 
 /* Same type as hipStream_t, declared without including the HIP headers. */
 struct ihipStream_t;
@@ -137,17 +137,25 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p,
                      void* workspace, size_t workspace_bytes, jfa_stream_t stream);
 
 /*
- * Split-KV paged decode: one query token per sequence.
- *   q           [B, Hq, d]                            bf16
+ * Split-KV paged decode of q_len (1..16) new tokens per sequence: single-token
+ * decode, and the few-token shapes of speculative decoding or chunked prefill
+ * ("Optimizing FlashAttention-4 for Efficient Inference": one or a few tokens
+ * at a time against cached KV, PR 1940 and PR 1993).
+ *   q           [B, q_len, Hq, d]                     bf16 (q_len = 1: [B, Hq, d])
  *   k_cache,
  *   v_cache     [num_pages, page_size, Hkv, d]        bf16
  *   page_table  [B, max_pages_per_seq]                int32, physical page of each logical page
  *   seqlens_k   [B]                                   int32, KV length of each sequence
- *   o           [B, Hq, d]                            bf16
- *   lse         [B, Hq]                               fp32, natural log
+ *                                                      (the new tokens included)
+ *   o           [B, q_len, Hq, d]                     bf16
+ *   lse         [B, q_len, Hq]                        fp32, natural log
  * Token t of sequence b lives in slot t % page_size of page
- * page_table[b][t / page_size].  The Hq/Hkv query heads that share a KV head are
- * processed together so every KV byte is read once.  Each sequence's tokens are
+ * page_table[b][t / page_size].  With causal = 1 the q_len tokens are the last
+ * ones of the sequence: token i (0-based) sees keys j <= i + seqlens_k[b] - q_len
+ * (bottom-right alignment); a token that sees no key gets O = 0, LSE = -inf.
+ * The Hq/Hkv query heads that share a KV head, for all q_len tokens, form the
+ * columns of one query tile (only real rows: no padding to a fixed tile height),
+ * so every KV byte is read once per 64 such columns.  Each sequence's tokens are
  * cut into num_splits contiguous chunks processed in parallel; every chunk
  * leaves a normalised partial output and its LSE, and a final pass merges them
  * with weights exp(LSE_s - LSE).  num_splits = 0 picks a count from the problem
@@ -156,13 +164,15 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p,
 typedef struct {
   int32_t batch;              /* B >= 1 */
   int32_t num_heads_q;        /* Hq >= 1 */
-  int32_t num_heads_kv;       /* Hkv >= 1, Hq % Hkv == 0, Hq / Hkv <= 16 */
+  int32_t num_heads_kv;       /* Hkv >= 1, Hq % Hkv == 0, (Hq / Hkv) * q_len <= 256 */
   int32_t head_dim;           /* d in {64, 96, 128} */
   int32_t page_size;          /* >= 1, any value */
   int32_t num_pages;          /* pages in the cache, >= 1 */
   int32_t max_pages_per_seq;  /* columns of page_table, >= 1 */
   int32_t num_splits;         /* 0 = automatic, else 1 .. 128 */
   float softmax_scale;        /* <= 0 selects 1/sqrt(d) */
+  int32_t q_len;              /* new tokens per sequence, 1 .. 16 */
+  int32_t causal;             /* 0 or 1: bottom-right mask over the q_len tokens */
 } jfa_decode_params_t;
 
 size_t jfa_decode_workspace_size(const jfa_decode_params_t* p);

@@ -7,5 +7,5 @@ autograd, central finite differences, and invariants of the softmax Jacobian).
 from .attention import (  # noqa: F401
     default_scale, sequence_forward, sequence_backward,
     attention_forward, attention_backward,
-    broadcast_q_forward, broadcast_q_backward, decode_forward,
+    broadcast_q_forward, broadcast_q_backward, decode_forward, decode_forward_multi,
 )

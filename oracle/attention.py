@@ -31,7 +31,10 @@ Definitions followed (notation of the pages):
   decode    one query per sequence against that sequence's whole KV
             ("Optimizing FlashAttention-4 for Efficient Inference", PR 1940,
             PR 1999/2104 and PR 2186 sections; paging and KV splitting change
-            the memory layout and the order of reduction, not the result).
+            the memory layout and the order of reduction, not the result);
+            a few new tokens per sequence (same page, "one or a few tokens at a
+            time") are the last q_len rows of that sequence, so the optional
+            causal mask is the bottom-right one below.
 
 Readings where the pages are silent:
   * causal masking is bottom-right aligned: key j is visible to query i iff
@@ -51,7 +54,7 @@ import numpy as np
 __all__ = [
     "default_scale", "sequence_forward", "sequence_backward",
     "attention_forward", "attention_backward",
-    "broadcast_q_forward", "broadcast_q_backward", "decode_forward",
+    "broadcast_q_forward", "broadcast_q_backward", "decode_forward", "decode_forward_multi",
 ]
 
 
@@ -232,3 +235,17 @@ def decode_forward(q, k, v, cu_seqlens_k, softmax_scale=None):
     cq = np.arange(nb + 1, dtype=np.int64)
     o, lse = attention_forward(q, k, v, cq, cu_seqlens_k, False, softmax_scale)
     return o, np.ascontiguousarray(lse.T)
+
+
+def decode_forward_multi(q, k, v, cu_seqlens_k, causal: bool = False, softmax_scale=None):
+    """Decode of q_len new tokens per sequence: q [B, q_len, Hq, d] against the
+    contiguous (pre-paging) K/V [Tk, Hkv, d].
+
+    The jagged forward with q_len queries per sequence; with causal the queries
+    are the last q_len positions of the sequence (bottom-right alignment).
+    Returns O [B, q_len, Hq, d] and LSE [B, q_len, Hq] (float64).
+    """
+    nb, lq, hq, d = q.shape
+    cq = np.arange(nb + 1, dtype=np.int64) * lq
+    o, lse = attention_forward(q.reshape(nb * lq, hq, d), k, v, cq, cu_seqlens_k, causal, softmax_scale)
+    return o.reshape(nb, lq, hq, d), np.ascontiguousarray(lse.T).reshape(nb, lq, hq)

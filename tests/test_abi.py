@@ -29,7 +29,7 @@ def test_header_declares_and_library_exports():
     for n in names:
         assert hasattr(lib, n), f"missing export {n}"
     assert set(names) == set(L.EXPORTS)
-    assert lib.jfa_abi_version() == 1
+    assert lib.jfa_abi_version() == 2
 
 
 def test_header_compiles_as_c(tmp_path):
@@ -91,7 +91,7 @@ def test_misaligned_workspace_is_rejected():
     assert lib.jfa_fwd(ctypes.byref(p), d, d, d, d, d, d, d, mis, nf, None) == L.JFA_ERR_INVALID_ARGUMENT
     assert lib.jfa_bwd(ctypes.byref(p), d, d, d, d, d, d, d, d, d, d, d, mis, nb, None) == L.JFA_ERR_INVALID_ARGUMENT
     pd = L.DecodeParams(batch=2, num_heads_q=32, num_heads_kv=8, head_dim=128, page_size=16, num_pages=10,
-                        max_pages_per_seq=5, num_splits=4, softmax_scale=0.0)
+                        max_pages_per_seq=5, num_splits=4, softmax_scale=0.0, q_len=1, causal=0)
     nd = lib.jfa_decode_workspace_size(ctypes.byref(pd))
     assert lib.jfa_decode_paged(ctypes.byref(pd), d, d, d, d, d, d, d, mis, nd, None) == L.JFA_ERR_INVALID_ARGUMENT
 
@@ -104,7 +104,9 @@ def test_empty_problem_is_a_no_op():
 
 DEC_BAD = [
     (dict(page_size=0), 1), (dict(num_splits=129), 1), (dict(num_splits=-1), 1), (dict(head_dim=48), 2),
-    (dict(num_heads_q=34, num_heads_kv=2), 2), (dict(num_heads_q=30), 1), (dict(num_pages=0), 1),
+    (dict(num_heads_q=514, num_heads_kv=2), 2), (dict(num_heads_q=34, num_heads_kv=2, q_len=16), 2),
+    (dict(num_heads_q=30), 1), (dict(num_pages=0), 1),
+    (dict(q_len=0), 1), (dict(q_len=17), 1), (dict(causal=2), 1),
 ]
 
 
@@ -112,7 +114,7 @@ DEC_BAD = [
 def test_invalid_decode_arguments(kw, status):
     L, lib = _lib()
     base = dict(batch=2, num_heads_q=32, num_heads_kv=8, head_dim=128, page_size=16, num_pages=10,
-                max_pages_per_seq=5, num_splits=4, softmax_scale=0.0)
+                max_pages_per_seq=5, num_splits=4, softmax_scale=0.0, q_len=1, causal=0)
     base.update(kw)
     p = L.DecodeParams(**base)
     d = ctypes.c_void_p(16)
@@ -122,8 +124,11 @@ def test_invalid_decode_arguments(kw, status):
 def test_decode_workspace_query():
     L, lib = _lib()
     p = L.DecodeParams(batch=32, num_heads_q=32, num_heads_kv=8, head_dim=128, page_size=16, num_pages=100,
-                       max_pages_per_seq=1024, num_splits=4, softmax_scale=0.0)
+                       max_pages_per_seq=1024, num_splits=4, softmax_scale=0.0, q_len=1, causal=0)
     assert lib.jfa_decode_workspace_size(ctypes.byref(p)) >= 4 * 32 * 32 * 129 * 4
+    p.q_len = 4
+    assert lib.jfa_decode_workspace_size(ctypes.byref(p)) >= 4 * 32 * 4 * 32 * 129 * 4   # partials per token
+    p.q_len = 1
     p.num_splits = 1
     assert lib.jfa_decode_workspace_size(ctypes.byref(p)) == 0
     d = ctypes.c_void_p(256)

@@ -114,3 +114,60 @@ def test_decode_equals_forward_with_one_query(jfa):
     torch.cuda.synchronize()
     assert np.abs(o - host(of)).max() <= 2e-2
     assert np.abs(lse - host(lf).T).max() <= 1e-3
+
+
+# ------------------------------------------------------------ a few new tokens per sequence
+def _ref_multi(inp, causal, scale=None):
+    f = lambda x: x.astype(np.float64)
+    return oracle.decode_forward_multi(f(inp.q), f(inp.k), f(inp.v), inp.cu_k, causal, scale)
+
+
+@pytest.mark.parametrize("q_len", [2, 3, 4, 8, 16])
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (6, 6), (16, 1)])
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_multi_token(jfa, q_len, hq, hkv, causal):
+    """Speculative-decode / chunked-prefill shapes: q_len tokens per sequence, GQA
+    ratios 4, 1 and 16 (up to 256 query columns per KV head), lengths shorter than
+    q_len included (causal tokens that see no key get O = 0, LSE = -inf)."""
+    lens = [1, 63, 64, 65, 300, 0, 700, 17, 5]
+    inp = workloads.decode(40 + q_len, lens, hq, hkv, 128, 16, q_len=q_len)
+    _say(f"decode multi q_len={q_len} hq={hq} hkv={hkv} causal={causal}")
+    d = _Dev(inp)
+    ro, rl = _ref_multi(inp, causal)
+    for splits in (1, 3, 0):
+        o, lse = jfa.jfa_decode_paged(d.q, d.kc, d.vc, d.pt, d.sl, splits, causal=causal)
+        torch.cuda.synchronize()
+        check_o(host(o), ro, f"O splits={splits}")
+        check_lse(host(lse), rl, f"LSE splits={splits}")
+
+
+@pytest.mark.parametrize("page_size", [1, 128])
+@pytest.mark.parametrize("dim", [64, 96])
+def test_decode_multi_token_pages_dims(jfa, page_size, dim):
+    inp = workloads.decode(55, [3, 200, 129, 64], 8, 2, dim, page_size, q_len=5)
+    d = _Dev(inp)
+    ro, rl = _ref_multi(inp, True)
+    for splits in (1, 2):
+        o, lse = jfa.jfa_decode_paged(d.q, d.kc, d.vc, d.pt, d.sl, splits, causal=True)
+        torch.cuda.synchronize()
+        check_o(host(o), ro)
+        check_lse(host(lse), rl)
+
+
+def test_decode_multi_token_config_sampled(jfa):
+    """Speculative decode at the decode config's size: B=32, 4 new tokens, Hq 32 / Hkv 8,
+    d=128, KV lengths U{4096..16384}, page 16, causal; sampled sequences vs the oracle."""
+    rng = np.random.default_rng(0)
+    lens = rng.integers(4096, 16385, size=32)
+    inp = workloads.decode(0, lens, 32, 8, 128, 16, max_pages_per_seq=1024, tail_fill=0.0, q_len=4)
+    d = _Dev(inp)
+    o, lse = jfa.jfa_decode_paged(d.q, d.kc, d.vc, d.pt, d.sl, 0, causal=True)
+    torch.cuda.synchronize()
+    o, lse = host(o), host(lse)
+    f = lambda x: x.astype(np.float64)
+    for b in (0, 13, 31):
+        ks, ke = inp.cu_k[b], inp.cu_k[b + 1]
+        ro, rl = oracle.decode_forward_multi(f(inp.q[b:b + 1]), f(inp.k[ks:ke]), f(inp.v[ks:ke]),
+                                             np.array([0, ke - ks]), True)
+        check_o(o[b:b + 1], ro, f"O[seq {b}]")
+        check_lse(lse[b:b + 1], rl, f"LSE[seq {b}]")

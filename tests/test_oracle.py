@@ -316,6 +316,32 @@ def test_decode_is_forward_with_one_query():
             np.testing.assert_allclose(lse[b, h], lb[0], atol=1e-14)
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_decode_multi_token_is_prefix_attention(causal):
+    """q_len new tokens per sequence: with the bottom-right mask token t attends to
+    exactly the key prefix [0, L - q_len + t] (checked with an unmasked call on the
+    truncated keys), without it to all L keys; a token with an empty prefix gets
+    O = 0 and LSE = -inf."""
+    lq = 3
+    inp = workloads.decode(92, [6, 2, 9, 3], heads_q=4, heads_kv=2, head_dim=8, page_size=4, q_len=lq)
+    q, k, v = (x.astype(np.float64) for x in (inp.q, inp.k, inp.v))
+    o, lse = oracle.decode_forward_multi(q, k, v, inp.cu_k, causal)
+    assert o.shape == q.shape and lse.shape == q.shape[:3]
+    for b in range(4):
+        ks, ke = inp.cu_k[b], inp.cu_k[b + 1]
+        L = ke - ks
+        for t in range(lq):
+            n = max(0, min(L, L - lq + t + 1)) if causal else L
+            for h in range(4):
+                if n == 0:
+                    assert np.all(o[b, t, h] == 0) and np.isneginf(lse[b, t, h])
+                    continue
+                ob, lb, _ = oracle.sequence_forward(q[b, t, h][None], k[ks:ks + n, h // 2], v[ks:ks + n, h // 2],
+                                                    1 / math.sqrt(8))
+                np.testing.assert_allclose(o[b, t, h], ob[0], atol=1e-14)
+                np.testing.assert_allclose(lse[b, t, h], lb[0], atol=1e-14)
+
+
 # ----------------------------------------------------------------- planted mistakes are caught
 def test_pins_catch_planted_mistakes(monkeypatch):
     """A wrong sign, a missing scale or a transposed operand in the oracle fails a pin."""

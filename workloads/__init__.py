@@ -168,12 +168,13 @@ class BroadcastInputs:
 
 @dataclass
 class DecodeInputs:
-    """Single-token decode against a paged KV cache.
+    """Decode of one (q [B, Hq, d]) or a few (q [B, q_len, Hq, d]) new tokens per
+    sequence against a paged KV cache.
 
     ``k``/``v`` are the contiguous (pre-paging) packed caches; ``k_cache``/``v_cache``
     hold the very same rows scattered into pages through ``page_table``.
     """
-    q: np.ndarray            # [B, Hq, d]
+    q: np.ndarray            # [B, Hq, d] or [B, q_len, Hq, d]
     k: np.ndarray            # [Tk, Hkv, d] contiguous
     v: np.ndarray            # [Tk, Hkv, d]
     cu_k: np.ndarray         # int32 [B+1]
@@ -265,8 +266,11 @@ def broadcast_q(seed: int = 0, sparsity: float = 0.5, batch: int = 512, max_len:
 
 def decode(seed: int, seqlens, heads_q: int = 32, heads_kv: int = 8, head_dim: int = 128,
            page_size: int = 16, max_pages_per_seq: Optional[int] = None, tail_fill: float = float("nan"),
-           name: str = "", _rng=None) -> DecodeInputs:
+           name: str = "", _rng=None, q_len: int = 1) -> DecodeInputs:
     """Paged decode inputs over explicit KV lengths.
+
+    q is [B, Hq, d] for q_len = 1, else [B, q_len, Hq, d] (the new tokens are the
+    last q_len of each sequence's KV length).
 
     num_pages = sum_b ceil(L_b / page_size).  Physical page ids are a seeded
     permutation of [0, num_pages) handed out in (sequence, logical page) order.
@@ -285,7 +289,7 @@ def decode(seed: int, seqlens, heads_q: int = 32, heads_kv: int = 8, head_dim: i
     perm = rng.permutation(num_pages).astype(np.int32)
     cu_k = offsets(seqlens)
     tk = int(cu_k[-1])
-    q = _normal_bf16(rng, (b, heads_q, head_dim))
+    q = _normal_bf16(rng, (b, heads_q, head_dim) if q_len == 1 else (b, q_len, heads_q, head_dim))
     k = _normal_bf16(rng, (tk, heads_kv, head_dim))
     v = _normal_bf16(rng, (tk, heads_kv, head_dim))
 
