@@ -131,8 +131,18 @@ int64_t lse_elems(const jfa_attn_params_t* p) {
   return p->broadcast_q ? (int64_t)p->batch * p->num_heads_q * p->total_q : (int64_t)p->num_heads_q * p->total_q;
 }
 
+// Broadcast-Q dQ: items split into chunks, enough (query tile, head, chunk) units
+// for two per CU; each chunk owns an fp32 partial of dQ.
+int bcast_dq_chunks(const jfa_attn_params_t* p) {
+  const int64_t tiles_heads = (int64_t)cdiv_i(p->total_q, bwd_dq_rows()) * p->num_heads_q;
+  const int64_t want = std::max<int64_t>(1, (2LL * cu_count() + tiles_heads - 1) / tiles_heads);
+  const int per = cdiv_i(p->batch, std::min<int64_t>(p->batch, want));
+  return cdiv_i(p->batch, per);
+}
+
 struct BwdLayout {
-  size_t delta = 0, dq_acc = 0;
+  size_t delta = 0, dq_part = 0;
+  int chunks = 0;
   SchedLayout dq_list, dkdv_list;
   size_t end = 0;
 };
@@ -142,8 +152,9 @@ BwdLayout bwd_layout(const jfa_attn_params_t* p) {
   l.delta = 0;
   size_t next = align_up((size_t)lse_elems(p) * sizeof(float));
   if (p->broadcast_q) {
-    l.dq_acc = next;
-    next = align_up(next + (size_t)p->total_q * p->num_heads_q * p->head_dim * sizeof(float));
+    l.chunks = bcast_dq_chunks(p);
+    l.dq_part = next;
+    next = align_up(next + (size_t)l.chunks * p->total_q * p->num_heads_q * p->head_dim * sizeof(float));
   }
   const int64_t groups = (int64_t)p->batch * p->num_heads_kv;
   l.dq_list = sched_layout(next, dq_max_entries(p) * p->num_heads_q, p->broadcast_q ? 0 : groups);
@@ -304,7 +315,7 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   hipStream_t stream = (hipStream_t)stream_;
   const float scale = eff_scale(p->softmax_scale, p->head_dim);
   float* delta = at<float>(workspace, L.delta);
-  float* dq_acc = p->broadcast_q ? at<float>(workspace, L.dq_acc) : nullptr;
+  float* dq_part = p->broadcast_q ? at<float>(workspace, L.dq_part) : nullptr;
   const int64_t dq_elems = (int64_t)p->total_q * p->num_heads_q * p->head_dim;
   const int cus = cu_count();
 
@@ -319,7 +330,7 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   ba.cu_q = cu_seqlens_q;
   ba.cu_k = cu_seqlens_k;
   ba.dq = (__bf16*)dq;
-  ba.dq_acc = dq_acc;
+  ba.dq_part = dq_part;
   ba.dk = (__bf16*)dk;
   ba.dv = (__bf16*)dv;
   ba.batch = p->batch;
@@ -369,20 +380,18 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   }
 
   if (p->total_q > 0) {
-    // Broadcast-Q: delta = rowsum(dO * O) for every item and zero the fp32 dQ
-    // accumulator.  Self-attention computes delta inside the dQ kernel.
+    // Broadcast-Q: delta = rowsum(dO * O) for every item.  Self-attention
+    // computes delta inside the dQ kernel.
     if (p->broadcast_q) {
     BwdPreArgs pa{};
     pa.o = (const __bf16*)o;
     pa.dout = (const __bf16*)dout;
     pa.delta = delta;
-    pa.dq_acc = dq_acc;
     pa.rows = p->broadcast_q ? (int64_t)p->batch * p->total_q : p->total_q;
     pa.hq = p->num_heads_q;
     pa.head_dim = p->head_dim;
     pa.lse_cols = p->total_q;
     pa.bcast = p->broadcast_q;
-    pa.dq_elems = dq_elems;
     e = launch_bwd_pre(pa, stream);
     if (e != hipSuccess) return JFA_ERR_HIP;
     }
@@ -391,9 +400,8 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
     if (p->broadcast_q) {
       const int qtiles = cdiv_i(p->total_q, bwd_dq_rows());
       const int64_t tiles_heads = (int64_t)qtiles * p->num_heads_q;
-      int chunks = (int)std::min<int64_t>(p->batch, std::max<int64_t>(1, (2LL * cus + tiles_heads - 1) / tiles_heads));
-      ba.bcast_chunk = cdiv_i(p->batch, chunks);
-      ba.bcast_chunks = cdiv_i(p->batch, ba.bcast_chunk);
+      ba.bcast_chunks = L.chunks;
+      ba.bcast_chunk = cdiv_i(p->batch, L.chunks);
       ba.bcast_units = (int)(tiles_heads * ba.bcast_chunks);
       TimedRegion tr(JFA_TIMING_BWD_DQ, stream);
       e = launch_bwd_dq(ba, p->head_dim, std::max(1, std::min(ba.bcast_units, 2 * cus)), stream);
@@ -423,9 +431,10 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
 
   if (p->broadcast_q && p->total_q > 0) {
     DqConvertArgs ca{};
-    ca.dq_acc = dq_acc;
+    ca.dq_part = dq_part;
     ca.dq = (__bf16*)dq;
     ca.n = dq_elems;
+    ca.chunks = L.chunks;
     ca.scale = scale;
     e = launch_dq_convert(ca, stream);
     if (e != hipSuccess) return JFA_ERR_HIP;

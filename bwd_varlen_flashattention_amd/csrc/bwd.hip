@@ -10,8 +10,8 @@
 // every item adds its dQ into the one shared dQ.
 //
 // Kernels:
-//   bwd_pre_kernel   delta (fp32, laid out like LSE); zeroes the fp32 dQ
-//                    accumulator used only by broadcast-Q
+//   bwd_pre_kernel   broadcast-Q only: delta (fp32, laid out like LSE) for
+//                    every item; self-attention computes delta in the dQ kernel
 //   bwd_dkdv_kernel  persistent, key-stationary: a workgroup owns 128 keys of one
 //                    KV head; K/V fragments stay in VGPRs and the dK^T/dV^T
 //                    accumulators in registers across all query tiles and all
@@ -26,8 +26,10 @@
 //                    and accumulates dQ^T += K^T dS^T in registers, with dS^T
 //                    straight from the accumulators and K^T staged transposed.
 //                    dQ is written once per query tile: no atomics, so dQ is
-//                    deterministic.  Broadcast-Q splits the items into chunks
-//                    whose partial dQ are added in fp32 (then dq_convert).
+//                    deterministic.  Broadcast-Q splits the items into chunks;
+//                    each chunk writes its fp32 partial dQ to a slice of its
+//                    own and dq_convert adds the slices in chunk order, so
+//                    broadcast-Q dQ is deterministic as well.
 //
 // The dQ kernel repeats S and dP (4d of the 14d flops per query-key pair); the
 // alternative -- dS K accumulated with fp32 atomics from the key-stationary
@@ -74,18 +76,11 @@ __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(BwdPreArgs a) {
     }
     a.delta[di] = acc;
   }
-  if (a.dq_acc) {   // broadcast-Q only: zero the fp32 dQ accumulator (grid-stride over float4)
-    const int64_t n4 = a.dq_elems / 4;
-    const int64_t stride = (int64_t)gridDim.x * kPreThreads;
-    for (int64_t i = gtid; i < n4; i += stride) ((f32x4*)a.dq_acc)[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int64_t i = n4 * 4 + gtid; i < a.dq_elems; i += stride) a.dq_acc[i] = 0.f;
-  }
 }
 
 hipError_t launch_bwd_pre(const BwdPreArgs& a, hipStream_t stream) {
   const int64_t threads = a.rows * a.hq * 16;
   int64_t blocks = (threads + kPreThreads - 1) / kPreThreads;
-  if (a.dq_acc && blocks < 256) blocks = 256;
   if (blocks < 1) blocks = 1;
   if (blocks > (1 << 30)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)blocks), dim3(kPreThreads), 0, stream, a);
@@ -93,16 +88,23 @@ hipError_t launch_bwd_pre(const BwdPreArgs& a, hipStream_t stream) {
 }
 
 // ----------------------------------------------------------------------------- dQ convert (broadcast-Q)
+// dQ = scale * sum of the chunk partials, added in chunk order: the result does
+// not depend on which workgroup finished first.
 __global__ __launch_bounds__(256) void dq_convert_kernel(DqConvertArgs a) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i + 3 < a.n) {
-    const f32x4 x = *(const f32x4*)(a.dq_acc + i);
+    f32x4 x = *(const f32x4*)(a.dq_part + i);
+    for (int c = 1; c < a.chunks; ++c) x += *(const f32x4*)(a.dq_part + (int64_t)c * a.n + i);
     bf16x4 y;
 #pragma unroll
     for (int e = 0; e < 4; ++e) y[e] = (__bf16)(x[e] * a.scale);
     *(bf16x4*)(a.dq + i) = y;
   } else {
-    for (int64_t j = i; j < a.n; ++j) a.dq[j] = (__bf16)(a.dq_acc[j] * a.scale);
+    for (int64_t j = i; j < a.n; ++j) {
+      float x = a.dq_part[j];
+      for (int c = 1; c < a.chunks; ++c) x += a.dq_part[(int64_t)c * a.n + j];
+      a.dq[j] = (__bf16)(x * a.scale);
+    }
   }
 }
 
@@ -407,15 +409,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     __syncthreads();
   }
   for (;;) {
-    int b_lo, b_hi, h, qtile;
+    int b_lo, b_hi, h, qtile, chunk = 0;
     if (BCAST) {
       if (bcast_item >= a.bcast_units) break;
       const int per_tile = a.hq * a.bcast_chunks;
       qtile = bcast_item / per_tile;
       const int rem = bcast_item % per_tile;
       h = rem / a.bcast_chunks;
-      const int c = rem % a.bcast_chunks;
-      b_lo = c * a.bcast_chunk;
+      chunk = rem % a.bcast_chunks;
+      b_lo = chunk * a.bcast_chunk;
       b_hi = min(a.batch, b_lo + a.bcast_chunk);
       bcast_item += gridDim.x;
     } else {
@@ -584,12 +586,14 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
     const int lq_e = BCAST ? a.bcast_nq : a.cu_q[b_lo + 1] - a.cu_q[b_lo];
     if (my_row < lq_e) {
       if (BCAST) {
-        float* dst = a.dq_acc + ((int64_t)my_row * a.hq + h) * D;
+        // this chunk's partial, 4 consecutive d per store (summed in order by dq_convert)
+        float* dst = a.dq_part + (((int64_t)chunk * a.bcast_nq + my_row) * a.hq + h) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            unsafeAtomicAdd(dst + 32 * db + 8 * (r >> 2) + 4 * hh + (r & 3), dqt[db][r]);
+          for (int r4 = 0; r4 < 4; ++r4)
+            *(f32x4*)(dst + 32 * db + 8 * r4 + 4 * hh) =
+                f32x4{dqt[db][4 * r4], dqt[db][4 * r4 + 1], dqt[db][4 * r4 + 2], dqt[db][4 * r4 + 3]};
       } else {
         __bf16* dst = a.dq + ((int64_t)(a.cu_q[b_lo] + my_row) * a.hq + h) * D;
 #pragma unroll

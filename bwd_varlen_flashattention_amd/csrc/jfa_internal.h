@@ -89,13 +89,11 @@ struct BwdPreArgs {
   const __bf16* o;
   const __bf16* dout;
   float* delta;             // same layout as lse
-  float* dq_acc;            // broadcast-Q only (else null): fp32 accumulator, zeroed here
   int64_t rows;             // rows of o / dout (self: total_q, broadcast: B * Nq)
   int32_t hq;
   int32_t head_dim;
   int32_t lse_cols;         // self: total_q; broadcast: Nq
   int32_t bcast;
-  int64_t dq_elems;
 };
 hipError_t launch_bwd_pre(const BwdPreArgs& a, hipStream_t stream);
 
@@ -110,7 +108,7 @@ struct BwdArgs {
   const int32_t* cu_q;
   const int32_t* cu_k;
   __bf16* dq;
-  float* dq_acc;            // broadcast-Q dQ accumulator
+  float* dq_part;           // broadcast-Q: fp32 dQ partial per chunk of items [chunks, Nq, Hq, d]
   __bf16* dk;
   __bf16* dv;
   const WorkItem* items;    // work list of the kernel being launched
@@ -134,9 +132,10 @@ int bwd_dq_rows();          // query rows per dQ item
 int bwd_dq_tile();          // keys per dQ tile
 
 struct DqConvertArgs {
-  const float* dq_acc;
+  const float* dq_part;     // [chunks, n] fp32 partials
   __bf16* dq;
-  int64_t n;                // elements
+  int64_t n;                // elements of dQ
+  int32_t chunks;
   float scale;
 };
 hipError_t launch_dq_convert(const DqConvertArgs& a, hipStream_t stream);

@@ -116,18 +116,19 @@ jfa_status_t jfa_fwd(const jfa_attn_params_t* p,
                      void* o, float* lse,
                      void* workspace, size_t workspace_bytes, jfa_stream_t stream);
 
-/* Bytes of workspace jfa_bwd needs (delta, the two work lists, and for broadcast-Q an fp32 dQ accumulator). */
+/* Bytes of workspace jfa_bwd needs (delta, the two work lists, and for broadcast-Q
+ * one fp32 partial of dQ per chunk of items). */
 size_t jfa_bwd_workspace_size(const jfa_attn_params_t* p);
 
 /*
  * Backward: given q, k, v, the forward's o and lse, and dout, writes dq, dk, dv.
  * P is rebuilt from lse; delta = rowsum(dout * o); dP = dout V^T;
  * dS = P * (dP - delta); dV = P^T dout; dK = scale dS^T Q; dQ = scale dS K.
- * dK/dV of a KV head sum over the Hq/Hkv query heads of its group.  Self-
- * attention results are deterministic (no atomics).  In broadcast-Q mode dQ is
- * the sum over all items, accumulated in fp32 with atomic adds across chunks
- * of items, so its last bits may vary between runs.  Keys that no query sees
- * get dK = dV = 0; queries that see no key get dQ = 0.
+ * dK/dV of a KV head sum over the Hq/Hkv query heads of its group.  Results
+ * are deterministic (no atomics): in broadcast-Q mode dQ, the sum over all
+ * items, is accumulated per chunk of items in fp32 and the chunk partials are
+ * added in a fixed order.  Keys that no query sees get dK = dV = 0; queries
+ * that see no key get dQ = 0.
  */
 jfa_status_t jfa_bwd(const jfa_attn_params_t* p,
                      const void* q, const void* k, const void* v,

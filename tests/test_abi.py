@@ -78,7 +78,7 @@ def test_null_pointers_and_small_workspace():
     nb = lib.jfa_bwd_workspace_size(ctypes.byref(p))
     assert nb >= 4 * 10 * 4           # at least delta (fp32 per query row and head)
     pb = _params(L, broadcast_q=1)
-    assert lib.jfa_bwd_workspace_size(ctypes.byref(pb)) >= 10 * 4 * 128 * 4   # + the fp32 dQ accumulator
+    assert lib.jfa_bwd_workspace_size(ctypes.byref(pb)) >= 10 * 4 * 128 * 4   # + at least one fp32 dQ partial
     assert lib.jfa_bwd(ctypes.byref(p), d, d, d, d, d, d, d, d, d, d, d, d, nb - 1, None) == L.JFA_ERR_WORKSPACE_TOO_SMALL
     assert lib.jfa_bwd(ctypes.byref(p), d, d, d, None, d, d, d, d, d, d, d, d, nb, None) == L.JFA_ERR_INVALID_ARGUMENT
 
