@@ -50,7 +50,8 @@ def pairs_of(cu_q, cu_k, causal, nq=None):
 def decode_bytes(inp):
     """Algorithmic bytes: K+V once, q and o, lse, page-table entries, lengths."""
     hkv, d = inp.k.shape[1], inp.k.shape[2]
-    kv = int(inp.seqlens_k.astype(np.int64).sum()) * hkv * d * 2 * 2
+    elem = 1 if inp.k_cache.dtype == np.uint8 else 2          # fp8 (e4m3) or bf16 cache
+    kv = int(inp.seqlens_k.astype(np.int64).sum()) * hkv * d * elem * 2
     b = inp.q.shape[0]
     rows = int(np.prod(inp.q.shape[:-1]))          # B * q_len * Hq
     pages = int(sum(-(-int(L) // inp.page_size) for L in inp.seqlens_k))
@@ -103,7 +104,12 @@ class DecodeCase:
     def __init__(self, torch, jfa, inp, splits=0, causal=False):
         self.torch, self.jfa, self.inp = torch, jfa, inp
         self.causal = causal
-        self.q, self.kc, self.vc = dev(inp.q, torch), dev(inp.k_cache, torch), dev(inp.v_cache, torch)
+        self.q = dev(inp.q, torch)
+        if inp.k_cache.dtype == np.uint8:       # e4m3 bytes
+            self.kc = torch.from_numpy(inp.k_cache).to("cuda").view(torch.float8_e4m3fn)
+            self.vc = torch.from_numpy(inp.v_cache).to("cuda").view(torch.float8_e4m3fn)
+        else:
+            self.kc, self.vc = dev(inp.k_cache, torch), dev(inp.v_cache, torch)
         self.pt, self.sl = dev(inp.page_table, torch), dev(inp.seqlens_k, torch)
         self.splits = splits
         self.nsplits = jfa.jfa_decode_num_splits(self.q, self.kc, self.pt, splits)
@@ -423,6 +429,15 @@ def sweep(torch, jfa, workloads, args, log):
         dc = DecodeCase(torch, jfa, inp, splits, causal=True)
         ms = timeit(dc.step)
         print(json.dumps({"workload": "decode_ps16_q4_causal", "splits": dc.nsplits, "ms": round(ms, 4),
+                          "tb_s": round(dc.bytes / ms / 1e9, 3)}), flush=True)
+        del dc
+    del inp
+    # fp8 (e4m3) KV cache, single token, page 16 (same lengths as the decode config)
+    inp = workloads.decode(0, lens, 32, 8, 128, 16, max_pages_per_seq=1024, kv_fp8=True)
+    for splits in (4, 8, 0):
+        dc = DecodeCase(torch, jfa, inp, splits)
+        ms = timeit(dc.step)
+        print(json.dumps({"workload": "decode_ps16_fp8kv", "splits": dc.nsplits, "ms": round(ms, 4),
                           "tb_s": round(dc.bytes / ms / 1e9, 3)}), flush=True)
         del dc
     del inp

@@ -111,14 +111,31 @@ def jfa_bwd(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int
     return dq, dk, dv
 
 
-def _decode_params(q, k_cache, page_table, num_splits, scale, causal=False):
-    """q is [B, Hq, d] (one token per sequence) or [B, q_len, Hq, d]."""
+def _kv_fp8(k_cache) -> bool:
+    torch = _torch()
+    return k_cache.dtype in (getattr(torch, "float8_e4m3fn", None), torch.uint8)
+
+
+def _decode_params(q, k_cache, page_table, num_splits, scale, causal=False, k_scale=None, v_scale=None):
+    """q is [B, Hq, d] (one token per sequence) or [B, q_len, Hq, d]; an fp8 cache
+    (float8_e4m3fn, or its raw bytes as uint8) selects the e4m3 path."""
     q_len = 1 if q.dim() == 3 else q.shape[1]
+    fp8 = _kv_fp8(k_cache)
     return DecodeParams(
         batch=q.shape[0], num_heads_q=q.shape[-2], num_heads_kv=k_cache.shape[2], head_dim=q.shape[-1],
         page_size=k_cache.shape[1], num_pages=k_cache.shape[0], max_pages_per_seq=page_table.shape[1],
         num_splits=int(num_splits), softmax_scale=float(scale) if scale is not None else 0.0,
-        q_len=int(q_len), causal=int(bool(causal)))
+        q_len=int(q_len), causal=int(bool(causal)), kv_dtype=1 if fp8 else 0,
+        k_scale=float(k_scale) if k_scale is not None else 0.0, v_scale=float(v_scale) if v_scale is not None else 0.0)
+
+
+def _check_cache(name, t):
+    torch = _torch()
+    if _kv_fp8(t):
+        if t.dim() != 4 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name}: expected a contiguous 4-d CUDA fp8 (e4m3) tensor, got {tuple(t.shape)}")
+    else:
+        _check_bf16(name, t, 4)
 
 
 def jfa_decode_num_splits(q, k_cache, page_table, num_splits: int = 0) -> int:
@@ -128,20 +145,24 @@ def jfa_decode_num_splits(q, k_cache, page_table, num_splits: int = 0) -> int:
 
 def jfa_decode_paged(q, k_cache, v_cache, page_table, seqlens_k, num_splits: int = 0,
                      softmax_scale: Optional[float] = None, out=None, lse=None, workspace=None,
-                     causal: bool = False):
+                     causal: bool = False, k_scale: Optional[float] = None, v_scale: Optional[float] = None):
     """Paged decode of q_len new tokens per sequence against a paged KV cache.
 
     q [B, Hq, d] (one token) or [B, q_len, Hq, d] (q_len <= 16); caches
     [num_pages, page_size, Hkv, d] -> o shaped like q, lse [B, Hq] or [B, q_len, Hq].
     causal: the q_len tokens are the last ones of each sequence (bottom-right mask).
+    FP8 caches (torch.float8_e4m3fn or raw uint8 bytes): K = k_scale * cache value,
+    V = v_scale * cache value.
     """
     torch = _torch()
     lib = load()
     if q.dim() not in (3, 4):
         raise ValueError("q must be [B, Hq, d] or [B, q_len, Hq, d]")
-    _check_bf16("q", q, q.dim()); _check_bf16("k_cache", k_cache, 4); _check_bf16("v_cache", v_cache, 4)
+    _check_bf16("q", q, q.dim()); _check_cache("k_cache", k_cache); _check_cache("v_cache", v_cache)
+    if _kv_fp8(k_cache) != _kv_fp8(v_cache):
+        raise ValueError("k_cache and v_cache must have the same element type")
     _check_i32("page_table", page_table); _check_i32("seqlens_k", seqlens_k)
-    p = _decode_params(q, k_cache, page_table, num_splits, softmax_scale, causal)
+    p = _decode_params(q, k_cache, page_table, num_splits, softmax_scale, causal, k_scale, v_scale)
     o = out if out is not None else torch.empty_like(q)
     l = lse if lse is not None else torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
     need = lib.jfa_decode_workspace_size(ctypes.byref(p))

@@ -55,6 +55,9 @@ class DecodeParams(ctypes.Structure):
         ("softmax_scale", ctypes.c_float),
         ("q_len", ctypes.c_int32),
         ("causal", ctypes.c_int32),
+        ("kv_dtype", ctypes.c_int32),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 

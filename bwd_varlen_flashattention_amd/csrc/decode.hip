@@ -49,7 +49,11 @@ __device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
 // NCG: 16-column query groups per workgroup (1 or 2).  A workgroup handles up to 16*NCG
 // query columns (token, query head of the GQA group) of one (sequence, KV head,
 // split); every K and V fragment it reads from LDS feeds all of its groups.
-template <int D, int NCG>
+// FP8: the KV cache holds OCP e4m3 bytes; rows are widened to bf16 (exactly:
+// every e4m3 value is a bf16 value) when they are written to LDS, and the
+// per-tensor scales are applied to the scores (K, folded into scale_log2 by the
+// host) and to the output (V).
+template <int D, int NCG, bool FP8>
 __global__ __launch_bounds__(256, NCG == 1 ? 4 : 2) void decode_kernel(DecodeArgs a) {
   using T = DecTile<D>;
   constexpr int BN = T::BN, KP = T::KP, VP = T::VP, KK = T::KK, DB = T::DB;
@@ -112,27 +116,61 @@ __global__ __launch_bounds__(256, NCG == 1 ? 4 : 2) void decode_kernel(DecodeArg
   }
 
   const int32_t* pt = a.page_table + (int64_t)b * a.max_pages;
-  u32x4 kr[T::LOADS], vr[T::LOADS];
+  // One 16-byte load per (row, chunk): 8 bf16 columns, or 16 fp8 columns.
+  constexpr int EPL = FP8 ? 16 : 8;                  // elements per 16-byte load
+  constexpr int CHL = D / EPL;                       // loads per row
+  constexpr int NLD = (BN * CHL + T::NT - 1) / T::NT;
+  u32x4 kr[NLD], vr[NLD];
   auto load_regs = [&](int j) {
 #pragma unroll
-    for (int i = 0; i < T::LOADS; ++i) {
+    for (int i = 0; i < NLD; ++i) {
       const int id = tid + i * T::NT;
-      const int r = id / T::CH, c = id % T::CH;
-      const int key = min(k_lo + j * BN + r, k_hi - 1);   // never past the sequence end
-      const int page = pt[key / a.page_size];
-      const int slot = key - (key / a.page_size) * a.page_size;
-      const int64_t off = (((int64_t)page * a.page_size + slot) * a.hkv + g) * D + c * 8;
-      kr[i] = *(const u32x4*)(a.k_cache + off);
-      vr[i] = *(const u32x4*)(a.v_cache + off);
+      if (BN * CHL % T::NT == 0 || id < BN * CHL) {
+        const int r = id / CHL, c = id % CHL;
+        const int key = min(k_lo + j * BN + r, k_hi - 1);   // never past the sequence end
+        const int page = pt[key / a.page_size];
+        const int slot = key - (key / a.page_size) * a.page_size;
+        const int64_t el = (((int64_t)page * a.page_size + slot) * a.hkv + g) * D + c * EPL;
+        const unsigned char* kb = (const unsigned char*)a.k_cache;
+        const unsigned char* vb = (const unsigned char*)a.v_cache;
+        kr[i] = *(const u32x4*)(kb + el * (FP8 ? 1 : 2));
+        vr[i] = *(const u32x4*)(vb + el * (FP8 ? 1 : 2));
+      }
+    }
+  };
+  // 16 e4m3 bytes -> 16 bf16 (two 16-byte stores)
+  auto widen = [&](const u32x4& x, u32x4& lo, u32x4& hi) {
+#pragma unroll
+    for (int w2 = 0; w2 < 4; ++w2) {
+      typedef float f2_t __attribute__((ext_vector_type(2)));
+      const f2_t p0 = __builtin_amdgcn_cvt_pk_f32_fp8(x[w2], false);
+      const f2_t p1 = __builtin_amdgcn_cvt_pk_f32_fp8(x[w2], true);
+      bf16x4 q;
+      q[0] = (__bf16)p0[0]; q[1] = (__bf16)p0[1]; q[2] = (__bf16)p1[0]; q[3] = (__bf16)p1[1];
+      const uint2 u = __builtin_bit_cast(uint2, q);
+      if (w2 < 2) { lo[2 * w2] = u.x; lo[2 * w2 + 1] = u.y; }
+      else { hi[2 * (w2 - 2)] = u.x; hi[2 * (w2 - 2) + 1] = u.y; }
     }
   };
   auto store_lds = [&]() {
 #pragma unroll
-    for (int i = 0; i < T::LOADS; ++i) {
+    for (int i = 0; i < NLD; ++i) {
       const int id = tid + i * T::NT;
-      const int r = id / T::CH, c = id % T::CH;
-      *(u32x4*)&k_lds[r * KP + c * 8] = kr[i];
-      *(u32x4*)&v_lds[r * VP + c * 8] = vr[i];
+      if (BN * CHL % T::NT == 0 || id < BN * CHL) {
+        const int r = id / CHL, c = id % CHL;
+        if constexpr (FP8) {
+          u32x4 k0, k1, v0, v1;
+          widen(kr[i], k0, k1);
+          widen(vr[i], v0, v1);
+          *(u32x4*)&k_lds[r * KP + c * 16] = k0;
+          *(u32x4*)&k_lds[r * KP + c * 16 + 8] = k1;
+          *(u32x4*)&v_lds[r * VP + c * 16] = v0;
+          *(u32x4*)&v_lds[r * VP + c * 16 + 8] = v1;
+        } else {
+          *(u32x4*)&k_lds[r * KP + c * 8] = kr[i];
+          *(u32x4*)&v_lds[r * VP + c * 8] = vr[i];
+        }
+      }
     }
   };
 
@@ -226,7 +264,7 @@ __global__ __launch_bounds__(256, NCG == 1 ? 4 : 2) void decode_kernel(DecodeArg
         Lsum += wt * l_s[ww * 16 + q];
         O += wt * o_s[(ww * 16 + q) * D + d];
       }
-      const float inv = Lsum > 0.f ? 1.f / Lsum : 0.f;
+      const float inv = Lsum > 0.f ? (FP8 ? a.v_scale : 1.f) / Lsum : 0.f;
       const float lse = Lsum > 0.f ? (M + __log2f(Lsum)) * kLn2 : NEG_INF;
       const int c = c0 + q;
       const int t = c / a.group;
@@ -276,12 +314,17 @@ int decode_chunk_align() { return DecTile<128>::BN; }
 int decode_col_groups(int columns) { return columns <= 16 ? 1 : 2; }
 int decode_blocks_per_cu(int columns) { return decode_col_groups(columns) == 1 ? 4 : 2; }
 
-template <int D>
+template <int D, bool FP8>
 static void launch_decode_d(const DecodeArgs& a, int ncg, unsigned grid, hipStream_t stream) {
   if (ncg == 1)
-    hipLaunchKernelGGL((decode_kernel<D, 1>), dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, 1, FP8>), dim3(grid), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((decode_kernel<D, 2>), dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<D, 2, FP8>), dim3(grid), dim3(256), 0, stream, a);
+}
+template <int D>
+static void launch_decode_d(const DecodeArgs& a, int ncg, unsigned grid, hipStream_t stream) {
+  if (a.kv_fp8) launch_decode_d<D, true>(a, ncg, grid, stream);
+  else launch_decode_d<D, false>(a, ncg, grid, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t stream) {

@@ -143,8 +143,8 @@ hipError_t launch_dq_convert(const DqConvertArgs& a, hipStream_t stream);
 // Decode.
 struct DecodeArgs {
   const __bf16* q;
-  const __bf16* k_cache;
-  const __bf16* v_cache;
+  const void* k_cache;      // bf16 or e4m3 bytes
+  const void* v_cache;
   const int32_t* page_table;
   const int32_t* seqlens;
   __bf16* o;                // final output when splits == 1
@@ -157,6 +157,8 @@ struct DecodeArgs {
   int32_t splits;
   int32_t q_len;            // query tokens per sequence (1 = single-token decode)
   int32_t causal;           // bottom-right mask over the q_len tokens
+  int32_t kv_fp8;           // caches hold OCP e4m3 bytes
+  float v_scale;            // fp8 V dequantisation scale (K's is folded into scale_log2)
   float scale_log2;
 };
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t stream);

@@ -137,6 +137,9 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p,
                      void* dq, void* dk, void* dv,
                      void* workspace, size_t workspace_bytes, jfa_stream_t stream);
 
+/* KV-cache element types of jfa_decode_paged. */
+enum { JFA_KV_BF16 = 0, JFA_KV_FP8_E4M3 = 1 };
+
 /*
  * Split-KV paged decode of q_len (1..16) new tokens per sequence: single-token
  * decode, and the few-token shapes of speculative decoding or chunked prefill
@@ -161,6 +164,10 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p,
  * leaves a normalised partial output and its LSE, and a final pass merges them
  * with weights exp(LSE_s - LSE).  num_splits = 0 picks a count from the problem
  * size; 1 writes o/lse directly.
+ * FP8 caches ("Optimizing FlashAttention-4 for Efficient Inference", PR 2109:
+ * FP8 inputs): k_cache / v_cache hold OCP e4m3 bytes (same shapes, one byte per
+ * element) with per-tensor scales; the result is that of bf16 attention on the
+ * dequantised values (every e4m3 value is exact in bf16), for half the KV bytes.
  */
 typedef struct {
   int32_t batch;              /* B >= 1 */
@@ -174,6 +181,9 @@ typedef struct {
   float softmax_scale;        /* <= 0 selects 1/sqrt(d) */
   int32_t q_len;              /* new tokens per sequence, 1 .. 16 */
   int32_t causal;             /* 0 or 1: bottom-right mask over the q_len tokens */
+  int32_t kv_dtype;           /* JFA_KV_BF16 or JFA_KV_FP8_E4M3 (k_cache / v_cache element type) */
+  float k_scale;              /* fp8 caches: K = k_scale * e4m3 value (<= 0 means 1) */
+  float v_scale;              /* fp8 caches: V = v_scale * e4m3 value (<= 0 means 1) */
 } jfa_decode_params_t;
 
 size_t jfa_decode_workspace_size(const jfa_decode_params_t* p);

@@ -171,3 +171,52 @@ def test_decode_multi_token_config_sampled(jfa):
                                              np.array([0, ke - ks]), True)
         check_o(o[b:b + 1], ro, f"O[seq {b}]")
         check_lse(lse[b:b + 1], rl, f"LSE[seq {b}]")
+
+
+# ------------------------------------------------------------ fp8 (e4m3) KV cache
+class _DevFp8(_Dev):
+    def __init__(self, inp):
+        self.q = dev(inp.q, torch)
+        self.kc = torch.from_numpy(inp.k_cache).to("cuda").view(torch.float8_e4m3fn)
+        self.vc = torch.from_numpy(inp.v_cache).to("cuda").view(torch.float8_e4m3fn)
+        self.pt = dev(inp.page_table, torch)
+        self.sl = dev(inp.seqlens_k, torch)
+
+
+@pytest.mark.parametrize("q_len,causal", [(1, False), (4, True), (9, False)])
+@pytest.mark.parametrize("page_size", [1, 16, 128])
+@pytest.mark.parametrize("dim", [64, 96, 128])
+def test_decode_fp8_kv(jfa, q_len, causal, page_size, dim):
+    """FP8 caches: the result equals attention on the dequantised K/V (scales 0.5 and
+    2.0 exercise both scale paths); unused slots hold NaN bytes."""
+    lens = [1, 63, 64, 65, 300, 0, 700, 17]
+    inp = workloads.decode(60 + dim, lens, 8, 2, dim, page_size, q_len=q_len, kv_fp8=True,
+                           k_scale=0.5, v_scale=2.0)
+    d = _DevFp8(inp)
+    f = lambda x: x.astype(np.float64)
+    if q_len == 1:
+        ro, rl = oracle.decode_forward(f(inp.q), f(inp.k), f(inp.v), inp.cu_k)
+    else:
+        ro, rl = oracle.decode_forward_multi(f(inp.q), f(inp.k), f(inp.v), inp.cu_k, causal)
+    for splits in (1, 3, 0):
+        o, lse = jfa.jfa_decode_paged(d.q, d.kc, d.vc, d.pt, d.sl, splits, causal=causal, k_scale=0.5, v_scale=2.0)
+        torch.cuda.synchronize()
+        check_o(host(o), ro, f"O splits={splits}")
+        check_lse(host(lse), rl, f"LSE splits={splits}")
+
+
+def test_decode_fp8_config_sampled(jfa):
+    """FP8 cache at the decode config's size (B=32, Hq 32 / Hkv 8, d=128, U{4096..16384}, page 16)."""
+    rng = np.random.default_rng(0)
+    lens = rng.integers(4096, 16385, size=32)
+    inp = workloads.decode(0, lens, 32, 8, 128, 16, max_pages_per_seq=1024, kv_fp8=True, k_scale=0.25, v_scale=0.25)
+    d = _DevFp8(inp)
+    o, lse = jfa.jfa_decode_paged(d.q, d.kc, d.vc, d.pt, d.sl, 0, k_scale=0.25, v_scale=0.25)
+    torch.cuda.synchronize()
+    o, lse = host(o), host(lse)
+    f = lambda x: x.astype(np.float64)
+    for b in (0, 13, 31):
+        ks, ke = inp.cu_k[b], inp.cu_k[b + 1]
+        ro, rl = oracle.decode_forward(f(inp.q[b:b + 1]), f(inp.k[ks:ke]), f(inp.v[ks:ke]), np.array([0, ke - ks]))
+        check_o(o[b:b + 1], ro, f"O[seq {b}]")
+        check_lse(lse[b:b + 1], rl, f"LSE[seq {b}]")

@@ -77,3 +77,29 @@ def test_repage_keeps_kv_and_moves_pages():
     for i, L in enumerate(b.seqlens_k):
         for t in range(L):
             np.testing.assert_array_equal(b.k_cache[b.page_table[i, t // 5], t % 5], b.k[b.cu_k[i] + t])
+
+
+def test_e4m3_decoding_matches_its_definition():
+    """The fp8 caches use OCP e4m3 (float8_e4m3fn): sign, 4 exponent bits with bias 7,
+    3 mantissa bits, subnormals m * 2^-9, and only S.1111.111 is NaN (no infinities).
+    Every one of the 256 byte values decodes as that definition says."""
+    import math
+    torch = pytest.importorskip("torch")
+    got = torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+    for x in range(256):
+        s, e, m = x >> 7, (x >> 3) & 15, x & 7
+        if e == 15 and m == 7:
+            assert math.isnan(got[x])
+            continue
+        val = m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        assert got[x] == (-val if s else val), x
+
+
+def test_fp8_decode_inputs_are_exact_dequantisations():
+    inp = workloads.decode(3, [5, 40], 8, 2, 64, 16, q_len=2, kv_fp8=True, k_scale=0.5, v_scale=2.0)
+    torch = pytest.importorskip("torch")
+    kc = torch.from_numpy(inp.k_cache).view(torch.float8_e4m3fn).float().numpy()
+    # token 3 of sequence 1 lives in page_table[1][0], slot 3
+    page = inp.page_table[1, 0]
+    np.testing.assert_array_equal(kc[page, 3] * 0.5, inp.k[inp.cu_k[1] + 3])
+    assert np.all(inp.k_cache[inp.page_table[0, 0], 5:] == 0x7F)     # unused slots hold the NaN byte

@@ -266,8 +266,13 @@ def broadcast_q(seed: int = 0, sparsity: float = 0.5, batch: int = 512, max_len:
 
 def decode(seed: int, seqlens, heads_q: int = 32, heads_kv: int = 8, head_dim: int = 128,
            page_size: int = 16, max_pages_per_seq: Optional[int] = None, tail_fill: float = float("nan"),
-           name: str = "", _rng=None, q_len: int = 1) -> DecodeInputs:
+           name: str = "", _rng=None, q_len: int = 1, kv_fp8: bool = False, k_scale: float = 1.0,
+           v_scale: float = 1.0) -> DecodeInputs:
     """Paged decode inputs over explicit KV lengths.
+
+    kv_fp8: the caches hold OCP e4m3 bytes (uint8) of K / k_scale and V / v_scale,
+    rounded to nearest by torch's float8_e4m3fn; ``k``/``v`` then hold the exact
+    dequantised values (byte value times scale) and unused slots the NaN byte 0x7F.
 
     q is [B, Hq, d] for q_len = 1, else [B, q_len, Hq, d] (the new tokens are the
     last q_len of each sequence's KV length).
@@ -293,12 +298,27 @@ def decode(seed: int, seqlens, heads_q: int = 32, heads_kv: int = 8, head_dim: i
     k = _normal_bf16(rng, (tk, heads_kv, head_dim))
     v = _normal_bf16(rng, (tk, heads_kv, head_dim))
 
-    page_table, k_cache, v_cache = _page(k, v, seqlens, cu_k, page_size, max_pages_per_seq, perm, tail_fill)
-    return DecodeInputs(q, k, v, cu_k, seqlens, page_size, page_table, k_cache, v_cache, name,
-                        {"num_pages": num_pages})
+    meta = {"num_pages": num_pages}
+    if kv_fp8:
+        kb, k = _e4m3(k, k_scale)
+        vb, v = _e4m3(v, v_scale)
+        page_table, k_cache, v_cache = _page(kb, vb, seqlens, cu_k, page_size, max_pages_per_seq, perm,
+                                             0x7F, np.uint8)
+        meta.update(k_scale=float(k_scale), v_scale=float(v_scale))
+    else:
+        page_table, k_cache, v_cache = _page(k, v, seqlens, cu_k, page_size, max_pages_per_seq, perm, tail_fill)
+    return DecodeInputs(q, k, v, cu_k, seqlens, page_size, page_table, k_cache, v_cache, name, meta)
 
 
-def _page(k, v, seqlens, cu_k, page_size, max_pages_per_seq, perm, tail_fill):
+def _e4m3(x, scale: float):
+    """Round x / scale to OCP e4m3 (torch float8_e4m3fn, nearest even); returns the
+    bytes and the exact dequantised values byte_value * scale (float32)."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x / scale, dtype=np.float32)).to(torch.float8_e4m3fn)
+    return t.view(torch.uint8).numpy().copy(), (t.float() * scale).numpy()
+
+
+def _page(k, v, seqlens, cu_k, page_size, max_pages_per_seq, perm, tail_fill, dtype=np.float32):
     """Scatter contiguous K/V rows into pages; physical ids come from `perm` in (sequence, page) order."""
     b = len(seqlens)
     tk, heads_kv, head_dim = k.shape
@@ -314,8 +334,8 @@ def _page(k, v, seqlens, cu_k, page_size, max_pages_per_seq, perm, tail_fill):
     pos = np.arange(tk, dtype=np.int64) - cu_k[seq_of_token].astype(np.int64)
     phys = page_table[seq_of_token, pos // page_size].astype(np.int64)
     slot = phys * page_size + pos % page_size
-    k_cache = np.full((num_pages * page_size, heads_kv, head_dim), tail_fill, dtype=np.float32)
-    v_cache = np.full((num_pages * page_size, heads_kv, head_dim), tail_fill, dtype=np.float32)
+    k_cache = np.full((num_pages * page_size, heads_kv, head_dim), tail_fill, dtype=dtype)
+    v_cache = np.full((num_pages * page_size, heads_kv, head_dim), tail_fill, dtype=dtype)
     k_cache[slot] = k
     v_cache[slot] = v
     return (page_table, k_cache.reshape(num_pages, page_size, heads_kv, head_dim),
