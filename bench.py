@@ -395,7 +395,9 @@ def sweep(torch, jfa, workloads, args, log):
              ("bcast_s0.1", lambda: workloads.broadcast_q(0, 0.1)), ("bcast_s0.5", lambda: workloads.broadcast_q(0, 0.5)),
              ("bcast_s0.9", lambda: workloads.broadcast_q(0, 0.9)),
              ("dense_causal_d128", lambda: workloads.dense_causal(0, head_dim=128)),
-             ("dense_causal_d96", lambda: workloads.dense_causal(0, head_dim=96))]
+             ("dense_causal_d96", lambda: workloads.dense_causal(0, head_dim=96)),
+             ("gem_s0.5_d256", lambda: workloads.gem(0, 0.5, head_dim=256)),
+             ("dense_causal_d256_h16", lambda: workloads.dense_causal(0, heads=16, head_dim=256))]
     for name, make in cases:
         inp = make()
         jc = JaggedCase(torch, jfa, bcast=inp) if name.startswith("bcast") else JaggedCase(torch, jfa, inp)
@@ -429,6 +431,15 @@ def sweep(torch, jfa, workloads, args, log):
         dc = DecodeCase(torch, jfa, inp, splits, causal=True)
         ms = timeit(dc.step)
         print(json.dumps({"workload": "decode_ps16_q4_causal", "splits": dc.nsplits, "ms": round(ms, 4),
+                          "tb_s": round(dc.bytes / ms / 1e9, 3)}), flush=True)
+        del dc
+    del inp
+    # head dim 256, single token, page 16 (same lengths and heads as the decode config)
+    inp = workloads.decode(0, lens, 32, 8, 256, 16, max_pages_per_seq=1024, tail_fill=0.0)
+    for splits in (4, 8, 0):
+        dc = DecodeCase(torch, jfa, inp, splits)
+        ms = timeit(dc.step)
+        print(json.dumps({"workload": "decode_ps16_d256", "splits": dc.nsplits, "ms": round(ms, 4),
                           "tb_s": round(dc.bytes / ms / 1e9, 3)}), flush=True)
         del dc
     del inp

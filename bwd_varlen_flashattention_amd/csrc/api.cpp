@@ -38,7 +38,7 @@ int cu_count() {
   return n;
 }
 
-bool supported_dim(int d) { return d == 64 || d == 96 || d == 128; }
+bool supported_dim(int d) { return d == 64 || d == 96 || d == 128 || d == 192 || d == 256; }
 
 // ------------------------------------------------------------------ timing
 struct Timing {
@@ -115,7 +115,7 @@ int64_t fwd_max_entries(const jfa_attn_params_t* p) {
 }
 
 int64_t dkdv_max_entries(const jfa_attn_params_t* p) {
-  return cdiv_i(p->total_k, bwd_dkdv_tile()) + (int64_t)p->batch;
+  return (cdiv_i(p->total_k, bwd_dkdv_tile()) + (int64_t)p->batch) * bwd_dkdv_slices(p->head_dim);
 }
 
 int64_t dq_max_entries(const jfa_attn_params_t* p) {
@@ -169,9 +169,9 @@ T* at(void* ws, size_t off) { return (T*)((char*)ws + off); }
 // Work-list fields of the scheduler arguments shared by every launch.
 void set_lists(SchedArgs& sa, const jfa_attn_params_t* p, void* ws, const SchedLayout& L) {
   // one item group per (sequence, KV head); a query-stationary tile has one item
-  // per query head of the GQA group, a key-stationary tile one item
+  // per query head of the GQA group, a key-stationary tile one per head-dim slice
   sa.groups_per_seq = p->num_heads_kv;
-  sa.per_tile = sa.mode == 0 ? p->num_heads_q / p->num_heads_kv : 1;
+  sa.per_tile = sa.mode == 0 ? p->num_heads_q / p->num_heads_kv : bwd_dkdv_slices(p->head_dim);
   sa.n_buckets = kMaxBuckets;
   sa.max_items = L.max_items;
   sa.scratch = at<int32_t>(ws, L.scratch);
@@ -204,9 +204,9 @@ int resolve_splits(const jfa_decode_params_t* p) {
   // about two workgroups per resident slot: the later ones fill in behind units
   // of short sequences, which balances mixed lengths
   const int cols = p->num_heads_q / p->num_heads_kv * p->q_len;
-  const int64_t col_units = cdiv_i(cdiv_i(cols, 16), decode_col_groups(cols));
+  const int64_t col_units = cdiv_i(cdiv_i(cols, 16), decode_col_groups(cols, p->head_dim));
   const int64_t units = (int64_t)p->batch * p->num_heads_kv * col_units;
-  int s = cdiv_i(2 * (int64_t)cu_count() * decode_blocks_per_cu(cols), units);
+  int s = cdiv_i(2 * (int64_t)cu_count() * decode_blocks_per_cu(cols, p->head_dim), units);
   const int64_t max_len = (int64_t)p->max_pages_per_seq * p->page_size;
   const int cap = (int)std::max<int64_t>(1, (max_len + 1023) / 1024);   // at least ~1k keys per split
   if (s > cap) s = cap;
@@ -258,7 +258,7 @@ jfa_status_t jfa_fwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   if (workspace_bytes < L.end) return JFA_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t stream = (hipStream_t)stream_;
 
-  const int bn = fwd_kv_tile();
+  const int bn = fwd_kv_tile(p->head_dim);
   SchedArgs sa{};
   sa.cu_q = cu_seqlens_q;
   sa.cu_k = cu_seqlens_k;
@@ -321,6 +321,7 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   float* dq_part = p->broadcast_q ? at<float>(workspace, L.dq_part) : nullptr;
   const int64_t dq_elems = (int64_t)p->total_q * p->num_heads_q * p->head_dim;
   const int cus = cu_count();
+  const int dq_per_cu = bwd_dq_blocks_per_cu(p->head_dim);
 
   BwdArgs ba{};
   ba.q = (const __bf16*)q;
@@ -357,7 +358,7 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
     dq_sa.cu_k = cu_seqlens_k;
     dq_sa.batch = p->batch;
     dq_sa.stat_tile = bwd_dq_rows();
-    dq_sa.loop_tile = bwd_dq_tile();
+    dq_sa.loop_tile = bwd_dq_tile(p->head_dim);
     dq_sa.mode = 0;
     dq_sa.causal = p->causal;
     dq_sa.bcast_nq = 0;
@@ -369,7 +370,7 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
     dkdv_sa.cu_k = cu_seqlens_k;
     dkdv_sa.batch = p->batch;
     dkdv_sa.stat_tile = bwd_dkdv_tile();
-    dkdv_sa.loop_tile = bwd_dkdv_rows();
+    dkdv_sa.loop_tile = bwd_dkdv_rows(p->head_dim);
     dkdv_sa.mode = 1;
     dkdv_sa.causal = p->causal;
     dkdv_sa.bcast_nq = p->broadcast_q ? p->total_q : 0;
@@ -407,7 +408,7 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
       ba.bcast_chunk = cdiv_i(p->batch, L.chunks);
       ba.bcast_units = (int)(tiles_heads * ba.bcast_chunks);
       TimedRegion tr(JFA_TIMING_BWD_DQ, stream);
-      e = launch_bwd_dq(ba, p->head_dim, std::max(1, std::min(ba.bcast_units, 2 * cus)), stream);
+      e = launch_bwd_dq(ba, p->head_dim, std::max(1, std::min(ba.bcast_units, dq_per_cu * cus)), stream);
       tr.finish();
       if (e != hipSuccess) return JFA_ERR_HIP;
     } else {
@@ -415,7 +416,7 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
       ba.queues = dq_sa.queues;
       const int64_t max_items = L.dq_list.max_items;
       TimedRegion tr(JFA_TIMING_BWD_DQ, stream);
-      e = launch_bwd_dq(ba, p->head_dim, (int)std::max<int64_t>(1, std::min<int64_t>(2LL * cus, max_items)), stream);
+      e = launch_bwd_dq(ba, p->head_dim, (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)dq_per_cu * cus, max_items)), stream);
       tr.finish();
       if (e != hipSuccess) return JFA_ERR_HIP;
     }

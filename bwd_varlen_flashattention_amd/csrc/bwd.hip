@@ -48,19 +48,22 @@ namespace jfa {
 constexpr int kPreThreads = 256;
 
 __global__ __launch_bounds__(kPreThreads) void bwd_pre_kernel(BwdPreArgs a) {
-  // 16 lanes per (row, head) pair; each lane reads 8 bf16 of O and dO.
+  // 16 lanes per (row, head) pair; lane l reads the 8-column chunks l, l + 16, ...
+  // of O and dO (one chunk up to d = 128, two for d = 256).
   const int64_t gtid = (int64_t)blockIdx.x * kPreThreads + threadIdx.x;
   const int lane16 = threadIdx.x & 15;
   const int64_t pair = gtid >> 4;
   const int64_t n_pairs = a.rows * a.hq;
   const int chunks = a.head_dim / 8;
   float acc = 0.f;
-  if (pair < n_pairs && lane16 < chunks) {
-    const int64_t base = pair * a.head_dim + lane16 * 8;
-    const bf16x8 o = *(const bf16x8*)(a.o + base);
-    const bf16x8 d = *(const bf16x8*)(a.dout + base);
+  if (pair < n_pairs) {
+    for (int c = lane16; c < chunks; c += 16) {
+      const int64_t base = pair * a.head_dim + c * 8;
+      const bf16x8 o = *(const bf16x8*)(a.o + base);
+      const bf16x8 d = *(const bf16x8*)(a.dout + base);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc = fmaf((float)o[i], (float)d[i], acc);
+      for (int i = 0; i < 8; ++i) acc = fmaf((float)o[i], (float)d[i], acc);
+    }
   }
 #pragma unroll
   for (int m = 8; m >= 1; m >>= 1) acc += __shfl_xor(acc, m, 16);
@@ -135,27 +138,39 @@ __device__ __forceinline__ void store_transposed_4x8(__bf16* dst, int pitch, con
 }
 
 // ============================================================================= dK / dV
+// Head-dim chunking ("Cutting edge isn't plug-and-play: customising
+// FlashAttention-4 on B300", Phase 2): for d = 256 one work item owns the dK/dV
+// columns of one DC-wide slice of the head dimension.  S = Q K^T and dP = dO V^T
+// are still summed over the whole head dimension (every item reads all of Q, K,
+// V and dO), and P, dS are rebuilt from them and the saved LSE; only the dK/dV
+// accumulators and the transposed Q/dO tiles are per slice.  d <= 192 keeps the
+// whole head in one item.  Above d = 128 a step takes 32 query rows, so that the
+// double-buffered full-width Q/dO tiles fit in LDS.
 template <int D>
 struct DkvTile {
   static constexpr int NT = 256;             // 4 waves, 32 keys each
   static constexpr int BN = 128;             // keys per item
-  static constexpr int BM = 64;              // query rows per step
+  static constexpr int BM = D <= 128 ? 64 : 32;   // query rows per step
+  static constexpr int DC = D <= 192 ? D : 128;   // head-dim slice owned by one item
+  static constexpr int NC = D / DC;               // slices per key tile
   static constexpr int QP = D + 8;           // row pitch of Q / dO tiles (elements)
   static constexpr int QTP = BM + 8;         // row pitch of Q^T / dO^T tiles
   static constexpr int QBLOCKS = (BM / 4) * (D / 8);   // 4-row x 8-column staging blocks
   static constexpr int KS = D / 16;
-  static constexpr int DB = D / 32;
+  static constexpr int DB = DC / 32;         // 32-wide blocks of the owned slice
   static_assert(QBLOCKS <= NT, "one Q block per thread");
+  static_assert(D % DC == 0 && DC % 32 == 0, "slice width");
+  static_assert(2 * (2 * BM * QP + 2 * DC * QTP) * 2 + 4 * BM * 4 <= 160 * 1024, "LDS budget");
 };
 
 template <int D, bool CAUSAL, bool BCAST>
 __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   using T = DkvTile<D>;
-  constexpr int BN = T::BN, BM = T::BM, QP = T::QP, QTP = T::QTP, KS = T::KS, DB = T::DB;
+  constexpr int BN = T::BN, BM = T::BM, QP = T::QP, QTP = T::QTP, KS = T::KS, DB = T::DB, DC = T::DC;
   __shared__ __attribute__((aligned(16))) __bf16 q_lds[2][BM * QP];
   __shared__ __attribute__((aligned(16))) __bf16 do_lds[2][BM * QP];
-  __shared__ __attribute__((aligned(16))) __bf16 qt_lds[2][D * QTP];
-  __shared__ __attribute__((aligned(16))) __bf16 dot_lds[2][D * QTP];
+  __shared__ __attribute__((aligned(16))) __bf16 qt_lds[2][DC * QTP];
+  __shared__ __attribute__((aligned(16))) __bf16 dot_lds[2][DC * QTP];
   __shared__ __attribute__((aligned(16))) float lse_lds[2][BM];
   __shared__ __attribute__((aligned(16))) float dlt_lds[2][BM];
   __shared__ int s_item;
@@ -183,7 +198,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     const int item = s_item;
     if (item < 0) break;
     const WorkItem e = a.items[item];
-    const int g = e.h;
+    const int g = e.h / T::NC;
+    const int c0 = (e.h % T::NC) * DC;         // first head-dim column of the owned slice
     const int b = e.b;
     int lq, q_base;
     if (BCAST) { lq = a.bcast_nq; q_base = 0; }
@@ -240,8 +256,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       const int rows = min(lq - row0, BM);
       if (tid < BM) {
         const int64_t li0 = BCAST ? ((int64_t)b * a.hq + h) * lq + row0 : (int64_t)h * a.total_q + q_base + row0;
-        const auto lrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.lse + li0), (short)0, (uint32_t)(rows * 4), kBufferFlags);
-        const auto drsrc = __builtin_amdgcn_make_buffer_rsrc((void*)(a.delta + li0), (short)0, (uint32_t)(rows * 4), kBufferFlags);
+        const auto lrsrc = uniform_rsrc(a.lse + li0, (uint32_t)(rows * 4));
+        const auto drsrc = uniform_rsrc(a.delta + li0, (uint32_t)(rows * 4));
         lse_raw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(lrsrc, tid * 4, 0, 0));
         dlt_raw = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(drsrc, tid * 4, 0, 0));
       }
@@ -249,8 +265,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       const __bf16* qb = a.q + ((int64_t)(q_base + row0) * a.hq + h) * D;
       const int64_t orow0 = BCAST ? (int64_t)b * lq + row0 : (int64_t)(q_base + row0);
       const __bf16* ob = a.dout + (orow0 * a.hq + h) * D;
-      const auto qrsrc = __builtin_amdgcn_make_buffer_rsrc((void*)qb, (short)0, nbytes, kBufferFlags);
-      const auto orsrc = __builtin_amdgcn_make_buffer_rsrc((void*)ob, (short)0, nbytes, kBufferFlags);
+      const auto qrsrc = uniform_rsrc(qb, nbytes);
+      const auto orsrc = uniform_rsrc(ob, nbytes);
       if (stager) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -266,9 +282,13 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
           *(u32x4*)&q_lds[buf][(4 * sq + i) * QP + 8 * sd] = qr[i];
           *(u32x4*)&do_lds[buf][(4 * sq + i) * QP + 8 * sd] = dr[i];
         }
+        // the transposed tiles hold the owned slice only (whole 8-column blocks)
         const int col = 16 * (sq >> 2) + 4 * quarter_pos(sq & 3);
-        store_transposed_4x8(&qt_lds[buf][(8 * sd) * QTP + col], QTP, qr);
-        store_transposed_4x8(&dot_lds[buf][(8 * sd) * QTP + col], QTP, dr);
+        const int trow = 8 * sd - c0;
+        if (trow >= 0 && trow < DC) {
+          store_transposed_4x8(&qt_lds[buf][trow * QTP + col], QTP, qr);
+          store_transposed_4x8(&dot_lds[buf][trow * QTP + col], QTP, dr);
+        }
       }
       if (tid < BM) {
         lse_lds[buf][tid] = (lse_raw == -INF) ? INF : lse_raw * kLog2e;   // rows that saw no key get P = 0
@@ -281,7 +301,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       const int qt = i_first + unit_of(s) % n_qt;
       if (s + 1 < n_steps) load_regs(s + 1);
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
+      for (int qb = 0; qb < BM / 32; ++qb) {
         // S[q][key], dP[q][key]: A = Q / dO rows, B = K / V fragments
         f32x16 sacc = f32x16{}, pacc = f32x16{};
         const __bf16* qp = &q_lds[buf][(32 * qb + l32) * QP + 8 * hh];
@@ -333,9 +353,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       for (int s = 0; s < n_steps; ++s) step(s);
     }
 
-    // epilogue: dK = scale * dK^T, dV = dV^T, 4 consecutive d per 8-byte store
+    // epilogue: dK = scale * dK^T, dV = dV^T for the owned slice, 4 consecutive d per 8-byte store
     if (key_ok) {
-      const int64_t base = ((int64_t)(k_base + my_key) * a.hkv + g) * D;
+      const int64_t base = ((int64_t)(k_base + my_key) * a.hkv + g) * D + c0;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -360,7 +380,10 @@ template <int D>
 struct DqTile {
   static constexpr int NT = 256;             // 4 waves, 32 query rows each
   static constexpr int BM = 128;             // query rows per item
-  static constexpr int BN = 64;              // keys per tile
+  static constexpr int BN = D <= 128 ? 64 : 32;   // keys per tile
+  // d <= 128: two workgroups per CU; d = 192 / 256 keep Q, dO and dQ^T of the
+  // whole head in the registers of one wave per SIMD
+  static constexpr int WG_PER_CU = D <= 128 ? 2 : 1;
   static constexpr int KP = D + 8;           // row pitch of K / V tiles
   static constexpr int KTP = BN + 8;         // row pitch of the K^T tile
   static constexpr int CH = D / 8;
@@ -369,10 +392,11 @@ struct DqTile {
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static_assert(BN * CH % NT == 0 && KBLOCKS <= NT, "tile load split");
+  static_assert(WG_PER_CU * (2 * BN * KP + D * KTP) * 2 <= 160 * 1024, "LDS budget");
 };
 
 template <int D, bool CAUSAL, bool BCAST>
-__global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__(256, DqTile<D>::WG_PER_CU) void bwd_dq_kernel(BwdArgs a) {
   using T = DqTile<D>;
   constexpr int BM = T::BM, BN = T::BN, KP = T::KP, KTP = T::KTP, KS = T::KS, DB = T::DB;
   __shared__ __attribute__((aligned(16))) __bf16 k_lds[BN * KP];
@@ -502,8 +526,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
       auto load_regs = [&](int j) {
         const int64_t tile_off = (int64_t)j * BN * rs;
         const uint32_t nbytes = (uint32_t)(min(lk - j * BN, BN) * rs * 2);
-        const auto krs = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + tile_off), (short)0, nbytes, kBufferFlags);
-        const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + tile_off), (short)0, nbytes, kBufferFlags);
+        const auto krs = uniform_rsrc(kbase + tile_off, nbytes);
+        const auto vrs = uniform_rsrc(vbase + tile_off, nbytes);
         if (k_stager) {
 #pragma unroll
           for (int i = 0; i < 4; ++i)
@@ -545,7 +569,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
         if (s + 1 < n_tiles) load_regs(tile_of(s + 1));
         const int kmax_ok = CAUSAL ? min(lk - 1, my_row + off) : lk - 1;
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < BN / 32; ++kb) {
           // S^T[key][q] = K Q^T and dP^T[key][q] = V dO^T for 32 keys
           f32x16 st = f32x16{}, pt = f32x16{};
           const __bf16* kp = &k_lds[(32 * kb + l32) * KP + 8 * hh];
@@ -612,9 +636,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(BwdArgs a) {
 }
 
 int bwd_dkdv_tile() { return DkvTile<128>::BN; }
-int bwd_dkdv_rows() { return DkvTile<128>::BM; }
+int bwd_dkdv_rows(int head_dim) { return head_dim <= 128 ? DkvTile<128>::BM : DkvTile<256>::BM; }
+int bwd_dkdv_slices(int head_dim) {
+  return head_dim <= 128 ? DkvTile<128>::NC : head_dim <= 192 ? DkvTile<192>::NC : DkvTile<256>::NC;
+}
 int bwd_dq_rows() { return DqTile<128>::BM; }
-int bwd_dq_tile() { return DqTile<128>::BN; }
+int bwd_dq_tile(int head_dim) { return head_dim <= 128 ? DqTile<128>::BN : DqTile<256>::BN; }
+int bwd_dq_blocks_per_cu(int head_dim) { return head_dim <= 128 ? DqTile<128>::WG_PER_CU : DqTile<256>::WG_PER_CU; }
 
 template <int D>
 static hipError_t launch_dkdv_d(const BwdArgs& a, int grid, hipStream_t stream) {
@@ -639,6 +667,8 @@ hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int grid, hipStream_t
     case 64: return launch_dkdv_d<64>(a, grid, stream);
     case 96: return launch_dkdv_d<96>(a, grid, stream);
     case 128: return launch_dkdv_d<128>(a, grid, stream);
+    case 192: return launch_dkdv_d<192>(a, grid, stream);
+    case 256: return launch_dkdv_d<256>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -648,6 +678,8 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int grid, hipStream_t s
     case 64: return launch_dq_d<64>(a, grid, stream);
     case 96: return launch_dq_d<96>(a, grid, stream);
     case 128: return launch_dq_d<128>(a, grid, stream);
+    case 192: return launch_dq_d<192>(a, grid, stream);
+    case 256: return launch_dq_d<256>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -37,6 +37,15 @@ struct DecTile {
   static_assert(BN * CH % NT == 0, "tile load split");
 };
 
+// Resident workgroups per CU: d <= 128 runs four one-group workgroups (two with
+// two column groups); d = 192 / 256 run one column group at two per CU, where the
+// K/V tile's LDS and the accumulator's registers allow no more.
+template <int D, int NCG>
+struct DecOcc {
+  static constexpr int WG_PER_CU = D <= 128 ? (NCG == 1 ? 4 : 2) : 2;
+  static_assert(D <= 128 || NCG == 1, "one column group above d = 128");
+};
+
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -54,12 +63,13 @@ __device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
 // per-tensor scales are applied to the scores (K, folded into scale_log2 by the
 // host) and to the output (V).
 template <int D, int NCG, bool FP8>
-__global__ __launch_bounds__(256, NCG == 1 ? 4 : 2) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, (DecOcc<D, NCG>::WG_PER_CU)) void decode_kernel(DecodeArgs a) {
   using T = DecTile<D>;
   constexpr int BN = T::BN, KP = T::KP, VP = T::VP, KK = T::KK, DB = T::DB;
   constexpr int KV_BYTES = BN * (KP + VP) * 2;
   constexpr int MERGE_BYTES = 4 * 16 * D * 4 + 2 * 4 * 16 * 4;
   constexpr int SMEM = KV_BYTES > MERGE_BYTES ? KV_BYTES : MERGE_BYTES;
+  static_assert(DecOcc<D, NCG>::WG_PER_CU * SMEM <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
   __bf16* k_lds = (__bf16*)smem;
   __bf16* v_lds = k_lds + BN * KP;
@@ -310,16 +320,23 @@ int decode_chunk_align() { return DecTile<128>::BN; }
 
 // Two 16-column groups at most: four would spill at d = 128 with two waves per
 // SIMD; wider query tiles use more column units (the KV chunk is then read once
-// per unit).
-int decode_col_groups(int columns) { return columns <= 16 ? 1 : 2; }
-int decode_blocks_per_cu(int columns) { return decode_col_groups(columns) == 1 ? 4 : 2; }
+// per unit).  Above d = 128 a workgroup holds one column group.
+int decode_col_groups(int columns, int head_dim) { return (columns <= 16 || head_dim > 128) ? 1 : 2; }
+int decode_blocks_per_cu(int columns, int head_dim) {
+  if (head_dim > 128) return DecOcc<256, 1>::WG_PER_CU;
+  return decode_col_groups(columns, head_dim) == 1 ? DecOcc<128, 1>::WG_PER_CU : DecOcc<128, 2>::WG_PER_CU;
+}
 
 template <int D, bool FP8>
 static void launch_decode_d(const DecodeArgs& a, int ncg, unsigned grid, hipStream_t stream) {
-  if (ncg == 1)
+  if constexpr (D > 128) {
     hipLaunchKernelGGL((decode_kernel<D, 1, FP8>), dim3(grid), dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((decode_kernel<D, 2, FP8>), dim3(grid), dim3(256), 0, stream, a);
+  } else {
+    if (ncg == 1)
+      hipLaunchKernelGGL((decode_kernel<D, 1, FP8>), dim3(grid), dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((decode_kernel<D, 2, FP8>), dim3(grid), dim3(256), 0, stream, a);
+  }
 }
 template <int D>
 static void launch_decode_d(const DecodeArgs& a, int ncg, unsigned grid, hipStream_t stream) {
@@ -329,7 +346,7 @@ static void launch_decode_d(const DecodeArgs& a, int ncg, unsigned grid, hipStre
 
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t stream) {
   const int cols = a.group * a.q_len;
-  const int ncg = decode_col_groups(cols);
+  const int ncg = decode_col_groups(cols, head_dim);
   const int n_cu = ((cols + 15) / 16 + ncg - 1) / ncg;
   const int64_t grid = (int64_t)a.batch * a.hkv * a.splits * n_cu;
   if (grid <= 0 || grid > (1ll << 31) - 1) return hipErrorInvalidValue;
@@ -337,6 +354,8 @@ hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t stream) 
     case 64: launch_decode_d<64>(a, ncg, (unsigned)grid, stream); break;
     case 96: launch_decode_d<96>(a, ncg, (unsigned)grid, stream); break;
     case 128: launch_decode_d<128>(a, ncg, (unsigned)grid, stream); break;
+    case 192: launch_decode_d<192>(a, ncg, (unsigned)grid, stream); break;
+    case 256: launch_decode_d<256>(a, ncg, (unsigned)grid, stream); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -348,6 +367,8 @@ hipError_t launch_decode_combine(const DecodeArgs& a, int head_dim, hipStream_t 
     case 64: hipLaunchKernelGGL(decode_combine_kernel<64>, dim3((unsigned)grid), dim3(64), 0, stream, a); break;
     case 96: hipLaunchKernelGGL(decode_combine_kernel<96>, dim3((unsigned)grid), dim3(96), 0, stream, a); break;
     case 128: hipLaunchKernelGGL(decode_combine_kernel<128>, dim3((unsigned)grid), dim3(128), 0, stream, a); break;
+    case 192: hipLaunchKernelGGL(decode_combine_kernel<192>, dim3((unsigned)grid), dim3(192), 0, stream, a); break;
+    case 256: hipLaunchKernelGGL(decode_combine_kernel<256>, dim3((unsigned)grid), dim3(256), 0, stream, a); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -34,6 +34,19 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // num_records return zero.
 constexpr int kBufferFlags = 0x00020000;
 
+// Raw buffer resource for a wave-uniform base and byte range.  The base and range
+// are moved to scalar registers explicitly: when a 64-bit address product ends up
+// in vector registers, the compiler otherwise wraps every load through the
+// resource in a readfirstlane loop.  Callers pass values that are the same in
+// every lane of the wave.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, uint32_t nbytes) {
+  const uint64_t a = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(nbytes);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0, n, kBufferFlags);
+}
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

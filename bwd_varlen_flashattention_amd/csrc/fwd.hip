@@ -13,8 +13,9 @@
 //     back to back on one XCD and so share its L2;
 //   * 4 waves, each owning 32 query rows whose Q fragment stays in VGPRs for the
 //     whole key loop;
-//   * two workgroups per CU (two waves per SIMD), so one wave's softmax VALU
-//     work overlaps the other's MFMAs;
+//   * two workgroups per CU (two waves per SIMD) for d <= 128, so one wave's
+//     softmax VALU work overlaps the other's MFMAs; d = 192 and 256 run one
+//     workgroup per CU, whose Q fragment and accumulator fill a SIMD's registers;
 //   * K/V tiles of 64 keys are double-buffered in LDS: the global loads of tile
 //     j+1 are in flight while tile j is consumed;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 so each lane owns one query column:
@@ -41,16 +42,21 @@ template <int D>
 struct FwdTile {
   static constexpr int NT = 256;            // 4 waves
   static constexpr int BM = 128;            // query rows per item (32 per wave)
-  static constexpr int BN = 64;             // keys per KV tile
+  static constexpr int BN = D <= 192 ? 64 : 32;   // keys per KV tile (d = 256: 32, so nothing spills)
+  static constexpr int KB = BN / 32;        // 32-key blocks per tile
   static constexpr int KP = D + 8;          // K row pitch in LDS (elements): +16 B staggers banks
-  static constexpr int VTP = BN + 8;        // V^T row pitch (elements): 144 B rows
+  static constexpr int VTP = BN + 8;        // V^T row pitch (elements): 144 B rows at 64 keys
   static constexpr int CH = D / 8;          // 16-byte chunks per row
   static constexpr int KLOADS = BN * CH / NT;
   static constexpr int VBLOCKS = (BN / 4) * (D / 8);   // 4-key x 8-column blocks of V
+  static constexpr int VPER = (VBLOCKS + NT - 1) / NT;  // V blocks per thread (2 for d > 128)
   static constexpr int KS = D / 16;         // k-steps of K Q^T
   static constexpr int DB = D / 32;         // 32-wide output column blocks
+  // d <= 128: two workgroups per CU; larger heads need the whole register file of
+  // one wave per SIMD (Q fragment + output accumulator) and most of the LDS
+  static constexpr int WG_PER_CU = D <= 128 ? 2 : 1;
   static_assert(BN * CH % NT == 0, "tile load split");
-  static_assert(VBLOCKS <= NT, "one V block per thread");
+  static_assert(WG_PER_CU * 2 * (BN * KP + D * VTP) * 2 <= 160 * 1024, "LDS budget");
 };
 
 // Position of a 4-key quarter inside its stored 16-key group: the S^T accumulator
@@ -61,9 +67,9 @@ __device__ __forceinline__ int vt_quarter_pos(int q) { return ((q & 1) << 1) | (
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 
 template <int D, bool CAUSAL, bool BCAST>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(256, FwdTile<D>::WG_PER_CU) void fwd_kernel(FwdArgs a) {
   using T = FwdTile<D>;
-  constexpr int BM = T::BM, BN = T::BN, KP = T::KP, VTP = T::VTP, KS = T::KS, DB = T::DB;
+  constexpr int BM = T::BM, BN = T::BN, KB = T::KB, KP = T::KP, VTP = T::VTP, KS = T::KS, DB = T::DB;
   __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][BN * KP];
   __shared__ __attribute__((aligned(16))) __bf16 vt_lds[2][D * VTP];
   __shared__ int s_item;
@@ -76,16 +82,24 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
   // byte offsets of this thread's staging loads inside a KV tile (row stride rs elements)
   const int rs = a.hkv * D;
-  const bool v_stager = tid < T::VBLOCKS;
-  const int vkb = tid % (BN / 4), vdb = tid / (BN / 4);
-  uint32_t koff[T::KLOADS], voff[4];
+  constexpr int VPER = T::VPER;
+  bool v_stager[VPER];
+  int vkb[VPER], vdb[VPER];
+  uint32_t koff[T::KLOADS], voff[VPER][4];
 #pragma unroll
   for (int i = 0; i < T::KLOADS; ++i) {
     const int id = tid + i * T::NT;
     koff[i] = (uint32_t)(((id / T::CH) * rs + (id % T::CH) * 8) * 2);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) voff[i] = (uint32_t)(((4 * vkb + i) * rs + vdb * 8) * 2);
+  for (int vi = 0; vi < VPER; ++vi) {
+    const int id = tid + vi * T::NT;
+    v_stager[vi] = id < T::VBLOCKS;
+    vkb[vi] = id % (BN / 4);
+    vdb[vi] = id / (BN / 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) voff[vi][i] = (uint32_t)(((4 * vkb[vi] + i) * rs + vdb[vi] * 8) * 2);
+  }
 
   int home_q = blockIdx.x % kQueues, drained = 0;   // work-queue state (thread 0)
   load_queues(a.queues, s_queue);
@@ -141,20 +155,22 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
     // past the sequence end fall outside the range and read as zero.
     const __bf16* kbase = a.k + ((int64_t)k_base * a.hkv + g) * D;
     const __bf16* vbase = a.v + ((int64_t)k_base * a.hkv + g) * D;
-    u32x4 kr[T::KLOADS], vr[4];
+    u32x4 kr[T::KLOADS], vr[VPER][4];
     auto load_regs = [&](int j) {
       const int64_t tile_off = (int64_t)j * BN * rs;
       const uint32_t nbytes = (uint32_t)(min(lk - j * BN, BN) * rs * 2);
-      const auto krs = __builtin_amdgcn_make_buffer_rsrc((void*)(kbase + tile_off), (short)0, nbytes, kBufferFlags);
-      const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(vbase + tile_off), (short)0, nbytes, kBufferFlags);
+      const auto krs = uniform_rsrc(kbase + tile_off, nbytes);
+      const auto vrs = uniform_rsrc(vbase + tile_off, nbytes);
 #pragma unroll
       for (int i = 0; i < T::KLOADS; ++i)
         kr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, koff[i], 0, 0));
-      if (v_stager) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-          vr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff[i], 0, 0));
-      }
+      for (int vi = 0; vi < VPER; ++vi)
+        if (v_stager[vi]) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            vr[vi][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff[vi][i], 0, 0));
+        }
     };
     auto store_lds = [&](int buf) {
 #pragma unroll
@@ -163,16 +179,19 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
         const int r = id / T::CH, c = id % T::CH;
         *(u32x4*)&k_lds[buf][r * KP + c * 8] = kr[i];
       }
-      if (v_stager) {
+#pragma unroll
+      for (int vi = 0; vi < VPER; ++vi) {
+        if (!v_stager[vi]) continue;
         // 4 keys x 8 columns -> 8 rows of V^T holding 4 keys each
-        const int col = 16 * (vkb >> 2) + 4 * vt_quarter_pos(vkb & 3);
-        __bf16* dst = &vt_lds[buf][(8 * vdb) * VTP + col];
+        const int col = 16 * (vkb[vi] >> 2) + 4 * vt_quarter_pos(vkb[vi] & 3);
+        __bf16* dst = &vt_lds[buf][(8 * vdb[vi]) * VTP + col];
+        const u32x4 (&r)[4] = vr[vi];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const uint32_t lo01 = __builtin_amdgcn_perm(vr[1][c], vr[0][c], 0x05040100u);
-          const uint32_t lo23 = __builtin_amdgcn_perm(vr[3][c], vr[2][c], 0x05040100u);
-          const uint32_t hi01 = __builtin_amdgcn_perm(vr[1][c], vr[0][c], 0x07060302u);
-          const uint32_t hi23 = __builtin_amdgcn_perm(vr[3][c], vr[2][c], 0x07060302u);
+          const uint32_t lo01 = __builtin_amdgcn_perm(r[1][c], r[0][c], 0x05040100u);
+          const uint32_t lo23 = __builtin_amdgcn_perm(r[3][c], r[2][c], 0x05040100u);
+          const uint32_t hi01 = __builtin_amdgcn_perm(r[1][c], r[0][c], 0x07060302u);
+          const uint32_t hi23 = __builtin_amdgcn_perm(r[3][c], r[2][c], 0x07060302u);
           *(uint2*)(dst + (2 * c) * VTP) = make_uint2(lo01, lo23);
           *(uint2*)(dst + (2 * c + 1) * VTP) = make_uint2(hi01, hi23);
         }
@@ -199,10 +218,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       const int j = tile_of(step);
       if (step + 1 < n_tiles) load_regs(tile_of(step + 1));
 
-      // S^T[key][query] for two 32-key blocks
-      f32x16 s[2];
+      // S^T[key][query] for the tile's 32-key blocks
+      f32x16 s[KB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         s[kb] = f32x16{};
         const __bf16* kp = &k_lds[buf][(32 * kb + l32) * KP + 8 * hh];
 #pragma unroll
@@ -213,7 +232,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       if constexpr (MASK) {
         const int kmax_ok = CAUSAL ? min(lk - 1, my_row + off) : lk - 1;   // last visible key
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const int key = j * BN + 32 * kb + 8 * (r >> 2) + 4 * hh + (r & 3);
@@ -223,7 +242,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 
       float mx = NEG_INF;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
       mx = xhalf_max(mx);
@@ -240,9 +259,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       const float m_sub = (m_run == NEG_INF) ? 0.f : m_run;
 
       float psum = 0.f;
-      bf16x8 pb[2][2];
+      bf16x8 pb[KB][2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < KB; ++kb) {
         float pv[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -259,7 +278,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
       for (int db = 0; db < DB; ++db) {
         const __bf16* vp = &vt_lds[buf][(32 * db + l32) * VTP + 8 * hh];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int t = 0; t < 2; ++t)
             acc[db] = mfma32x32x16(*(const bf16x8*)(vp + 16 * (2 * kb + t)), pb[kb][t], acc[db]);
@@ -307,8 +326,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdArgs a) {
 }
 
 int fwd_block_rows() { return FwdTile<128>::BM; }
-int fwd_kv_tile() { return FwdTile<128>::BN; }
-int fwd_blocks_per_cu(int) { return 2; }
+int fwd_kv_tile(int head_dim) { return head_dim <= 128 ? FwdTile<128>::BN : head_dim <= 192 ? FwdTile<192>::BN : FwdTile<256>::BN; }
+int fwd_blocks_per_cu(int head_dim) {
+  return head_dim <= 128 ? FwdTile<128>::WG_PER_CU : head_dim <= 192 ? FwdTile<192>::WG_PER_CU : FwdTile<256>::WG_PER_CU;
+}
 
 template <int D>
 static hipError_t launch_fwd_d(const FwdArgs& a, int grid, hipStream_t stream) {
@@ -327,6 +348,8 @@ hipError_t launch_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t stre
     case 64: return launch_fwd_d<64>(a, grid, stream);
     case 96: return launch_fwd_d<96>(a, grid, stream);
     case 128: return launch_fwd_d<128>(a, grid, stream);
+    case 192: return launch_fwd_d<192>(a, grid, stream);
+    case 256: return launch_fwd_d<256>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

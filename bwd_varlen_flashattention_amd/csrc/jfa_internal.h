@@ -81,7 +81,7 @@ struct FwdArgs {
 
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t stream);
 int fwd_block_rows();       // BM of the forward kernel
-int fwd_kv_tile();          // BN of the forward kernel
+int fwd_kv_tile(int head_dim);   // BN of the forward kernel
 int fwd_blocks_per_cu(int head_dim);
 
 // Backward.
@@ -126,10 +126,12 @@ struct BwdArgs {
 };
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int grid, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int grid, hipStream_t stream);
-int bwd_dkdv_tile();        // keys per dK/dV item
-int bwd_dkdv_rows();        // query rows per dK/dV step
-int bwd_dq_rows();          // query rows per dQ item
-int bwd_dq_tile();          // keys per dQ tile
+int bwd_dkdv_tile();                       // keys per dK/dV item
+int bwd_dkdv_rows(int head_dim);           // query rows per dK/dV step
+int bwd_dkdv_slices(int head_dim);         // head-dim slices (dK/dV items) per key tile
+int bwd_dq_rows();                         // query rows per dQ item
+int bwd_dq_tile(int head_dim);             // keys per dQ tile
+int bwd_dq_blocks_per_cu(int head_dim);    // resident dQ workgroups per CU
 
 struct DqConvertArgs {
   const float* dq_part;     // [chunks, n] fp32 partials
@@ -164,7 +166,7 @@ struct DecodeArgs {
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeArgs& a, int head_dim, hipStream_t stream);
 int decode_chunk_align();
-int decode_col_groups(int columns);      // 16-column query groups per decode workgroup
-int decode_blocks_per_cu(int columns);   // decode workgroups resident per CU
+int decode_col_groups(int columns, int head_dim);      // 16-column query groups per decode workgroup
+int decode_blocks_per_cu(int columns, int head_dim);   // decode workgroups resident per CU
 
 }  // namespace jfa

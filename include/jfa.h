@@ -60,7 +60,7 @@ typedef struct ihipStream_t* jfa_stream_t;
 typedef enum {
   JFA_OK = 0,
   JFA_ERR_INVALID_ARGUMENT = 1,   /* null pointer, negative size, Hq % Hkv != 0, ... */
-  JFA_ERR_UNSUPPORTED = 2,        /* head_dim outside {64, 96, 128}, causal broadcast-Q, ... */
+  JFA_ERR_UNSUPPORTED = 2,        /* head_dim outside {64, 96, 128, 192, 256}, causal broadcast-Q, ... */
   JFA_ERR_WORKSPACE_TOO_SMALL = 3,
   JFA_ERR_HIP = 4                 /* a HIP call or kernel launch failed */
 } jfa_status_t;
@@ -87,7 +87,7 @@ typedef struct {
   int32_t batch;          /* B >= 1 */
   int32_t num_heads_q;    /* Hq >= 1 */
   int32_t num_heads_kv;   /* Hkv >= 1, Hq % Hkv == 0 */
-  int32_t head_dim;       /* d in {64, 96, 128}; anything else is JFA_ERR_UNSUPPORTED */
+  int32_t head_dim;       /* d in {64, 96, 128, 192, 256}; anything else is JFA_ERR_UNSUPPORTED */
   int32_t total_q;        /* packed query rows (broadcast-Q: Nq) */
   int32_t total_k;        /* packed key rows */
   int32_t max_seqlen_q;   /* upper bound on any Lq (broadcast-Q: ignored, Nq is used) */
@@ -128,7 +128,10 @@ size_t jfa_bwd_workspace_size(const jfa_attn_params_t* p);
  * are deterministic (no atomics): in broadcast-Q mode dQ, the sum over all
  * items, is accumulated per chunk of items in fp32 and the chunk partials are
  * added in a fixed order.  Keys that no query sees get dK = dV = 0; queries
- * that see no key get dQ = 0.
+ * that see no key get dQ = 0.  For d = 256 the dK/dV work is split along the
+ * head dimension ("Cutting edge isn't plug-and-play", Phase 2 chunked
+ * backward): each slice of 128 columns is a work item of its own that rebuilds
+ * S and dP from the whole head; the results are the same.
  */
 jfa_status_t jfa_bwd(const jfa_attn_params_t* p,
                      const void* q, const void* k, const void* v,
@@ -173,7 +176,7 @@ typedef struct {
   int32_t batch;              /* B >= 1 */
   int32_t num_heads_q;        /* Hq >= 1 */
   int32_t num_heads_kv;       /* Hkv >= 1, Hq % Hkv == 0, (Hq / Hkv) * q_len <= 256 */
-  int32_t head_dim;           /* d in {64, 96, 128} */
+  int32_t head_dim;           /* d in {64, 96, 128, 192, 256} */
   int32_t page_size;          /* >= 1, any value */
   int32_t num_pages;          /* pages in the cache, >= 1 */
   int32_t max_pages_per_seq;  /* columns of page_table, >= 1 */

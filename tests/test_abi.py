@@ -47,7 +47,7 @@ def _params(L, **kw):
 
 
 BAD = [
-    (dict(head_dim=80), 2), (dict(head_dim=256), 2), (dict(num_heads_q=3), 1), (dict(batch=0), 1),
+    (dict(head_dim=80), 2), (dict(head_dim=320), 2), (dict(head_dim=160), 2), (dict(num_heads_q=3), 1), (dict(batch=0), 1),
     (dict(total_q=-1), 1), (dict(causal=2), 1), (dict(broadcast_q=1, causal=1), 2),
     (dict(softmax_scale=float("nan")), 1),
 ]
@@ -140,3 +140,22 @@ def test_status_strings():
     L, lib = _lib()
     assert L.status_string(0) == "JFA_OK"
     assert L.status_string(2) == "JFA_ERR_UNSUPPORTED"
+
+
+@pytest.mark.parametrize("d", [192, 256])
+def test_large_head_dims_are_accepted(d):
+    """d = 192 and 256 are supported: workspace queries succeed, and at d = 256 the
+    dK/dV work list holds one item per 128-column head-dim slice (more workspace)."""
+    L, lib = _lib()
+    p = _params(L, head_dim=d, total_q=5000, total_k=5000, max_seqlen_q=2500, max_seqlen_k=2500)
+    assert lib.jfa_fwd_workspace_size(ctypes.byref(p)) > 0
+    wd = lib.jfa_bwd_workspace_size(ctypes.byref(p))
+    p128 = _params(L, total_q=5000, total_k=5000, max_seqlen_q=2500, max_seqlen_k=2500)
+    w128 = lib.jfa_bwd_workspace_size(ctypes.byref(p128))
+    assert wd >= w128
+    if d == 256:
+        items = (5000 // 128 + 1 + 2) * 2 * 16      # (key tiles + batch) x Hkv x 16-byte items
+        assert wd - w128 >= items - 256             # one more item per slice, up to a 256-byte pad
+    pd = L.DecodeParams(batch=2, num_heads_q=8, num_heads_kv=2, head_dim=d, page_size=16, num_pages=10,
+                        max_pages_per_seq=5, num_splits=2, softmax_scale=0.0, q_len=1, causal=0)
+    assert lib.jfa_decode_workspace_size(ctypes.byref(pd)) >= 2 * 2 * 8 * (d + 1) * 4

@@ -86,7 +86,7 @@ def test_tiny(jfa, seed):
 RAGGED = [1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 200, 0, 257, 5]
 
 
-@pytest.mark.parametrize("d", [64, 96, 128])
+@pytest.mark.parametrize("d", [64, 96, 128, 192, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("hq,hkv", [(2, 2), (4, 2), (3, 1)])
 def test_ragged(jfa, d, causal, hq, hkv):
@@ -239,5 +239,32 @@ def test_broadcast_repeatability(jfa):
     first = _run_bcast(jfa, inp)
     for _ in range(5):
         got = _run_bcast(jfa, inp)
+        for x, y in zip(got, first):
+            np.testing.assert_array_equal(x, y)
+
+@pytest.mark.parametrize("d", [192, 256])
+def test_broadcast_q_large_head_dims(jfa, d):
+    """Broadcast-Q at d = 192 / 256 (d = 256: dK/dV split into two head-dim slices)."""
+    inp = workloads.broadcast(6, 130, [70, 0, 200, 129, 1], 4, 2, d)
+    _say(f"broadcast d={d}")
+    _compare_full(_run_bcast(jfa, inp), _oracle_bcast(inp))
+
+
+@pytest.mark.parametrize("d", [192, 256])
+def test_large_head_dim_long_causal_sampled(jfa, d):
+    """Long causal sequences (2048 and 2500 + ragged) at d = 192 / 256, 4 heads over 2 KV
+    heads; oracle on the two long sequences, every head."""
+    inp = workloads.jagged(70 + d, [2048, 1, 2500, 77], None, 4, 2, d, True)
+    _say(f"long causal d={d}")
+    got = _run_self(jfa, inp)
+    _compare_sampled(inp, got, _oracle_self(inp, seqs=[0, 2]))
+
+
+def test_large_head_dim_repeatability(jfa):
+    """d = 256: the sliced dK/dV and every other output are bitwise identical across runs."""
+    inp = workloads.jagged(13, [300, 129, 64], None, 4, 2, 256, True)
+    first = _run_self(jfa, inp)
+    for _ in range(4):
+        got = _run_self(jfa, inp)
         for x, y in zip(got, first):
             np.testing.assert_array_equal(x, y)

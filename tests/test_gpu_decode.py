@@ -60,7 +60,7 @@ def test_decode_small(jfa, page_size, hq, hkv):
         check_lse(lse, rl, f"LSE splits={splits}")
 
 
-@pytest.mark.parametrize("dim", [64, 96])
+@pytest.mark.parametrize("dim", [64, 96, 192, 256])
 def test_decode_head_dims(jfa, dim):
     inp = workloads.decode(31, [5, 200, 129], 8, 2, dim, 16)
     d = _Dev(inp)
@@ -142,7 +142,7 @@ def test_decode_multi_token(jfa, q_len, hq, hkv, causal):
 
 
 @pytest.mark.parametrize("page_size", [1, 128])
-@pytest.mark.parametrize("dim", [64, 96])
+@pytest.mark.parametrize("dim", [64, 96, 256])
 def test_decode_multi_token_pages_dims(jfa, page_size, dim):
     inp = workloads.decode(55, [3, 200, 129, 64], 8, 2, dim, page_size, q_len=5)
     d = _Dev(inp)
@@ -185,7 +185,7 @@ class _DevFp8(_Dev):
 
 @pytest.mark.parametrize("q_len,causal", [(1, False), (4, True), (9, False)])
 @pytest.mark.parametrize("page_size", [1, 16, 128])
-@pytest.mark.parametrize("dim", [64, 96, 128])
+@pytest.mark.parametrize("dim", [64, 96, 128, 192, 256])
 def test_decode_fp8_kv(jfa, q_len, causal, page_size, dim):
     """FP8 caches: the result equals attention on the dequantised K/V (scales 0.5 and
     2.0 exercise both scale paths); unused slots hold NaN bytes."""
