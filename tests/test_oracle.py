@@ -226,6 +226,57 @@ def test_finite_differences_broadcast_q():
     _fd_check(f, {"q": q, "k": k, "v": v}, {"q": dq, "k": dk, "v": dv})
 
 
+# ----------------------------------------------------------------- head-dim-sliced backward
+def _sliced_backward(q, k, v, o, lse, do, causal, hc, bq=16, bk=8):
+    """The chunked backward of "Cutting edge isn't plug-and-play: customising FlashAttention-4
+    on B300" (Phase 2 pseudocode and buffer list), for one sequence and head: per
+    (Q tile, KV tile) and output slice c of width hc, S and dP are summed over every
+    slice of the head dimension, P is rebuilt from the saved LSE, and only dQ[:, c],
+    dK[:, c], dV[:, c] are written."""
+    lq, d = q.shape
+    lk = k.shape[0]
+    scale = 1.0 / math.sqrt(d)
+    delta = (do * o).sum(1)
+    dq, dk, dv = np.zeros_like(q), np.zeros_like(k), np.zeros_like(v)
+    for c0 in range(0, d, hc):
+        c = slice(c0, c0 + hc)
+        for i0 in range(0, lq, bq):
+            i = slice(i0, min(i0 + bq, lq))
+            for j0 in range(0, lk, bk):
+                j = slice(j0, min(j0 + bk, lk))
+                s_t = np.zeros((i.stop - i.start, j.stop - j.start))
+                dp_t = np.zeros_like(s_t)
+                for h0 in range(0, d, hc):
+                    h = slice(h0, h0 + hc)
+                    s_t += q[i, h] @ k[j, h].T
+                    dp_t += do[i, h] @ v[j, h].T
+                p_t = np.exp(s_t * scale - lse[i, None])
+                if causal:
+                    rows = np.arange(i.start, i.stop)[:, None] + (lk - lq)
+                    p_t = np.where(np.arange(j.start, j.stop)[None, :] <= rows, p_t, 0.0)
+                ds_t = p_t * (dp_t - delta[i, None])
+                dq[i, c] += scale * ds_t @ k[j, c]
+                dk[j, c] += scale * ds_t.T @ q[i, c]
+                dv[j, c] += p_t.T @ do[i, c]
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("hc", [128, 64])
+@pytest.mark.parametrize("causal", [False, True])
+def test_head_dim_sliced_backward_equals_oracle(hc, causal):
+    """At d = 256 the slice-by-slice backward (S and dP summed over all slices, each
+    slice writing its own dQ/dK/dV columns) equals the oracle's unsliced gradients."""
+    rng = np.random.default_rng(40)
+    lq, lk, d = 37, 29, 256
+    q, k, v, do = (rng.standard_normal((n, 1, d)) for n in (lq, lk, lk, lq))
+    cq, ck = np.array([0, lq]), np.array([0, lk])
+    o, lse = oracle.attention_forward(q, k, v, cq, ck, causal)
+    dq, dk, dv = oracle.attention_backward(q, k, v, do, cq, ck, causal)
+    got = _sliced_backward(q[:, 0], k[:, 0], v[:, 0], o[:, 0], lse[0], do[:, 0], causal, hc)
+    for g, r in zip(got, (dq[:, 0], dk[:, 0], dv[:, 0])):
+        np.testing.assert_allclose(g, r, rtol=1e-10, atol=1e-12)
+
+
 # ----------------------------------------------------------------- invariants and symmetries
 @pytest.mark.parametrize("causal", [False, True])
 def test_softmax_jacobian_invariants(causal):
