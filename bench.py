@@ -413,6 +413,26 @@ def sweep(torch, jfa, workloads, args, log):
         print(json.dumps(line), flush=True)
         del jc
         torch.cuda.empty_cache()
+    # e4m3 forward (Q K^T on the fp8 matrix cores) against the bf16 forward of the same workload
+    for name, make in (("gem_s0.5", lambda: workloads.gem(0, 0.5)),
+                       ("dense_causal_d128", lambda: workloads.dense_causal(0, head_dim=128))):
+        base = make()
+        inp, enc = workloads.fp8_qkv(base)
+        del base
+        jc = JaggedCase(torch, jfa, inp)
+        q8, k8, v8 = (torch.from_numpy(enc[n]).to("cuda").view(torch.float8_e4m3fn) for n in ("q", "k", "v"))
+        sc = dict(q_scale=enc["q_scale"], k_scale=enc["k_scale"], v_scale=enc["v_scale"])
+        del inp, enc
+        # the forward's workspace (its work list) does not depend on the element type
+        f8_ms = timeit(lambda: jfa.jfa_fwd(q8, k8, v8, jc.cq, jc.ck, jc.mq, jc.mk, jc.causal, out=jc.o, lse=jc.lse,
+                                           workspace=jc.ws_f, **sc))
+        bf_ms = timeit(lambda: jfa.jfa_fwd(jc.q, jc.k, jc.v, jc.cq, jc.ck, jc.mq, jc.mk, jc.causal,
+                                           out=jc.o, lse=jc.lse, workspace=jc.ws_f))
+        print(json.dumps({"workload": name + "_fp8_fwd", "fwd_ms": round(f8_ms, 4), "bf16_fwd_ms": round(bf_ms, 4),
+                          "fwd_tflops": round(jc.fwd_flops / f8_ms / 1e9, 1), "speedup": round(bf_ms / f8_ms, 3)}),
+              flush=True)
+        del jc, q8, k8, v8
+        torch.cuda.empty_cache()
     for ps in (16, 1, 128):
         inp = workloads.decode_paged(0, ps, tail_fill=0.0)
         for splits in (1, 2, 4, 8, 16, 0):

@@ -46,29 +46,48 @@ def _check_i32(name, t):
         raise ValueError(f"{name}: expected a contiguous int32 CUDA tensor")
 
 
-def _attn_params(q, k, cu_q, cu_k, max_q, max_k, causal, scale, broadcast_q, batch):
+def _attn_params(q, k, cu_q, cu_k, max_q, max_k, causal, scale, broadcast_q, batch, fp8=False,
+                 q_scale=None, k_scale=None, v_scale=None):
     nb = batch if batch is not None else (cu_k.numel() - 1)
+    sc = lambda x: float(x) if x is not None else 1.0
     return AttnParams(
         batch=nb, num_heads_q=q.shape[1], num_heads_kv=k.shape[1], head_dim=q.shape[2],
         total_q=q.shape[0], total_k=k.shape[0], max_seqlen_q=int(max_q), max_seqlen_k=int(max_k),
         causal=int(bool(causal)), broadcast_q=int(bool(broadcast_q)),
-        softmax_scale=float(scale) if scale is not None else 0.0)
+        softmax_scale=float(scale) if scale is not None else 0.0,
+        qkv_dtype=1 if fp8 else 0, q_scale=sc(q_scale), k_scale=sc(k_scale), v_scale=sc(v_scale))
+
+
+def _is_fp8(t) -> bool:
+    torch = _torch()
+    return t.dtype in (getattr(torch, "float8_e4m3fn", None), torch.uint8)
+
+
+def _check_fp8(name, t, ndim):
+    if not _is_fp8(t) or t.dim() != ndim or not t.is_cuda or not t.is_contiguous():
+        raise ValueError(f"{name}: expected a contiguous float8_e4m3fn (or uint8 e4m3 bytes) CUDA tensor "
+                         f"with {ndim} dims, got {t.dtype} {tuple(t.shape)}")
 
 
 def jfa_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
             causal: bool = False, softmax_scale: Optional[float] = None, broadcast_q: bool = False,
-            out=None, lse=None, workspace=None):
+            out=None, lse=None, workspace=None, q_scale: Optional[float] = None,
+            k_scale: Optional[float] = None, v_scale: Optional[float] = None):
     """Jagged forward.  Self-attention: q [Tq,Hq,d], k/v [Tk,Hkv,d] -> o [Tq,Hq,d], lse [Hq,Tq].
-    Broadcast-Q: q [Nq,Hq,d] shared by B items -> o [B,Nq,Hq,d], lse [B,Hq,Nq]."""
+    Broadcast-Q: q [Nq,Hq,d] shared by B items -> o [B,Nq,Hq,d], lse [B,Hq,Nq].
+    q, k, v are all bfloat16, or all e4m3 (float8_e4m3fn or raw uint8 bytes) with
+    per-tensor scales q_scale, k_scale, v_scale (default 1); o is bfloat16 either way."""
     torch = _torch()
     lib = load()
-    _check_bf16("q", q, 3); _check_bf16("k", k, 3); _check_bf16("v", v, 3)
+    fp8 = _is_fp8(q)
+    chk = _check_fp8 if fp8 else _check_bf16
+    chk("q", q, 3); chk("k", k, 3); chk("v", v, 3)
     _check_i32("cu_seqlens_k", cu_seqlens_k)
     if not broadcast_q:
         _check_i32("cu_seqlens_q", cu_seqlens_q)
     nb = cu_seqlens_k.numel() - 1
     p = _attn_params(q, k, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k, causal, softmax_scale,
-                     broadcast_q, nb)
+                     broadcast_q, nb, fp8, q_scale, k_scale, v_scale)
     if broadcast_q:
         o_shape, lse_shape = (nb, q.shape[0], q.shape[1], q.shape[2]), (nb, q.shape[1], q.shape[0])
     else:

@@ -39,6 +39,10 @@ class AttnParams(ctypes.Structure):
         ("causal", ctypes.c_int32),
         ("broadcast_q", ctypes.c_int32),
         ("softmax_scale", ctypes.c_float),
+        ("qkv_dtype", ctypes.c_int32),
+        ("q_scale", ctypes.c_float),
+        ("k_scale", ctypes.c_float),
+        ("v_scale", ctypes.c_float),
     ]
 
 

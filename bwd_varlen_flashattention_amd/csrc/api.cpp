@@ -74,6 +74,8 @@ struct TimedRegion {
 };
 
 // ------------------------------------------------------------------ validation
+bool positive_finite(float x) { return x > 0.f && !isinf(x); }   // false for NaN as well
+
 jfa_status_t check_attn(const jfa_attn_params_t* p) {
   if (!p) return JFA_ERR_INVALID_ARGUMENT;
   if (p->batch < 1 || p->num_heads_q < 1 || p->num_heads_kv < 1) return JFA_ERR_INVALID_ARGUMENT;
@@ -81,7 +83,12 @@ jfa_status_t check_attn(const jfa_attn_params_t* p) {
   if (p->total_q < 0 || p->total_k < 0 || p->max_seqlen_q < 0 || p->max_seqlen_k < 0) return JFA_ERR_INVALID_ARGUMENT;
   if ((p->causal != 0 && p->causal != 1) || (p->broadcast_q != 0 && p->broadcast_q != 1)) return JFA_ERR_INVALID_ARGUMENT;
   if (!(p->softmax_scale == p->softmax_scale) || isinf(p->softmax_scale)) return JFA_ERR_INVALID_ARGUMENT;
+  if (p->qkv_dtype != JFA_DTYPE_BF16 && p->qkv_dtype != JFA_DTYPE_FP8_E4M3) return JFA_ERR_INVALID_ARGUMENT;
+  if (p->qkv_dtype == JFA_DTYPE_FP8_E4M3 && !(positive_finite(p->q_scale) && positive_finite(p->k_scale) &&
+                                              positive_finite(p->v_scale)))
+    return JFA_ERR_INVALID_ARGUMENT;
   if (!supported_dim(p->head_dim)) return JFA_ERR_UNSUPPORTED;
+  if (p->qkv_dtype == JFA_DTYPE_FP8_E4M3 && p->head_dim % 64 != 0) return JFA_ERR_UNSUPPORTED;
   if (p->broadcast_q && p->causal) return JFA_ERR_UNSUPPORTED;
   // 32-bit element offsets of packed rows stay within int64 math; row counts must fit int32 tiles
   if ((int64_t)p->total_q * p->num_heads_q * p->head_dim > (int64_t)1 << 40) return JFA_ERR_INVALID_ARGUMENT;
@@ -288,7 +295,10 @@ jfa_status_t jfa_fwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   fa.bcast_nq = sa.bcast_nq;
   fa.total_q = p->total_q;
   fa.causal = p->causal;
-  fa.scale_log2 = eff_scale(p->softmax_scale, p->head_dim) * 1.4426950408889634f;
+  const bool fp8 = p->qkv_dtype == JFA_DTYPE_FP8_E4M3;
+  fa.scale_log2 = eff_scale(p->softmax_scale, p->head_dim) * 1.4426950408889634f * (fp8 ? p->q_scale * p->k_scale : 1.f);
+  fa.fp8 = fp8;
+  fa.v_scale = fp8 ? p->v_scale : 1.f;
   const int64_t max_items = L.max_items;
   const int grid = (int)std::min<int64_t>((int64_t)cu_count() * fwd_blocks_per_cu(p->head_dim), max_items);
   TimedRegion tr(JFA_TIMING_FWD, stream);
@@ -297,8 +307,15 @@ jfa_status_t jfa_fwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   return hip_status(e);
 }
 
+// The backward is a bf16 computation (e4m3 is an inference input format).
+jfa_status_t check_bwd(const jfa_attn_params_t* p) {
+  const jfa_status_t st = check_attn(p);
+  if (st != JFA_OK) return st;
+  return p->qkv_dtype == JFA_DTYPE_BF16 ? JFA_OK : JFA_ERR_UNSUPPORTED;
+}
+
 size_t jfa_bwd_workspace_size(const jfa_attn_params_t* p) {
-  if (check_attn(p) != JFA_OK) return 0;
+  if (check_bwd(p) != JFA_OK) return 0;
   return bwd_layout(p).end;
 }
 
@@ -306,7 +323,7 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
                      const void* o, const float* lse, const void* dout,
                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                      void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes, jfa_stream_t stream_) {
-  jfa_status_t st = check_attn(p);
+  jfa_status_t st = check_bwd(p);
   if (st != JFA_OK) return st;
   if (p->total_q == 0 && p->total_k == 0) return JFA_OK;
   if (!cu_seqlens_k || (!p->broadcast_q && !cu_seqlens_q)) return JFA_ERR_INVALID_ARGUMENT;

@@ -38,26 +38,59 @@
 
 namespace jfa {
 
-template <int D>
+// FP8: Q, K and V are OCP e4m3 bytes.  K stays e4m3 in LDS and S^T = K Q^T runs
+// on v_mfma_f32_32x32x64_f8f6f4 (64-deep k-steps, twice the bf16 rate); V is
+// widened to bf16 (exactly: every e4m3 value is a bf16 value) while it is staged
+// transposed, so P V is the bf16 contraction of the bf16 path.
+template <int D, bool FP8 = false>
 struct FwdTile {
   static constexpr int NT = 256;            // 4 waves
   static constexpr int BM = 128;            // query rows per item (32 per wave)
   static constexpr int BN = D <= 192 ? 64 : 32;   // keys per KV tile (d = 256: 32, so nothing spills)
   static constexpr int KB = BN / 32;        // 32-key blocks per tile
-  static constexpr int KP = D + 8;          // K row pitch in LDS (elements): +16 B staggers banks
+  static constexpr int EB = FP8 ? 1 : 2;    // bytes per Q/K/V element in memory
+  static constexpr int KP = FP8 ? D + 16 : D + 8;   // K row pitch in LDS (elements): +16 B staggers banks
   static constexpr int VTP = BN + 8;        // V^T row pitch (elements): 144 B rows at 64 keys
-  static constexpr int CH = D / 8;          // 16-byte chunks per row
+  static constexpr int CH = D * EB / 16;    // 16-byte chunks per K row
   static constexpr int KLOADS = BN * CH / NT;
   static constexpr int VBLOCKS = (BN / 4) * (D / 8);   // 4-key x 8-column blocks of V
   static constexpr int VPER = (VBLOCKS + NT - 1) / NT;  // V blocks per thread (2 for d > 128)
-  static constexpr int KS = D / 16;         // k-steps of K Q^T
+  static constexpr int KS = D / 16;         // k-steps of K Q^T (bf16)
+  static constexpr int KS8 = D / 64;        // k-steps of K Q^T (e4m3)
   static constexpr int DB = D / 32;         // 32-wide output column blocks
+  static constexpr int K_LDS_BYTES = BN * KP * EB;
   // d <= 128: two workgroups per CU; larger heads need the whole register file of
   // one wave per SIMD (Q fragment + output accumulator) and most of the LDS
   static constexpr int WG_PER_CU = D <= 128 ? 2 : 1;
   static_assert(BN * CH % NT == 0, "tile load split");
-  static_assert(WG_PER_CU * 2 * (BN * KP + D * VTP) * 2 <= 160 * 1024, "LDS budget");
+  static_assert(!FP8 || D % 64 == 0, "e4m3 k-steps are 64 deep");
+  static_assert(WG_PER_CU * 2 * (K_LDS_BYTES + D * VTP * 2) <= 160 * 1024, "LDS budget");
 };
+
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// e4m3 x e4m3 -> fp32, 32x32x64; zero scale operands select the unscaled form.
+// A and B hold their 64 k-values per row in the same lane/slot order, so any
+// consistent placement of the head dimension gives the dot products.
+__device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// 8 e4m3 bytes -> 8 bf16 (exact), packed two per dword in column order.
+__device__ __forceinline__ u32x4 widen_e4m3x8(uint2 x) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  u32x4 r;
+  const f2_t p[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(x.x, false), __builtin_amdgcn_cvt_pk_f32_fp8(x.x, true),
+                     __builtin_amdgcn_cvt_pk_f32_fp8(x.y, false), __builtin_amdgcn_cvt_pk_f32_fp8(x.y, true)};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    bf16x2 q;
+    q[0] = (__bf16)p[i][0];
+    q[1] = (__bf16)p[i][1];
+    r[i] = __builtin_bit_cast(uint32_t, q);
+  }
+  return r;
+}
 
 // Position of a 4-key quarter inside its stored 16-key group: the S^T accumulator
 // gives lane half h the keys {4h..4h+3, 8+4h..8+4h+3} of each group as one
@@ -66,11 +99,12 @@ __device__ __forceinline__ int vt_quarter_pos(int q) { return ((q & 1) << 1) | (
 
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 
-template <int D, bool CAUSAL, bool BCAST>
+template <int D, bool CAUSAL, bool BCAST, bool FP8>
 __global__ __launch_bounds__(256, FwdTile<D>::WG_PER_CU) void fwd_kernel(FwdArgs a) {
-  using T = FwdTile<D>;
+  using T = FwdTile<D, FP8>;
   constexpr int BM = T::BM, BN = T::BN, KB = T::KB, KP = T::KP, VTP = T::VTP, KS = T::KS, DB = T::DB;
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[2][BN * KP];
+  constexpr int EB = T::EB;
+  __shared__ __attribute__((aligned(16))) unsigned char k_raw[2][T::K_LDS_BYTES];
   __shared__ __attribute__((aligned(16))) __bf16 vt_lds[2][D * VTP];
   __shared__ int s_item;
   __shared__ int s_queue[2 * kQueues];
@@ -82,6 +116,9 @@ __global__ __launch_bounds__(256, FwdTile<D>::WG_PER_CU) void fwd_kernel(FwdArgs
 
   // byte offsets of this thread's staging loads inside a KV tile (row stride rs elements)
   const int rs = a.hkv * D;
+  const unsigned char* const qb8 = (const unsigned char*)a.q;
+  const unsigned char* const kb8 = (const unsigned char*)a.k;
+  const unsigned char* const vb8 = (const unsigned char*)a.v;
   constexpr int VPER = T::VPER;
   bool v_stager[VPER];
   int vkb[VPER], vdb[VPER];
@@ -89,7 +126,7 @@ __global__ __launch_bounds__(256, FwdTile<D>::WG_PER_CU) void fwd_kernel(FwdArgs
 #pragma unroll
   for (int i = 0; i < T::KLOADS; ++i) {
     const int id = tid + i * T::NT;
-    koff[i] = (uint32_t)(((id / T::CH) * rs + (id % T::CH) * 8) * 2);
+    koff[i] = (uint32_t)((id / T::CH) * rs * EB + (id % T::CH) * 16);
   }
 #pragma unroll
   for (int vi = 0; vi < VPER; ++vi) {
@@ -98,7 +135,7 @@ __global__ __launch_bounds__(256, FwdTile<D>::WG_PER_CU) void fwd_kernel(FwdArgs
     vkb[vi] = id % (BN / 4);
     vdb[vi] = id / (BN / 4);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) voff[vi][i] = (uint32_t)(((4 * vkb[vi] + i) * rs + vdb[vi] * 8) * 2);
+    for (int i = 0; i < 4; ++i) voff[vi][i] = (uint32_t)(((4 * vkb[vi] + i) * rs + vdb[vi] * 8) * EB);
   }
 
   int home_q = blockIdx.x % kQueues, drained = 0;   // work-queue state (thread 0)
@@ -124,13 +161,18 @@ __global__ __launch_bounds__(256, FwdTile<D>::WG_PER_CU) void fwd_kernel(FwdArgs
     const bool row_ok = my_row < lq;
     const int off = lk - lq;                 // bottom-right causal alignment
 
-    // Q fragment: B operand of S^T = K Q^T, lane holds row my_row, d-slots 16*ks + 8*hh + 0..7
-    bf16x8 qf[KS];
+    // Q fragment: B operand of S^T = K Q^T, lane holds row my_row, d-slots
+    // 16*ks + 8*hh + 0..7 (bf16) or 64*ks + 32*hh + 0..31 (e4m3)
+    using QFrag = std::conditional_t<FP8, i32x8, bf16x8>;
+    constexpr int QSTEPS = FP8 ? T::KS8 : KS;
+    QFrag qf[QSTEPS];
     {
-      const __bf16* qp = a.q + ((int64_t)(q_base + my_row) * a.hq + h) * D + 8 * hh;
+      const int64_t qrow = ((int64_t)(q_base + my_row) * a.hq + h) * D;
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks)
-        qf[ks] = row_ok ? *(const bf16x8*)(qp + 16 * ks) : zero_bf16x8();
+      for (int ks = 0; ks < QSTEPS; ++ks) {
+        if constexpr (FP8) qf[ks] = row_ok ? *(const i32x8*)(qb8 + qrow + 64 * ks + 32 * hh) : i32x8{};
+        else qf[ks] = row_ok ? *(const bf16x8*)(a.q + qrow + 16 * ks + 8 * hh) : zero_bf16x8();
+      }
     }
 
     int n_tiles, n_bulk;
@@ -153,12 +195,14 @@ __global__ __launch_bounds__(256, FwdTile<D>::WG_PER_CU) void fwd_kernel(FwdArgs
     // Raw buffer loads: the per-thread byte offsets are fixed (koff/voff), the
     // tile base and its valid byte range live in the 4-SGPR resource, and rows
     // past the sequence end fall outside the range and read as zero.
-    const __bf16* kbase = a.k + ((int64_t)k_base * a.hkv + g) * D;
-    const __bf16* vbase = a.v + ((int64_t)k_base * a.hkv + g) * D;
-    u32x4 kr[T::KLOADS], vr[VPER][4];
+    const unsigned char* kbase = kb8 + ((int64_t)k_base * a.hkv + g) * D * EB;
+    const unsigned char* vbase = vb8 + ((int64_t)k_base * a.hkv + g) * D * EB;
+    using VReg = std::conditional_t<FP8, uint2, u32x4>;   // one 8-column row piece of V
+    u32x4 kr[T::KLOADS];
+    VReg vr[VPER][4];
     auto load_regs = [&](int j) {
-      const int64_t tile_off = (int64_t)j * BN * rs;
-      const uint32_t nbytes = (uint32_t)(min(lk - j * BN, BN) * rs * 2);
+      const int64_t tile_off = (int64_t)j * BN * rs * EB;
+      const uint32_t nbytes = (uint32_t)(min(lk - j * BN, BN) * rs * EB);
       const auto krs = uniform_rsrc(kbase + tile_off, nbytes);
       const auto vrs = uniform_rsrc(vbase + tile_off, nbytes);
 #pragma unroll
@@ -168,8 +212,10 @@ __global__ __launch_bounds__(256, FwdTile<D>::WG_PER_CU) void fwd_kernel(FwdArgs
       for (int vi = 0; vi < VPER; ++vi)
         if (v_stager[vi]) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i)
-            vr[vi][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff[vi][i], 0, 0));
+          for (int i = 0; i < 4; ++i) {
+            if constexpr (FP8) vr[vi][i] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(vrs, voff[vi][i], 0, 0));
+            else vr[vi][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff[vi][i], 0, 0));
+          }
         }
     };
     auto store_lds = [&](int buf) {
@@ -177,7 +223,7 @@ __global__ __launch_bounds__(256, FwdTile<D>::WG_PER_CU) void fwd_kernel(FwdArgs
       for (int i = 0; i < T::KLOADS; ++i) {
         const int id = tid + i * T::NT;
         const int r = id / T::CH, c = id % T::CH;
-        *(u32x4*)&k_lds[buf][r * KP + c * 8] = kr[i];
+        *(u32x4*)&k_raw[buf][r * KP * EB + c * 16] = kr[i];
       }
 #pragma unroll
       for (int vi = 0; vi < VPER; ++vi) {
@@ -185,7 +231,12 @@ __global__ __launch_bounds__(256, FwdTile<D>::WG_PER_CU) void fwd_kernel(FwdArgs
         // 4 keys x 8 columns -> 8 rows of V^T holding 4 keys each
         const int col = 16 * (vkb[vi] >> 2) + 4 * vt_quarter_pos(vkb[vi] & 3);
         __bf16* dst = &vt_lds[buf][(8 * vdb[vi]) * VTP + col];
-        const u32x4 (&r)[4] = vr[vi];
+        u32x4 r[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if constexpr (FP8) r[i] = widen_e4m3x8(vr[vi][i]);
+          else r[i] = vr[vi][i];
+        }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const uint32_t lo01 = __builtin_amdgcn_perm(r[1][c], r[0][c], 0x05040100u);
@@ -223,10 +274,17 @@ __global__ __launch_bounds__(256, FwdTile<D>::WG_PER_CU) void fwd_kernel(FwdArgs
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         s[kb] = f32x16{};
-        const __bf16* kp = &k_lds[buf][(32 * kb + l32) * KP + 8 * hh];
+        if constexpr (FP8) {
+          const unsigned char* kp = &k_raw[buf][(32 * kb + l32) * KP + 32 * hh];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-          s[kb] = mfma32x32x16(*(const bf16x8*)(kp + 16 * ks), qf[ks], s[kb]);
+          for (int ks = 0; ks < QSTEPS; ++ks)
+            s[kb] = mfma32x32x64_fp8(*(const i32x8*)(kp + 64 * ks), qf[ks], s[kb]);
+        } else {
+          const __bf16* kp = (const __bf16*)k_raw[buf] + (32 * kb + l32) * KP + 8 * hh;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks)
+            s[kb] = mfma32x32x16(*(const bf16x8*)(kp + 16 * ks), qf[ks], s[kb]);
+        }
       }
 
       if constexpr (MASK) {
@@ -300,7 +358,7 @@ __global__ __launch_bounds__(256, FwdTile<D>::WG_PER_CU) void fwd_kernel(FwdArgs
 
     // epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
     const float l_tot = xhalf_sum(l_run);
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const float inv = l_tot > 0.f ? (FP8 ? a.v_scale : 1.f) / l_tot : 0.f;
     if (row_ok) {
       __bf16* op = BCAST ? a.o + (((int64_t)b * lq + my_row) * a.hq + h) * D
                          : a.o + ((int64_t)(q_base + my_row) * a.hq + h) * D;
@@ -331,16 +389,26 @@ int fwd_blocks_per_cu(int head_dim) {
   return head_dim <= 128 ? FwdTile<128>::WG_PER_CU : head_dim <= 192 ? FwdTile<192>::WG_PER_CU : FwdTile<256>::WG_PER_CU;
 }
 
+template <int D, bool FP8>
+static hipError_t launch_fwd_dt(const FwdArgs& a, int grid, hipStream_t stream) {
+  const dim3 g(grid), blk(FwdTile<D, FP8>::NT);
+  if (a.bcast_nq > 0)
+    hipLaunchKernelGGL((fwd_kernel<D, false, true, FP8>), g, blk, 0, stream, a);
+  else if (a.causal)
+    hipLaunchKernelGGL((fwd_kernel<D, true, false, FP8>), g, blk, 0, stream, a);
+  else
+    hipLaunchKernelGGL((fwd_kernel<D, false, false, FP8>), g, blk, 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int D>
 static hipError_t launch_fwd_d(const FwdArgs& a, int grid, hipStream_t stream) {
-  const dim3 g(grid), blk(FwdTile<D>::NT);
-  if (a.bcast_nq > 0)
-    hipLaunchKernelGGL((fwd_kernel<D, false, true>), g, blk, 0, stream, a);
-  else if (a.causal)
-    hipLaunchKernelGGL((fwd_kernel<D, true, false>), g, blk, 0, stream, a);
-  else
-    hipLaunchKernelGGL((fwd_kernel<D, false, false>), g, blk, 0, stream, a);
-  return hipGetLastError();
+  if constexpr (D % 64 == 0) {
+    if (a.fp8) return launch_fwd_dt<D, true>(a, grid, stream);
+  } else {
+    if (a.fp8) return hipErrorInvalidValue;   // e4m3 needs 64-deep k-steps
+  }
+  return launch_fwd_dt<D, false>(a, grid, stream);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t stream) {

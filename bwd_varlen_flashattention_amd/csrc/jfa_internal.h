@@ -76,7 +76,9 @@ struct FwdArgs {
   int32_t bcast_nq;         // > 0: broadcast-Q
   int32_t total_q;          // LSE row stride for self-attention
   int32_t causal;
-  float scale_log2;         // softmax scale * log2(e)
+  float scale_log2;         // softmax scale * log2(e) (e4m3: times the Q and K scales)
+  int32_t fp8;              // Q, K, V are e4m3 bytes
+  float v_scale;            // e4m3: V scale, applied to O
 };
 
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t stream);

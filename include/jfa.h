@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define JFA_ABI_VERSION 2
+#define JFA_ABI_VERSION 3
 
 /* Same type as hipStream_t, declared without including the HIP headers. */
 struct ihipStream_t;
@@ -64,6 +64,9 @@ typedef enum {
   JFA_ERR_WORKSPACE_TOO_SMALL = 3,
   JFA_ERR_HIP = 4                 /* a HIP call or kernel launch failed */
 } jfa_status_t;
+
+/* Element types of the q/k/v (and KV-cache) tensors. */
+enum { JFA_DTYPE_BF16 = 0, JFA_DTYPE_FP8_E4M3 = 1 };
 
 /*
  * Problem description for jfa_fwd / jfa_bwd.
@@ -95,6 +98,12 @@ typedef struct {
   int32_t causal;         /* 0 or 1 */
   int32_t broadcast_q;    /* 0 or 1 */
   float softmax_scale;    /* <= 0 selects 1/sqrt(d) */
+  int32_t qkv_dtype;      /* JFA_DTYPE_BF16 (0), or JFA_DTYPE_FP8_E4M3: q, k, v hold OCP e4m3
+                             bytes in the same layouts (jfa_fwd only, d a multiple of 64;
+                             jfa_bwd returns JFA_ERR_UNSUPPORTED) */
+  float q_scale;          /* e4m3 only: per-tensor scales, each tensor's value = scale x its */
+  float k_scale;          /* e4m3 value; finite and > 0.  Ignored for bf16 */
+  float v_scale;
 } jfa_attn_params_t;
 
 /* Bytes of workspace jfa_fwd needs for this problem (0 if the params are invalid). */
@@ -102,7 +111,11 @@ size_t jfa_fwd_workspace_size(const jfa_attn_params_t* p);
 
 /*
  * Forward: O = softmax(S) V per sequence and head, plus LSE, with no score
- * matrix or padding ever written to memory.  Work items (sequence, query tile,
+ * matrix or padding ever written to memory.  With e4m3 inputs ("Optimizing
+ * FlashAttention-4 for Efficient Inference", PR 2109: FP8 inputs) the result is
+ * that of attention on the scaled e4m3 values: Q K^T runs on the e4m3 matrix
+ * cores with fp32 accumulation, V is widened exactly to bf16 for P V; o stays
+ * bf16 and lse fp32.  Work items (sequence, query tile,
  * head) are listed on the device from the offsets.  The tiles of one (sequence,
  * KV head) form a group that shares its K/V; groups are sorted by cost (longest
  * first) and dealt to one queue per XCD, and persistent workgroups pull from
@@ -140,8 +153,8 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p,
                      void* dq, void* dk, void* dv,
                      void* workspace, size_t workspace_bytes, jfa_stream_t stream);
 
-/* KV-cache element types of jfa_decode_paged. */
-enum { JFA_KV_BF16 = 0, JFA_KV_FP8_E4M3 = 1 };
+/* KV-cache element types of jfa_decode_paged (the JFA_DTYPE_* values). */
+enum { JFA_KV_BF16 = JFA_DTYPE_BF16, JFA_KV_FP8_E4M3 = JFA_DTYPE_FP8_E4M3 };
 
 /*
  * Split-KV paged decode of q_len (1..16) new tokens per sequence: single-token

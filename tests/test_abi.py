@@ -29,7 +29,7 @@ def test_header_declares_and_library_exports():
     for n in names:
         assert hasattr(lib, n), f"missing export {n}"
     assert set(names) == set(L.EXPORTS)
-    assert lib.jfa_abi_version() == 2
+    assert lib.jfa_abi_version() == 3
 
 
 def test_header_compiles_as_c(tmp_path):
@@ -50,6 +50,10 @@ BAD = [
     (dict(head_dim=80), 2), (dict(head_dim=320), 2), (dict(head_dim=160), 2), (dict(num_heads_q=3), 1), (dict(batch=0), 1),
     (dict(total_q=-1), 1), (dict(causal=2), 1), (dict(broadcast_q=1, causal=1), 2),
     (dict(softmax_scale=float("nan")), 1),
+    (dict(qkv_dtype=2), 1), (dict(qkv_dtype=1, q_scale=0.0, k_scale=1.0, v_scale=1.0), 1),
+    (dict(qkv_dtype=1, q_scale=1.0, k_scale=float("inf"), v_scale=1.0), 1),
+    (dict(qkv_dtype=1, q_scale=1.0, k_scale=1.0, v_scale=float("nan")), 1),
+    (dict(qkv_dtype=1, q_scale=1.0, k_scale=1.0, v_scale=1.0, head_dim=96), 2),
 ]
 
 
@@ -159,3 +163,15 @@ def test_large_head_dims_are_accepted(d):
     pd = L.DecodeParams(batch=2, num_heads_q=8, num_heads_kv=2, head_dim=d, page_size=16, num_pages=10,
                         max_pages_per_seq=5, num_splits=2, softmax_scale=0.0, q_len=1, causal=0)
     assert lib.jfa_decode_workspace_size(ctypes.byref(pd)) >= 2 * 2 * 8 * (d + 1) * 4
+
+
+def test_fp8_forward_only():
+    """e4m3 Q/K/V is an inference input: the forward accepts it (d a multiple of 64),
+    the backward reports JFA_ERR_UNSUPPORTED and needs no workspace."""
+    L, lib = _lib()
+    p = _params(L, qkv_dtype=1, q_scale=0.5, k_scale=0.25, v_scale=2.0)
+    assert lib.jfa_fwd_workspace_size(ctypes.byref(p)) > 0
+    assert lib.jfa_bwd_workspace_size(ctypes.byref(p)) == 0
+    d = ctypes.c_void_p(256)
+    st = lib.jfa_bwd(ctypes.byref(p), d, d, d, d, d, d, d, d, d, d, d, d, 1 << 20, None)
+    assert st == L.JFA_ERR_UNSUPPORTED

@@ -103,3 +103,21 @@ def test_fp8_decode_inputs_are_exact_dequantisations():
     page = inp.page_table[1, 0]
     np.testing.assert_array_equal(kc[page, 3] * 0.5, inp.k[inp.cu_k[1] + 3])
     assert np.all(inp.k_cache[inp.page_table[0, 0], 5:] == 0x7F)     # unused slots hold the NaN byte
+
+
+def test_fp8_qkv_are_exact_dequantisations():
+    """fp8_qkv: bytes x scale reproduce the returned values exactly; the default
+    scale maps each tensor's amax to 448 (the largest finite e4m3 value)."""
+    torch = pytest.importorskip("torch")
+    inp = workloads.jagged(5, [7, 30], None, 4, 2, 64, True)
+    got, enc = workloads.fp8_qkv(inp)
+    for n in ("q", "k", "v"):
+        dec = torch.from_numpy(enc[n]).view(torch.float8_e4m3fn).float().numpy() * enc[n + "_scale"]
+        np.testing.assert_array_equal(dec, getattr(got, n))
+        assert enc[n + "_scale"] == pytest.approx(np.abs(getattr(inp, n)).max() / 448.0)
+        assert np.abs(getattr(got, n) - getattr(inp, n)).max() <= np.abs(getattr(inp, n)).max() / 16
+    np.testing.assert_array_equal(got.do, inp.do)
+    _, enc2 = workloads.fp8_qkv(inp, 0.5, 0.25, 2.0)
+    assert (enc2["q_scale"], enc2["k_scale"], enc2["v_scale"]) == (0.5, 0.25, 2.0)
+    with pytest.raises(ValueError):
+        workloads.fp8_qkv(inp, 1e-3, 1.0, 1.0)        # |q| / scale beyond 448

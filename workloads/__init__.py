@@ -318,6 +318,23 @@ def _e4m3(x, scale: float):
     return t.view(torch.uint8).numpy().copy(), (t.float() * scale).numpy()
 
 
+def fp8_qkv(inp, q_scale=None, k_scale=None, v_scale=None):
+    """e4m3 copies of q, k, v with per-tensor scales (default: amax / 448, the
+    largest finite e4m3 value).  Returns (same inputs with q, k, v replaced by the
+    exact dequantised values, {"q": bytes, "k": bytes, "v": bytes, "q_scale": ...})."""
+    from dataclasses import replace
+    out, enc = {}, {}
+    for name, x, sc in (("q", inp.q, q_scale), ("k", inp.k, k_scale), ("v", inp.v, v_scale)):
+        amax = float(np.abs(x).max(initial=0.0))
+        if sc is None:
+            sc = amax / 448.0 if amax > 0 else 1.0
+        if amax / sc > 448.0 * (1 + 1e-6):   # the default scale lands on 448 up to rounding
+            raise ValueError(f"{name}: |x| / scale reaches {amax / sc:.1f}, beyond e4m3's largest finite 448")
+        enc[name], out[name] = _e4m3(x, float(sc))
+        enc[name + "_scale"] = float(sc)
+    return replace(inp, q=out["q"], k=out["k"], v=out["v"]), enc
+
+
 def _page(k, v, seqlens, cu_k, page_size, max_pages_per_seq, perm, tail_fill, dtype=np.float32):
     """Scatter contiguous K/V rows into pages; physical ids come from `perm` in (sequence, page) order."""
     b = len(seqlens)
