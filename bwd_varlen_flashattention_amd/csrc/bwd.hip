@@ -192,20 +192,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   int home_q = blockIdx.x % kQueues, drained = 0;   // work-queue state (thread 0)
   load_queues(a.queues, s_queue);
   __syncthreads();
-  for (;;) {
-    if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
-    __syncthreads();
-    const int item = s_item;
-    if (item < 0) break;
+  if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
+  __syncthreads();
+  int item = __builtin_amdgcn_readfirstlane(s_item);   // uniform: the item loads are scalar
+  while (item >= 0) {
     const WorkItem e = a.items[item];
     const int g = e.h / T::NC;
     const int c0 = (e.h % T::NC) * DC;         // first head-dim column of the owned slice
     const int b = e.b;
-    int lq, q_base;
-    if (BCAST) { lq = a.bcast_nq; q_base = 0; }
-    else { q_base = a.cu_q[b]; lq = a.cu_q[b + 1] - q_base; }
-    const int k_base = a.cu_k[b];
-    const int lk = a.cu_k[b + 1] - k_base;
+    const int lq = e.lq, q_base = e.q_base;
+    const int k_base = e.k_base, lk = e.lk;
     const int off = lk - lq;
     const int kt0 = e.t * BN;
     const int my_key = kt0 + 32 * w + l32;
@@ -371,7 +367,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
           *(bf16x4*)(a.dv + base + d0) = vv4;
         }
     }
-    __syncthreads();   // s_item and the LDS buffers are reused by the next item
+    __syncthreads();   // the LDS buffers are reused by the next item
+    if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
+    __syncthreads();
+    item = __builtin_amdgcn_readfirstlane(s_item);
   }
 }
 
@@ -428,12 +427,17 @@ __global__ __launch_bounds__(256, DqTile<D>::WG_PER_CU) void bwd_dq_kernel(BwdAr
   // per-XCD work queues; broadcast-Q owns (query tile, head, chunk of items) by block index.
   int bcast_item = blockIdx.x;
   int home_q = blockIdx.x % kQueues, drained = 0;   // work-queue state (thread 0)
+  int item = -1;
   if (!BCAST) {   // broadcast-Q runs without a work list (a.queues is null)
     load_queues(a.queues, s_queue);
     __syncthreads();
+    if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
+    __syncthreads();
+    item = __builtin_amdgcn_readfirstlane(s_item);   // uniform: the item loads are scalar
   }
   for (;;) {
     int b_lo, b_hi, h, qtile, chunk = 0;
+    int e_qbase = 0, e_lq = 0, e_kbase = 0, e_lk = 0;   // self-attention: the item's sequence
     if (BCAST) {
       if (bcast_item >= a.bcast_units) break;
       const int per_tile = a.hq * a.bcast_chunks;
@@ -445,15 +449,16 @@ __global__ __launch_bounds__(256, DqTile<D>::WG_PER_CU) void bwd_dq_kernel(BwdAr
       b_hi = min(a.batch, b_lo + a.bcast_chunk);
       bcast_item += gridDim.x;
     } else {
-      if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
-      __syncthreads();
-      const int item = s_item;
       if (item < 0) break;
       const WorkItem e = a.items[item];
       h = e.h;
       b_lo = e.b;
       b_hi = e.b + 1;
       qtile = e.t;
+      e_qbase = e.q_base;
+      e_lq = e.lq;
+      e_kbase = e.k_base;
+      e_lk = e.lk;
     }
     const int g = h / a.group;
     const int row0 = qtile * BM;
@@ -464,11 +469,9 @@ __global__ __launch_bounds__(256, DqTile<D>::WG_PER_CU) void bwd_dq_kernel(BwdAr
     for (int db = 0; db < DB; ++db) dqt[db] = f32x16{};
 
     for (int b = b_lo; b < b_hi; ++b) {
-      int lq, q_base;
-      if (BCAST) { lq = a.bcast_nq; q_base = 0; }
-      else { q_base = a.cu_q[b]; lq = a.cu_q[b + 1] - q_base; }
-      const int k_base = a.cu_k[b];
-      const int lk = a.cu_k[b + 1] - k_base;
+      int lq, q_base, k_base, lk;
+      if (BCAST) { lq = a.bcast_nq; q_base = 0; k_base = a.cu_k[b]; lk = a.cu_k[b + 1] - k_base; }
+      else { lq = e_lq; q_base = e_qbase; k_base = e_kbase; lk = e_lk; }
       const bool row_ok = my_row < lq;
       const int off = lk - lq;
 
@@ -607,7 +610,7 @@ __global__ __launch_bounds__(256, DqTile<D>::WG_PER_CU) void bwd_dq_kernel(BwdAr
     }
 
     // epilogue: dQ = scale * dQ^T; 4 consecutive d per store
-    const int lq_e = BCAST ? a.bcast_nq : a.cu_q[b_lo + 1] - a.cu_q[b_lo];
+    const int lq_e = BCAST ? a.bcast_nq : e_lq;
     if (my_row < lq_e) {
       if (BCAST) {
         // this chunk's partial, 4 consecutive d per store (summed in order by dq_convert)
@@ -619,7 +622,7 @@ __global__ __launch_bounds__(256, DqTile<D>::WG_PER_CU) void bwd_dq_kernel(BwdAr
             *(f32x4*)(dst + 32 * db + 8 * r4 + 4 * hh) =
                 f32x4{dqt[db][4 * r4], dqt[db][4 * r4 + 1], dqt[db][4 * r4 + 2], dqt[db][4 * r4 + 3]};
       } else {
-        __bf16* dst = a.dq + ((int64_t)(a.cu_q[b_lo] + my_row) * a.hq + h) * D;
+        __bf16* dst = a.dq + ((int64_t)(e_qbase + my_row) * a.hq + h) * D;
 #pragma unroll
         for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -631,7 +634,12 @@ __global__ __launch_bounds__(256, DqTile<D>::WG_PER_CU) void bwd_dq_kernel(BwdAr
           }
       }
     }
-    if (!BCAST) __syncthreads();   // s_item is rewritten by the next pull
+    if (!BCAST) {
+      __syncthreads();   // every thread has read s_item before it is rewritten
+      if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
+      __syncthreads();
+      item = __builtin_amdgcn_readfirstlane(s_item);
+    }
   }
 }
 

@@ -141,21 +141,16 @@ __global__ __launch_bounds__(256, FwdTile<D>::WG_PER_CU) void fwd_kernel(FwdArgs
   int home_q = blockIdx.x % kQueues, drained = 0;   // work-queue state (thread 0)
   load_queues(a.queues, s_queue);
   __syncthreads();
-  for (;;) {
-    if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
-    __syncthreads();
-    const int item = s_item;
-    if (item < 0) break;
+  if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
+  __syncthreads();
+  int item = __builtin_amdgcn_readfirstlane(s_item);   // uniform: the item loads are scalar
+  while (item >= 0) {
     const WorkItem e = a.items[item];
     const int h = e.h;
     const int g = h / a.group;
     const int b = e.b;
-
-    int lq, q_base;
-    if (BCAST) { lq = a.bcast_nq; q_base = 0; }
-    else { q_base = a.cu_q[b]; lq = a.cu_q[b + 1] - q_base; }
-    const int k_base = a.cu_k[b];
-    const int lk = a.cu_k[b + 1] - k_base;
+    const int lq = e.lq, q_base = e.q_base;
+    const int k_base = e.k_base, lk = e.lk;
     const int row0 = e.t * BM;
     const int my_row = row0 + w * 32 + l32;
     const bool row_ok = my_row < lq;
@@ -379,7 +374,10 @@ __global__ __launch_bounds__(256, FwdTile<D>::WG_PER_CU) void fwd_kernel(FwdArgs
         a.lse[li] = lse;
       }
     }
-    __syncthreads();   // s_item and the LDS buffers are reused by the next item
+    __syncthreads();   // the LDS buffers are reused by the next item
+    if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
+    __syncthreads();
+    item = __builtin_amdgcn_readfirstlane(s_item);
   }
 }
 

@@ -14,11 +14,17 @@ constexpr int kQueues = 8;
 // One work item: sequence (or broadcast item) b, tile t along the stationary
 // axis, head h (a query head for query-stationary kernels, a KV head for the
 // key-stationary one).
+// One work item: sequence b, tile t, head (or head/slice) h, and the sequence's
+// packed offsets and lengths, so a consumer needs one 32-byte load per item.
 struct WorkItem {
   int32_t b;
   int32_t t;
   int32_t h;
   int32_t pad;
+  int32_t q_base;   // first packed query row (broadcast-Q: 0)
+  int32_t lq;       // query rows (broadcast-Q: Nq)
+  int32_t k_base;   // first packed key row
+  int32_t lk;       // key rows
 };
 
 // Queue descriptors.  start/size are read once per workgroup; each consumer

@@ -193,6 +193,10 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedBatch batch) 
     const int nt = n / per_tile;
     const int base = q_start[q] + r_off[r];
     const int end = min(q_start[q] + q_size[q], base + n);
+    const int q_base = a.bcast_nq > 0 ? 0 : a.cu_q[b];
+    const int lq = a.bcast_nq > 0 ? a.bcast_nq : a.cu_q[b + 1] - q_base;
+    const int k_base = a.cu_k[b];
+    const int lk = a.cu_k[b + 1] - k_base;
     for (int idx = 0; base + idx < end; ++idx) {
       const int tt = idx / per_tile, hi = idx % per_tile;
       WorkItem it;
@@ -200,6 +204,10 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedBatch batch) 
       it.t = (a.causal && a.mode == 0) ? nt - 1 - tt : tt;
       it.h = g * per_tile + hi;
       it.pad = 0;
+      it.q_base = q_base;
+      it.lq = lq;
+      it.k_base = k_base;
+      it.lk = lk;
       a.items[base + idx] = it;
     }
   }
