@@ -194,7 +194,7 @@ jfa_status_t check_decode(const jfa_decode_params_t* p) {
   if (p->batch < 1 || p->num_heads_q < 1 || p->num_heads_kv < 1) return JFA_ERR_INVALID_ARGUMENT;
   if (p->num_heads_q % p->num_heads_kv != 0) return JFA_ERR_INVALID_ARGUMENT;
   if (p->page_size < 1 || p->num_pages < 1 || p->max_pages_per_seq < 1) return JFA_ERR_INVALID_ARGUMENT;
-  if (p->num_splits < 0 || p->num_splits > 128) return JFA_ERR_INVALID_ARGUMENT;
+  if (p->num_splits < 0 || p->num_splits > kMaxDecodeSplits) return JFA_ERR_INVALID_ARGUMENT;
   if (!(p->softmax_scale == p->softmax_scale) || isinf(p->softmax_scale)) return JFA_ERR_INVALID_ARGUMENT;
   if (!supported_dim(p->head_dim)) return JFA_ERR_UNSUPPORTED;
   if (p->q_len < 1 || p->q_len > 16 || (p->causal != 0 && p->causal != 1)) return JFA_ERR_INVALID_ARGUMENT;

@@ -48,6 +48,11 @@ struct DecOcc {
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
+#ifndef JFA_DECODE_LPT
+#define JFA_DECODE_LPT 1
+#endif
+constexpr int kLptMaxBatch = 256;   // one rank per thread
+
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -90,7 +95,26 @@ __global__ __launch_bounds__(256, (DecOcc<D, NCG>::WG_PER_CU)) void decode_kerne
   const int cu = unit % n_cu;
   unit /= n_cu;
   const int s = unit % a.splits;
-  const int b = unit / a.splits;
+  const int b_rank = unit / a.splits;
+  // Longest sequences first: the workgroups are dispatched in index order, so the
+  // units of long sequences start early and short ones fill in at the end.  The
+  // rank is computed from the KV lengths by every workgroup (batches up to
+  // kLptMaxBatch; larger ones keep the given order).
+  __shared__ int s_b;
+  int b = b_rank;
+  if (JFA_DECODE_LPT && a.batch <= kLptMaxBatch) {
+    if (tid < a.batch) {
+      const int lt = a.seqlens[tid];
+      int rank = 0;
+      for (int j = 0; j < a.batch; ++j) {
+        const int lj = a.seqlens[j];
+        rank += (lj > lt || (lj == lt && j < tid)) ? 1 : 0;
+      }
+      if (rank == b_rank) s_b = tid;
+    }
+    __syncthreads();
+    b = s_b;
+  }
   const int L = a.seqlens[b];
   const int chunk = cdiv(cdiv(L, a.splits), BN) * BN;
   const int k_lo = s * chunk;
@@ -295,21 +319,31 @@ __global__ __launch_bounds__(256, (DecOcc<D, NCG>::WG_PER_CU)) void decode_kerne
 
 // LSE-weighted merge of the split partials: LSE = log sum_s exp(LSE_s),
 // O = sum_s exp(LSE_s - LSE) O_s.  Splits with LSE_s = -inf (no keys) weigh 0.
+// One block per (b, token, h) row: the split LSEs are read in parallel into LDS,
+// then every thread (one d each) sums its column with the partial loads unrolled,
+// so a row costs a few memory round trips instead of two per split.
 template <int D>
 __global__ __launch_bounds__(D) void decode_combine_kernel(DecodeArgs a) {
+  __shared__ float w_s[kMaxDecodeSplits];
   const int bh = blockIdx.x;            // (b * q_len + t) * hq + h
   const int d = threadIdx.x;
   const int64_t plane = (int64_t)a.batch * a.q_len * a.hq;
   const float NEG_INF = -__builtin_inff();
+  const int splits = a.splits;
+  for (int s = d; s < splits; s += D) w_s[s] = a.lse_part[s * plane + bh];
+  __syncthreads();
   float M = NEG_INF;
-  for (int s = 0; s < a.splits; ++s) M = fmaxf(M, a.lse_part[s * plane + bh]);
+  for (int s = 0; s < splits; ++s) M = fmaxf(M, w_s[s]);
   float wsum = 0.f, O = 0.f;
   if (M != NEG_INF) {
-    for (int s = 0; s < a.splits; ++s) {
-      const float ls = a.lse_part[s * plane + bh];
+    const float* op = a.o_part + (int64_t)bh * D + d;
+    const int64_t stride = plane * D;
+#pragma unroll 4
+    for (int s = 0; s < splits; ++s) {
+      const float ls = w_s[s];
       const float wt = ls == NEG_INF ? 0.f : __expf(ls - M);
       wsum += wt;
-      O += wt * a.o_part[(s * plane + bh) * D + d];
+      O = fmaf(wt, op[s * stride], O);
     }
   }
   a.o[(int64_t)bh * D + d] = (__bf16)(wsum > 0.f ? O / wsum : 0.f);

@@ -173,6 +173,7 @@ struct DecodeArgs {
 };
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeArgs& a, int head_dim, hipStream_t stream);
+constexpr int kMaxDecodeSplits = 128;   // largest num_splits the decode accepts
 int decode_chunk_align();
 int decode_col_groups(int columns, int head_dim);      // 16-column query groups per decode workgroup
 int decode_blocks_per_cu(int columns, int head_dim);   // decode workgroups resident per CU
