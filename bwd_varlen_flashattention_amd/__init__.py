@@ -135,17 +135,20 @@ def _kv_fp8(k_cache) -> bool:
     return k_cache.dtype in (getattr(torch, "float8_e4m3fn", None), torch.uint8)
 
 
-def _decode_params(q, k_cache, page_table, num_splits, scale, causal=False, k_scale=None, v_scale=None):
+def _decode_params(q, k_cache, page_table, num_splits, scale, causal=False, k_scale=None, v_scale=None,
+                   q_scale=None):
     """q is [B, Hq, d] (one token per sequence) or [B, q_len, Hq, d]; an fp8 cache
-    (float8_e4m3fn, or its raw bytes as uint8) selects the e4m3 path."""
+    or query (float8_e4m3fn, or its raw bytes as uint8) selects the e4m3 path."""
     q_len = 1 if q.dim() == 3 else q.shape[1]
     fp8 = _kv_fp8(k_cache)
+    q8 = _is_fp8(q)
     return DecodeParams(
         batch=q.shape[0], num_heads_q=q.shape[-2], num_heads_kv=k_cache.shape[2], head_dim=q.shape[-1],
         page_size=k_cache.shape[1], num_pages=k_cache.shape[0], max_pages_per_seq=page_table.shape[1],
         num_splits=int(num_splits), softmax_scale=float(scale) if scale is not None else 0.0,
         q_len=int(q_len), causal=int(bool(causal)), kv_dtype=1 if fp8 else 0,
-        k_scale=float(k_scale) if k_scale is not None else 0.0, v_scale=float(v_scale) if v_scale is not None else 0.0)
+        k_scale=float(k_scale) if k_scale is not None else 0.0, v_scale=float(v_scale) if v_scale is not None else 0.0,
+        q_dtype=1 if q8 else 0, q_scale=float(q_scale) if q_scale is not None else 0.0)
 
 
 def _check_cache(name, t):
@@ -164,25 +167,27 @@ def jfa_decode_num_splits(q, k_cache, page_table, num_splits: int = 0) -> int:
 
 def jfa_decode_paged(q, k_cache, v_cache, page_table, seqlens_k, num_splits: int = 0,
                      softmax_scale: Optional[float] = None, out=None, lse=None, workspace=None,
-                     causal: bool = False, k_scale: Optional[float] = None, v_scale: Optional[float] = None):
+                     causal: bool = False, k_scale: Optional[float] = None, v_scale: Optional[float] = None,
+                     q_scale: Optional[float] = None):
     """Paged decode of q_len new tokens per sequence against a paged KV cache.
 
     q [B, Hq, d] (one token) or [B, q_len, Hq, d] (q_len <= 16); caches
-    [num_pages, page_size, Hkv, d] -> o shaped like q, lse [B, Hq] or [B, q_len, Hq].
+    [num_pages, page_size, Hkv, d] -> o (bfloat16, shaped like q), lse [B, Hq] or [B, q_len, Hq].
     causal: the q_len tokens are the last ones of each sequence (bottom-right mask).
     FP8 caches (torch.float8_e4m3fn or raw uint8 bytes): K = k_scale * cache value,
-    V = v_scale * cache value.
+    V = v_scale * cache value.  An FP8 q: Q = q_scale * q value.
     """
     torch = _torch()
     lib = load()
     if q.dim() not in (3, 4):
         raise ValueError("q must be [B, Hq, d] or [B, q_len, Hq, d]")
-    _check_bf16("q", q, q.dim()); _check_cache("k_cache", k_cache); _check_cache("v_cache", v_cache)
+    (_check_fp8 if _is_fp8(q) else _check_bf16)("q", q, q.dim())
+    _check_cache("k_cache", k_cache); _check_cache("v_cache", v_cache)
     if _kv_fp8(k_cache) != _kv_fp8(v_cache):
         raise ValueError("k_cache and v_cache must have the same element type")
     _check_i32("page_table", page_table); _check_i32("seqlens_k", seqlens_k)
-    p = _decode_params(q, k_cache, page_table, num_splits, softmax_scale, causal, k_scale, v_scale)
-    o = out if out is not None else torch.empty_like(q)
+    p = _decode_params(q, k_cache, page_table, num_splits, softmax_scale, causal, k_scale, v_scale, q_scale)
+    o = out if out is not None else torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     l = lse if lse is not None else torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
     need = lib.jfa_decode_workspace_size(ctypes.byref(p))
     ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

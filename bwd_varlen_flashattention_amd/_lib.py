@@ -62,6 +62,8 @@ class DecodeParams(ctypes.Structure):
         ("kv_dtype", ctypes.c_int32),
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
+        ("q_dtype", ctypes.c_int32),
+        ("q_scale", ctypes.c_float),
     ]
 
 

@@ -199,6 +199,8 @@ jfa_status_t check_decode(const jfa_decode_params_t* p) {
   if (!supported_dim(p->head_dim)) return JFA_ERR_UNSUPPORTED;
   if (p->q_len < 1 || p->q_len > 16 || (p->causal != 0 && p->causal != 1)) return JFA_ERR_INVALID_ARGUMENT;
   if (p->kv_dtype != JFA_KV_BF16 && p->kv_dtype != JFA_KV_FP8_E4M3) return JFA_ERR_INVALID_ARGUMENT;
+  if (p->q_dtype != JFA_DTYPE_BF16 && p->q_dtype != JFA_DTYPE_FP8_E4M3) return JFA_ERR_INVALID_ARGUMENT;
+  if (!(p->q_scale == p->q_scale) || isinf(p->q_scale)) return JFA_ERR_INVALID_ARGUMENT;
   if (!(p->k_scale == p->k_scale) || isinf(p->k_scale) || !(p->v_scale == p->v_scale) || isinf(p->v_scale))
     return JFA_ERR_INVALID_ARGUMENT;
   if ((int64_t)(p->num_heads_q / p->num_heads_kv) * p->q_len > 256) return JFA_ERR_UNSUPPORTED;
@@ -507,9 +509,11 @@ jfa_status_t jfa_decode_paged(const jfa_decode_params_t* p, const void* q, const
   a.q_len = p->q_len;
   a.causal = p->causal;
   a.kv_fp8 = p->kv_dtype == JFA_KV_FP8_E4M3;
+  a.q_fp8 = p->q_dtype == JFA_DTYPE_FP8_E4M3;
   const float k_scale = (a.kv_fp8 && p->k_scale > 0.f) ? p->k_scale : 1.f;
+  const float q_scale = (a.q_fp8 && p->q_scale > 0.f) ? p->q_scale : 1.f;
   a.v_scale = (a.kv_fp8 && p->v_scale > 0.f) ? p->v_scale : 1.f;
-  a.scale_log2 = eff_scale(p->softmax_scale, p->head_dim) * 1.4426950408889634f * k_scale;
+  a.scale_log2 = eff_scale(p->softmax_scale, p->head_dim) * 1.4426950408889634f * k_scale * q_scale;
   TimedRegion tr(JFA_TIMING_DECODE, stream);
   hipError_t e = launch_decode(a, p->head_dim, stream);
   tr.finish();

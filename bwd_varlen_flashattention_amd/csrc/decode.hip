@@ -133,9 +133,14 @@ __global__ __launch_bounds__(256, (DecOcc<D, NCG>::WG_PER_CU)) void decode_kerne
     const bool ok = c < cols;
     const int t = ok ? c / a.group : 0;
     const int h = g * a.group + (ok ? c % a.group : 0);
-    const __bf16* qp = a.q + (((int64_t)b * a.q_len + t) * a.hq + h) * D + 8 * g16;
+    const int64_t qe = (((int64_t)b * a.q_len + t) * a.hq + h) * D + 8 * g16;   // element offset
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) qf[cg][kk] = ok ? *(const bf16x8*)(qp + 32 * kk) : zero_bf16x8();
+    for (int kk = 0; kk < KK; ++kk) {
+      if (!ok) qf[cg][kk] = zero_bf16x8();
+      else if (a.q_fp8)   // e4m3 query: 8 bytes widened exactly to bf16
+        qf[cg][kk] = __builtin_bit_cast(bf16x8, widen_e4m3x8(*(const uint2*)((const unsigned char*)a.q + qe + 32 * kk)));
+      else qf[cg][kk] = *(const bf16x8*)(a.q + qe + 32 * kk);
+    }
     kmax[cg] = min(k_hi - 1, a.causal ? t + L - a.q_len : L - 1);
   }
 

@@ -34,6 +34,22 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // num_records return zero.
 constexpr int kBufferFlags = 0x00020000;
 
+// 8 e4m3 bytes -> 8 bf16 (exact), packed two per dword in column order.
+__device__ __forceinline__ u32x4 widen_e4m3x8(uint2 x) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  u32x4 r;
+  const f2_t p[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(x.x, false), __builtin_amdgcn_cvt_pk_f32_fp8(x.x, true),
+                     __builtin_amdgcn_cvt_pk_f32_fp8(x.y, false), __builtin_amdgcn_cvt_pk_f32_fp8(x.y, true)};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    bf16x2 q;
+    q[0] = (__bf16)p[i][0];
+    q[1] = (__bf16)p[i][1];
+    r[i] = __builtin_bit_cast(uint32_t, q);
+  }
+  return r;
+}
+
 // Raw buffer resource for a wave-uniform base and byte range.  The base and range
 // are moved to scalar registers explicitly: when a 64-bit address product ends up
 // in vector registers, the compiler otherwise wraps every load through the

@@ -76,21 +76,6 @@ __device__ __forceinline__ f32x16 mfma32x32x64_fp8(i32x8 a, i32x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
 }
 
-// 8 e4m3 bytes -> 8 bf16 (exact), packed two per dword in column order.
-__device__ __forceinline__ u32x4 widen_e4m3x8(uint2 x) {
-  typedef float f2_t __attribute__((ext_vector_type(2)));
-  u32x4 r;
-  const f2_t p[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(x.x, false), __builtin_amdgcn_cvt_pk_f32_fp8(x.x, true),
-                     __builtin_amdgcn_cvt_pk_f32_fp8(x.y, false), __builtin_amdgcn_cvt_pk_f32_fp8(x.y, true)};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    bf16x2 q;
-    q[0] = (__bf16)p[i][0];
-    q[1] = (__bf16)p[i][1];
-    r[i] = __builtin_bit_cast(uint32_t, q);
-  }
-  return r;
-}
 
 // Position of a 4-key quarter inside its stored 16-key group: the S^T accumulator
 // gives lane half h the keys {4h..4h+3, 8+4h..8+4h+3} of each group as one

@@ -168,6 +168,7 @@ struct DecodeArgs {
   int32_t q_len;            // query tokens per sequence (1 = single-token decode)
   int32_t causal;           // bottom-right mask over the q_len tokens
   int32_t kv_fp8;           // caches hold OCP e4m3 bytes
+  int32_t q_fp8;            // q holds OCP e4m3 bytes (its scale is folded into scale_log2)
   float v_scale;            // fp8 V dequantisation scale (K's is folded into scale_log2)
   float scale_log2;
 };

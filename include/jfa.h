@@ -200,6 +200,8 @@ typedef struct {
   int32_t kv_dtype;           /* JFA_KV_BF16 or JFA_KV_FP8_E4M3 (k_cache / v_cache element type) */
   float k_scale;              /* fp8 caches: K = k_scale * e4m3 value (<= 0 means 1) */
   float v_scale;              /* fp8 caches: V = v_scale * e4m3 value (<= 0 means 1) */
+  int32_t q_dtype;            /* JFA_DTYPE_BF16 or JFA_DTYPE_FP8_E4M3 (q element type) */
+  float q_scale;              /* e4m3 q: Q = q_scale * e4m3 value (<= 0 means 1) */
 } jfa_decode_params_t;
 
 size_t jfa_decode_workspace_size(const jfa_decode_params_t* p);

@@ -111,6 +111,7 @@ DEC_BAD = [
     (dict(num_heads_q=514, num_heads_kv=2), 2), (dict(num_heads_q=34, num_heads_kv=2, q_len=16), 2),
     (dict(num_heads_q=30), 1), (dict(num_pages=0), 1),
     (dict(q_len=0), 1), (dict(q_len=17), 1), (dict(causal=2), 1),
+    (dict(q_dtype=2), 1), (dict(q_dtype=1, q_scale=float("nan")), 1), (dict(kv_dtype=3), 1),
 ]
 
 

@@ -220,3 +220,27 @@ def test_decode_fp8_config_sampled(jfa):
         ro, rl = oracle.decode_forward(f(inp.q[b:b + 1]), f(inp.k[ks:ke]), f(inp.v[ks:ke]), np.array([0, ke - ks]))
         check_o(o[b:b + 1], ro, f"O[seq {b}]")
         check_lse(lse[b:b + 1], rl, f"LSE[seq {b}]")
+
+
+@pytest.mark.parametrize("kv_fp8", [False, True])
+@pytest.mark.parametrize("q_len,causal", [(1, False), (4, True)])
+@pytest.mark.parametrize("dim", [64, 128, 256])
+def test_decode_fp8_query(jfa, kv_fp8, q_len, causal, dim):
+    """An e4m3 query (with bf16 or e4m3 caches): the result is attention of the
+    dequantised query; the query scale folds into the scores."""
+    lens = [1, 63, 300, 0, 129]
+    inp = workloads.decode(70 + dim, lens, 8, 2, dim, 16, q_len=q_len, kv_fp8=kv_fp8, k_scale=0.5, v_scale=2.0)
+    q8, qd = workloads.e4m3(inp.q, 0.03125)
+    d = _DevFp8(inp) if kv_fp8 else _Dev(inp)
+    qdev = torch.from_numpy(q8).to("cuda").view(torch.float8_e4m3fn)
+    f = lambda x: x.astype(np.float64)
+    if q_len == 1:
+        ro, rl = oracle.decode_forward(f(qd), f(inp.k), f(inp.v), inp.cu_k)
+    else:
+        ro, rl = oracle.decode_forward_multi(f(qd), f(inp.k), f(inp.v), inp.cu_k, causal)
+    sc = dict(k_scale=0.5, v_scale=2.0) if kv_fp8 else {}
+    for splits in (1, 3):
+        o, lse = jfa.jfa_decode_paged(qdev, d.kc, d.vc, d.pt, d.sl, splits, causal=causal, q_scale=0.03125, **sc)
+        torch.cuda.synchronize()
+        check_o(host(o), ro, f"O splits={splits}")
+        check_lse(host(lse), rl, f"LSE splits={splits}")

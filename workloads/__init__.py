@@ -318,6 +318,11 @@ def _e4m3(x, scale: float):
     return t.view(torch.uint8).numpy().copy(), (t.float() * scale).numpy()
 
 
+def e4m3(x, scale: float):
+    """OCP e4m3 bytes of x / scale (nearest even) and their exact dequantised values."""
+    return _e4m3(x, scale)
+
+
 def fp8_qkv(inp, q_scale=None, k_scale=None, v_scale=None):
     """e4m3 copies of q, k, v with per-tensor scales (default: amax / 448, the
     largest finite e4m3 value).  Returns (same inputs with q, k, v replaced by the
