@@ -137,6 +137,27 @@ __device__ __forceinline__ void store_transposed_4x8(__bf16* dst, int pitch, con
   }
 }
 
+// Staging block of a thread: (row block, 8-column block) of a tile staged as
+// 4-row x 8-column blocks, each written row-major (16-byte stores) and
+// transposed (8-byte stores).  gfx950's LDS serves 16-byte accesses 8 lanes and
+// 8-byte accesses 16 lanes per cycle over 32 banks (measured with in-bounds store
+// probes).  With 16 row blocks: the transposed stores' bank depends only on the
+// row block, so the 16 lanes of a group take 16 row blocks (thread bits 0-3);
+// the row-major stores need (4 * row block + column block) mod 8 distinct in
+// each 8-lane group, which the column block gets from bits 1-2 xor bits 4-5
+// (bits 6-7 give its high half).  Both stores are then free of bank conflicts;
+// stepping the lanes down rows alone made the row-major stores 4-way.  Tiles of
+// 8 row blocks keep row blocks fastest.
+__device__ __forceinline__ void staging_block(int tid, int row_blocks, int& rb, int& cb) {
+  if (row_blocks == 16) {
+    rb = tid & 15;
+    cb = (((tid >> 1) ^ (tid >> 4)) & 3) | ((tid >> 6) << 2);
+  } else {
+    rb = tid % row_blocks;
+    cb = tid / row_blocks;
+  }
+}
+
 // ============================================================================= dK / dV
 // Head-dim chunking ("Cutting edge isn't plug-and-play: customising
 // FlashAttention-4 on B300", Phase 2): for d = 256 one work item owns the dK/dV
@@ -182,8 +203,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   const float INF = __builtin_inff();
 
   // staging: thread owns rows 4*sq..4*sq+3, columns 8*sd..8*sd+7 of the Q and dO tiles
-  const bool stager = tid < T::QBLOCKS;
-  const int sq = tid % (BM / 4), sd = tid / (BM / 4);
+  int sq, sd;
+  staging_block(tid, BM / 4, sq, sd);
+  const bool stager = sd < D / 8;
   const int qrs = a.hq * D;                           // elements between query rows
   uint32_t qoff[4];
 #pragma unroll
@@ -412,8 +434,9 @@ __global__ __launch_bounds__(256, DqTile<D>::WG_PER_CU) void bwd_dq_kernel(BwdAr
   // staging: K as one 4-key x 8-column block per thread (written row-major and
   // transposed); V as row-major 16-byte chunks
   const int rs = a.hkv * D;
-  const bool k_stager = tid < T::KBLOCKS;
-  const int skb = tid % (BN / 4), skd = tid / (BN / 4);
+  int skb, skd;
+  staging_block(tid, BN / 4, skb, skd);
+  const bool k_stager = skd < D / 8;
   uint32_t koff[4], voff[T::VLOADS];
 #pragma unroll
   for (int i = 0; i < 4; ++i) koff[i] = (uint32_t)(((4 * skb + i) * rs + 8 * skd) * 2);
