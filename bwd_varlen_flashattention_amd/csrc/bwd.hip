@@ -159,6 +159,10 @@ __device__ __forceinline__ void staging_block(int tid, int row_blocks, int& rb, 
 }
 
 // ============================================================================= dK / dV
+#ifndef JFA_DKDV_PIPE
+#define JFA_DKDV_PIPE 1
+#endif
+
 // Head-dim chunking ("Cutting edge isn't plug-and-play: customising
 // FlashAttention-4 on B300", Phase 2): for d = 256 one work item owns the dK/dV
 // columns of one DC-wide slice of the head dimension.  S = Q K^T and dP = dO V^T
@@ -318,10 +322,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       const int buf = s & 1;
       const int qt = i_first + unit_of(s) % n_qt;
       if (s + 1 < n_steps) load_regs(s + 1);
-#pragma unroll
-      for (int qb = 0; qb < BM / 32; ++qb) {
-        // S[q][key], dP[q][key]: A = Q / dO rows, B = K / V fragments
-        f32x16 sacc = f32x16{}, pacc = f32x16{};
+      // S[q][key], dP[q][key] of query block qb: A = Q / dO rows, B = K / V fragments
+      auto scores = [&](int qb, f32x16& sacc, f32x16& pacc) {
+        sacc = f32x16{};
+        pacc = f32x16{};
         const __bf16* qp = &q_lds[buf][(32 * qb + l32) * QP + 8 * hh];
         const __bf16* dp = &do_lds[buf][(32 * qb + l32) * QP + 8 * hh];
 #pragma unroll
@@ -329,7 +333,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
           sacc = mfma32x32x16(*(const bf16x8*)(qp + 16 * ks), kf[ks], sacc);
           pacc = mfma32x32x16(*(const bf16x8*)(dp + 16 * ks), vf[ks], pacc);
         }
-        // P = exp2(S*c - LSE*log2e); dS = P * (dP - delta)
+      };
+      // P = exp2(S*c - LSE*log2e); dS = P * (dP - delta); then
+      // dV^T[d][key] += dO^T P ; dK^T[d][key] += Q^T dS  (A operands from the transposed tiles)
+      auto grads = [&](int qb, const f32x16& sacc, const f32x16& pacc) {
         float pv[16], dsv[16];
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
@@ -347,7 +354,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         }
         const bf16x8 pb0 = to_bf16x8(pv), pb1 = to_bf16x8(pv + 8);
         const bf16x8 sb0 = to_bf16x8(dsv), sb1 = to_bf16x8(dsv + 8);
-        // dV^T[d][key] += dO^T P ; dK^T[d][key] += Q^T dS  (A operands from the transposed tiles)
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
           const __bf16* dtp = &dot_lds[buf][(32 * db + l32) * QTP + 32 * qb + 8 * hh];
@@ -356,6 +362,22 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
           dvt[db] = mfma32x32x16(*(const bf16x8*)(dtp + 16), pb1, dvt[db]);
           dkt[db] = mfma32x32x16(*(const bf16x8*)(qtp), sb0, dkt[db]);
           dkt[db] = mfma32x32x16(*(const bf16x8*)(qtp + 16), sb1, dkt[db]);
+        }
+      };
+      if constexpr (BM == 64 && JFA_DKDV_PIPE) {
+        // both query blocks' S/dP first: the second block's MFMAs run while the
+        // first block's softmax occupies the VALU
+        f32x16 s0, p0, s1, p1;
+        scores(0, s0, p0);
+        scores(1, s1, p1);
+        grads(0, s0, p0);
+        grads(1, s1, p1);
+      } else {
+#pragma unroll
+        for (int qb = 0; qb < BM / 32; ++qb) {
+          f32x16 sacc, pacc;
+          scores(qb, sacc, pacc);
+          grads(qb, sacc, pacc);
         }
       }
       if (s + 1 < n_steps) store_lds(buf ^ 1);
