@@ -146,15 +146,17 @@ __device__ __forceinline__ void store_transposed_4x8(__bf16* dst, int pitch, con
 // the row-major stores need (4 * row block + column block) mod 8 distinct in
 // each 8-lane group, which the column block gets from bits 1-2 xor bits 4-5
 // (bits 6-7 give its high half).  Both stores are then free of bank conflicts;
-// stepping the lanes down rows alone made the row-major stores 4-way.  Tiles of
-// 8 row blocks keep row blocks fastest.
+// stepping the lanes down rows alone made the row-major stores 4-way.  With 8
+// row blocks (head dims above 128) the same construction (row block = bits 0-2,
+// column block from bits 1-2 xor 3-4) frees the row-major stores; the transposed
+// stores stay 2-way, as 16 lanes cannot hold 16 distinct row blocks.
 __device__ __forceinline__ void staging_block(int tid, int row_blocks, int& rb, int& cb) {
   if (row_blocks == 16) {
     rb = tid & 15;
     cb = (((tid >> 1) ^ (tid >> 4)) & 3) | ((tid >> 6) << 2);
-  } else {
-    rb = tid % row_blocks;
-    cb = tid / row_blocks;
+  } else {   // 8 row blocks
+    rb = tid & 7;
+    cb = (((tid >> 1) ^ (tid >> 3)) & 3) | ((tid >> 5) << 2);
   }
 }
 
