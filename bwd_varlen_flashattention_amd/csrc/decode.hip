@@ -72,7 +72,8 @@ __global__ __launch_bounds__(256, (DecOcc<D, NCG>::WG_PER_CU)) void decode_kerne
   using T = DecTile<D>;
   constexpr int BN = T::BN, KP = T::KP, VP = T::VP, KK = T::KK, DB = T::DB;
   constexpr int KV_BYTES = BN * (KP + VP) * 2;
-  constexpr int MERGE_BYTES = 4 * 16 * D * 4 + 2 * 4 * 16 * 4;
+  constexpr int OP = D + 4;   // merge row pitch (floats): 16-byte stores of 8 lanes on distinct banks
+  constexpr int MERGE_BYTES = 4 * 16 * OP * 4 + 2 * 4 * 16 * 4;
   constexpr int SMEM = KV_BYTES > MERGE_BYTES ? KV_BYTES : MERGE_BYTES;
   static_assert(DecOcc<D, NCG>::WG_PER_CU * SMEM <= 160 * 1024, "LDS budget");
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
@@ -269,8 +270,8 @@ __global__ __launch_bounds__(256, (DecOcc<D, NCG>::WG_PER_CU)) void decode_kerne
 
   // merge the four waves, one column group at a time: lanes of one column share
   // m_run; l sums over the 4 row groups
-  float* o_s = (float*)smem;                       // [4][16][D]
-  float* m_s = o_s + 4 * 16 * D;                   // [4][16]
+  float* o_s = (float*)smem;                       // [4][16][OP]
+  float* m_s = o_s + 4 * 16 * OP;                  // [4][16]
   float* l_s = m_s + 4 * 16;                       // [4][16]
   if (n_tiles > 0) __syncthreads();
 #pragma unroll
@@ -279,9 +280,7 @@ __global__ __launch_bounds__(256, (DecOcc<D, NCG>::WG_PER_CU)) void decode_kerne
     lr += __shfl_xor(lr, 16);
     lr = xhalf_sum(lr);
 #pragma unroll
-    for (int db = 0; db < DB; ++db)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) o_s[(w * 16 + l16) * D + 16 * db + 4 * g16 + r] = acc[cg][db][r];
+    for (int db = 0; db < DB; ++db) *(f32x4*)&o_s[(w * 16 + l16) * OP + 16 * db + 4 * g16] = acc[cg][db];
     if (g16 == 0) {
       m_s[w * 16 + l16] = m_run[cg];
       l_s[w * 16 + l16] = lr;
@@ -301,7 +300,7 @@ __global__ __launch_bounds__(256, (DecOcc<D, NCG>::WG_PER_CU)) void decode_kerne
         const float mw = m_s[ww * 16 + q];
         const float wt = (mw == NEG_INF) ? 0.f : fast_exp2(mw - M);
         Lsum += wt * l_s[ww * 16 + q];
-        O += wt * o_s[(ww * 16 + q) * D + d];
+        O += wt * o_s[(ww * 16 + q) * OP + d];
       }
       const float inv = Lsum > 0.f ? (FP8 ? a.v_scale : 1.f) / Lsum : 0.f;
       const float lse = Lsum > 0.f ? (M + __log2f(Lsum)) * kLn2 : NEG_INF;
