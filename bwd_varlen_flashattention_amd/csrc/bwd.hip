@@ -2,7 +2,7 @@
 //
 // What is computed ("Cutting edge isn't plug-and-play: customising
 // FlashAttention-4 on B300", Phase 2 chunked-backward pseudocode and its buffer
-// list, restated without head-dim chunking because d <= 128 fits on chip):
+// list; the head-dim slicing is used for dK/dV at d = 256, see DkvTile):
 //   P = exp(S - LSE) rebuilt from the forward's saved LSE, S = Q K^T * scale,
 //   delta = rowsum(dO * O), dP = dO V^T, dS = P * (dP - delta),
 //   dV = P^T dO, dK = scale dS^T Q, dQ = scale dS K.
@@ -15,7 +15,8 @@
 //   bwd_dkdv_kernel  persistent, key-stationary: a workgroup owns 128 keys of one
 //                    KV head; K/V fragments stay in VGPRs and the dK^T/dV^T
 //                    accumulators in registers across all query tiles and all
-//                    query heads of the GQA group.  64-row Q/dO tiles are staged
+//                    query heads of the GQA group.  64-row Q/dO tiles (32 above
+//                    d = 128) are staged
 //                    into double-buffered LDS both row-major (A operands of
 //                    S = Q K^T and dP = dO V^T) and transposed (A operands of
 //                    dV^T += dO^T P and dK^T += Q^T dS, with P and dS taken
