@@ -23,7 +23,7 @@
 //                    straight from the S/dP accumulators), so every MFMA operand
 //                    is a single ds_read_b128.
 //   bwd_dq_kernel    persistent, query-stationary (the forward's structure):
-//                    recomputes S^T = K Q^T and dP^T = V dO^T per 64-key tile
+//                    recomputes S^T = K Q^T and dP^T = V dO^T per 32-key tile
 //                    and accumulates dQ^T += K^T dS^T in registers, with dS^T
 //                    straight from the accumulators and K^T staged transposed.
 //                    dQ is written once per query tile: no atomics, so dQ is
@@ -426,7 +426,12 @@ template <int D>
 struct DqTile {
   static constexpr int NT = 256;             // 4 waves, 32 query rows each
   static constexpr int BM = 128;             // query rows per item
-  static constexpr int BN = D <= 128 ? 64 : 32;   // keys per tile
+  // keys per tile: 32, with the LDS stage double-buffered (one barrier per tile;
+  // the next tile's stores leave the critical path); d = 96 splits evenly over
+  // the 256 staging threads only with 64-key tiles, of which two workgroups per
+  // CU fit a single stage
+  static constexpr int BN = D == 96 ? 64 : 32;
+  static constexpr int NSTAGE = BN == 32 ? 2 : 1;
   // d <= 128: two workgroups per CU; d = 192 / 256 keep Q, dO and dQ^T of the
   // whole head in the registers of one wave per SIMD
   static constexpr int WG_PER_CU = D <= 128 ? 2 : 1;
@@ -438,16 +443,17 @@ struct DqTile {
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
   static_assert(BN * CH % NT == 0 && KBLOCKS <= NT, "tile load split");
-  static_assert(WG_PER_CU * (2 * BN * KP + D * KTP) * 2 <= 160 * 1024, "LDS budget");
+  static_assert(WG_PER_CU * NSTAGE * (2 * BN * KP + D * KTP) * 2 <= 160 * 1024, "LDS budget");
 };
 
 template <int D, bool CAUSAL, bool BCAST>
 __global__ __launch_bounds__(256, DqTile<D>::WG_PER_CU) void bwd_dq_kernel(BwdArgs a) {
   using T = DqTile<D>;
   constexpr int BM = T::BM, BN = T::BN, KP = T::KP, KTP = T::KTP, KS = T::KS, DB = T::DB;
-  __shared__ __attribute__((aligned(16))) __bf16 k_lds[BN * KP];
-  __shared__ __attribute__((aligned(16))) __bf16 v_lds[BN * KP];
-  __shared__ __attribute__((aligned(16))) __bf16 kt_lds[D * KTP];
+  constexpr int NSTAGE = T::NSTAGE;
+  __shared__ __attribute__((aligned(16))) __bf16 k_lds[NSTAGE][BN * KP];
+  __shared__ __attribute__((aligned(16))) __bf16 v_lds[NSTAGE][BN * KP];
+  __shared__ __attribute__((aligned(16))) __bf16 kt_lds[NSTAGE][D * KTP];
   __shared__ int s_item;
   __shared__ int s_queue[2 * kQueues];
 
@@ -588,16 +594,16 @@ __global__ __launch_bounds__(256, DqTile<D>::WG_PER_CU) void bwd_dq_kernel(BwdAr
         for (int i = 0; i < T::VLOADS; ++i)
           vr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff[i], 0, 0));
       };
-      auto store_lds = [&]() {
+      auto store_lds = [&](int st) {
         if (k_stager) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) *(u32x4*)&k_lds[(4 * skb + i) * KP + 8 * skd] = kr[i];
-          store_transposed_4x8(&kt_lds[(8 * skd) * KTP + 16 * (skb >> 2) + 4 * quarter_pos(skb & 3)], KTP, kr);
+          for (int i = 0; i < 4; ++i) *(u32x4*)&k_lds[st][(4 * skb + i) * KP + 8 * skd] = kr[i];
+          store_transposed_4x8(&kt_lds[st][(8 * skd) * KTP + 16 * (skb >> 2) + 4 * quarter_pos(skb & 3)], KTP, kr);
         }
 #pragma unroll
         for (int i = 0; i < T::VLOADS; ++i) {
           const int id = tid + i * T::NT;
-          *(u32x4*)&v_lds[(id / T::CH) * KP + (id % T::CH) * 8] = vr[i];
+          *(u32x4*)&v_lds[st][(id / T::CH) * KP + (id % T::CH) * 8] = vr[i];
         }
       };
 
@@ -615,16 +621,19 @@ __global__ __launch_bounds__(256, DqTile<D>::WG_PER_CU) void bwd_dq_kernel(BwdAr
       auto tile = [&](int s, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
         const int j = tile_of(s);
-        store_lds();
-        __syncthreads();
+        const int stg = NSTAGE == 2 ? (s & 1) : 0;
+        if (NSTAGE == 1) {   // one stage: fill it once every reader of the last tile is done
+          store_lds(0);
+          __syncthreads();
+        }
         if (s + 1 < n_tiles) load_regs(tile_of(s + 1));
         const int kmax_ok = CAUSAL ? min(lk - 1, my_row + off) : lk - 1;
 #pragma unroll
         for (int kb = 0; kb < BN / 32; ++kb) {
           // S^T[key][q] = K Q^T and dP^T[key][q] = V dO^T for 32 keys
           f32x16 st = f32x16{}, pt = f32x16{};
-          const __bf16* kp = &k_lds[(32 * kb + l32) * KP + 8 * hh];
-          const __bf16* vp = &v_lds[(32 * kb + l32) * KP + 8 * hh];
+          const __bf16* kp = &k_lds[stg][(32 * kb + l32) * KP + 8 * hh];
+          const __bf16* vp = &v_lds[stg][(32 * kb + l32) * KP + 8 * hh];
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
             st = mfma32x32x16(*(const bf16x8*)(kp + 16 * ks), qf[ks], st);
@@ -644,15 +653,22 @@ __global__ __launch_bounds__(256, DqTile<D>::WG_PER_CU) void bwd_dq_kernel(BwdAr
           // dQ^T[d][q] += K^T[d][key] dS^T[key][q]
 #pragma unroll
           for (int db = 0; db < DB; ++db) {
-            const __bf16* ktp = &kt_lds[(32 * db + l32) * KTP + 32 * kb + 8 * hh];
+            const __bf16* ktp = &kt_lds[stg][(32 * db + l32) * KTP + 32 * kb + 8 * hh];
             dqt[db] = mfma32x32x16(*(const bf16x8*)(ktp), sb0, dqt[db]);
             dqt[db] = mfma32x32x16(*(const bf16x8*)(ktp + 16), sb1, dqt[db]);
           }
         }
-        __syncthreads();   // the single LDS stage is refilled by the next tile
+        // two stages: the next tile goes into the other stage, whose readers
+        // finished before the previous barrier; one stage: refilled next tile
+        if (NSTAGE == 2 && s + 1 < n_tiles) store_lds(stg ^ 1);
+        __syncthreads();
       };
 
       load_regs(tile_of(0));
+      if (NSTAGE == 2) {
+        store_lds(0);
+        __syncthreads();
+      }
       for (int s = 0; s < n_bulk; ++s) tile(s, std::false_type{});
       for (int s = n_bulk; s < n_tiles; ++s) tile(s, std::true_type{});
     }
@@ -697,7 +713,9 @@ int bwd_dkdv_slices(int head_dim) {
   return head_dim <= 128 ? DkvTile<128>::NC : head_dim <= 192 ? DkvTile<192>::NC : DkvTile<256>::NC;
 }
 int bwd_dq_rows() { return DqTile<128>::BM; }
-int bwd_dq_tile(int head_dim) { return head_dim <= 128 ? DqTile<128>::BN : DqTile<256>::BN; }
+int bwd_dq_tile(int head_dim) {
+  return head_dim == 96 ? DqTile<96>::BN : head_dim <= 128 ? DqTile<128>::BN : DqTile<256>::BN;
+}
 int bwd_dq_blocks_per_cu(int head_dim) { return head_dim <= 128 ? DqTile<128>::WG_PER_CU : DqTile<256>::WG_PER_CU; }
 
 template <int D>
