@@ -26,6 +26,7 @@ namespace jfa {
 constexpr int kSchedThreads = 1024;
 constexpr int kMaxBuckets = 4096;
 constexpr int kPerQueue = kSchedThreads / kQueues;
+static_assert(kPerQueue % 64 == 0 && kSchedThreads % 64 == 0, "scan segments are whole waves");
 constexpr int kLdsGroups = 6144;              // per-group arrays in LDS up to this many groups (96 KB)
 
 __device__ __forceinline__ int entry_cost(const SchedArgs& a, int lq, int lk, int t) {
@@ -50,22 +51,33 @@ __device__ __forceinline__ int snake_rank(int q, int j) {
   return j * kQueues + ((j & 1) ? kQueues - 1 - q : q);
 }
 
-// Exclusive scan of one value per thread over segments of `seg` consecutive threads.
-// Returns the exclusive prefix; *seg_total receives the segment's total.
+// Exclusive scan of one value per thread over segments of `seg` consecutive
+// threads (seg a multiple of 64).  Returns the exclusive prefix; *seg_total
+// receives the segment's total.  Each wave scans its 64 values with lane
+// shuffles; the wave totals go through LDS, so the whole scan costs two
+// barriers instead of two per doubling step.
 __device__ int segmented_scan(int* part, int x, int seg, int* seg_total) {
   const int tid = threadIdx.x;
-  part[tid] = x;
-  __syncthreads();
-  for (int off = 1; off < seg; off <<= 1) {
-    const int add = (tid % seg) >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += add;
-    __syncthreads();
+  const int lane = tid & 63, wave = tid >> 6;
+  int incl = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
   }
-  const int incl = part[tid];
-  *seg_total = part[(tid / seg) * seg + seg - 1];
+  if (lane == 63) part[wave] = incl;             // wave totals
   __syncthreads();
-  return incl - x;
+  const int waves_per_seg = seg >> 6;
+  const int first = wave - wave % waves_per_seg;   // first wave of this segment
+  int before = 0, total = 0;
+  for (int w = first; w < first + waves_per_seg; ++w) {
+    const int t = part[w];
+    before += w < wave ? t : 0;
+    total += t;
+  }
+  *seg_total = total;
+  __syncthreads();                                  // part is reused by the next scan
+  return before + incl - x;
 }
 
 // Total cost of the nt tiles of one group member.
