@@ -268,3 +268,44 @@ def test_large_head_dim_repeatability(jfa):
         got = _run_self(jfa, inp)
         for x, y in zip(got, first):
             np.testing.assert_array_equal(x, y)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_twenty_thousand_short_sequences(jfa, causal):
+    """80 000 (sequence, KV head) groups of 0-12 tokens: the work lists far exceed
+    the scheduler's on-chip arrays; oracle on a sample of sequences."""
+    rng = np.random.default_rng(41)
+    lengths = rng.integers(0, 13, 20000).tolist()
+    inp = workloads.jagged(12, lengths, None, 4, 4, 64, causal)
+    _say(f"20000 short sequences, causal={causal}, tokens {sum(lengths)}")
+    got = _run_self(jfa, inp)
+    seqs = sorted(set(rng.integers(0, 20000, 40).tolist() + [0, 19999]))
+    _compare_sampled(inp, got, _oracle_self(inp, seqs=seqs))
+
+
+def test_one_long_causal_sequence(jfa):
+    """One 32768-token causal sequence (2 query heads on 1 KV head, d = 64).  Rows of a
+    causal sequence depend only on their own keys, so O, LSE and dQ of sampled row
+    blocks come from the oracle on (those rows, keys up to the block's end); dK and dV
+    are checked through the softmax-Jacobian invariants (sum dK = 0, sum dV = sum dO)."""
+    L = 32768
+    inp = workloads.jagged(13, [L], None, 2, 1, 64, True)
+    got = _run_self(jfa, inp)
+    o, lse, dq, dk, dv = got
+    f = lambda x: x.astype(np.float64)
+    for i0 in (0, 16000, L - 64):
+        i1 = i0 + 64
+        cq, ck = np.array([0, 64]), np.array([0, i1])
+        ro, rl = oracle.attention_forward(f(inp.q[i0:i1]), f(inp.k[:i1]), f(inp.v[:i1]), cq, ck, True)
+        rdq, _, _ = oracle.attention_backward(f(inp.q[i0:i1]), f(inp.k[:i1]), f(inp.v[:i1]), f(inp.do[i0:i1]),
+                                              cq, ck, True)
+        check_o(o[i0:i1], ro, f"O rows {i0}..")
+        check_lse(lse[:, i0:i1], rl, f"LSE rows {i0}..")
+        check_grad(dq[i0:i1], rdq, f"dQ rows {i0}..")
+        _say(f"  rows {i0}..{i1} ok")
+    # dK sums to zero over the keys; dV sums to the group's dO summed over the queries
+    dk_sum = dk.sum(axis=0)
+    dv_sum, do_sum = dv.sum(axis=0), inp.do.astype(np.float64).sum(axis=(0, 1))[None, :]
+    scale = np.abs(dk).sum(axis=0).max()
+    assert np.abs(dk_sum).max() <= 2e-3 * scale, (np.abs(dk_sum).max(), scale)
+    assert np.abs(dv_sum - do_sum).max() <= 2e-3 * np.abs(dv).sum(axis=0).max()
