@@ -244,3 +244,29 @@ def test_decode_fp8_query(jfa, kv_fp8, q_len, causal, dim):
         torch.cuda.synchronize()
         check_o(host(o), ro, f"O splits={splits}")
         check_lse(host(lse), rl, f"LSE splits={splits}")
+
+
+def test_decode_one_very_long_sequence(jfa):
+    """One sequence of 262144 cached tokens (16384 pages of 16), Hq 32 / Hkv 8, d = 128,
+    automatic and explicit splits."""
+    inp = workloads.decode(90, [262144], 32, 8, 128, 16)
+    d = _Dev(inp)
+    ro, rl = _ref(inp)
+    for splits in (0, 7, 128):
+        o, lse = _run(jfa, d, splits)
+        check_o(o, ro, f"O splits={splits}")
+        check_lse(lse, rl, f"LSE splits={splits}")
+
+
+def test_decode_large_batch(jfa):
+    """4096 short sequences (0-100 tokens): past the batch size up to which the
+    units are dispatched longest first, so the given order is kept."""
+    rng = np.random.default_rng(91)
+    lens = rng.integers(0, 101, 4096).tolist()
+    inp = workloads.decode(92, lens, 8, 2, 64, 16)
+    d = _Dev(inp)
+    ro, rl = _ref(inp)
+    for splits in (0, 1, 3):
+        o, lse = _run(jfa, d, splits)
+        check_o(o, ro, f"O splits={splits}")
+        check_lse(lse, rl, f"LSE splits={splits}")
