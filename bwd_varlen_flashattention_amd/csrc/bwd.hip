@@ -251,7 +251,6 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         kf[ks] = key_ok ? *(const bf16x8*)(a.k + base + 16 * ks) : zero_bf16x8();
         vf[ks] = key_ok ? *(const bf16x8*)(a.v + base + 16 * ks) : zero_bf16x8();
       }
-      wait_vmem_all();
     }
     f32x16 dkt[DB], dvt[DB];
 #pragma unroll
@@ -388,7 +387,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     };
 
     if (n_steps > 0) {
-      load_regs(0);
+      load_regs(0);   // in flight together with the K/V fragments: one round trip
+      wait_vmem_all();
       store_lds(0);
       __syncthreads();
       // causal masking is one compare per element in every step: a single step
@@ -396,9 +396,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       for (int s = 0; s < n_steps; ++s) step(s);
     }
 
-    // epilogue: dK = scale * dK^T, dV = dV^T for the owned slice, 4 consecutive d per 8-byte store
-    if (key_ok) {
-      const int64_t base = ((int64_t)(k_base + my_key) * a.hkv + g) * D + c0;
+    // epilogue: dK = scale * dK^T, dV = dV^T of the owned slice.  A lane holds 4
+    // consecutive columns of one key per register quad, so direct stores would
+    // write 32 rows in 8-byte pieces per instruction; the wave's 32 x DC block is
+    // transposed through LDS instead (free after the last step's barrier) and
+    // written back 16 bytes per lane, DC / 8 lanes covering one row.
+    {
+      constexpr int EP = DC + 8;                 // row pitch of the epilogue blocks
+      static_assert(2 * 32 * EP <= 2 * BM * QP && 2 * 32 * EP <= 2 * DC * QTP, "epilogue blocks fit");
+      __bf16* kblk = (w < 2 ? &q_lds[0][0] : &do_lds[0][0]) + (w & 1) * 32 * EP;
+      __bf16* vblk = (w < 2 ? &qt_lds[0][0] : &dot_lds[0][0]) + (w & 1) * 32 * EP;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -410,13 +417,27 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
             vv4[x] = (__bf16)(dvt[db][4 * r4 + x]);
           }
           const int d0 = 32 * db + 8 * r4 + 4 * hh;
-          *(bf16x4*)(a.dk + base + d0) = kv4;
-          *(bf16x4*)(a.dv + base + d0) = vv4;
+          *(bf16x4*)(kblk + l32 * EP + d0) = kv4;
+          *(bf16x4*)(vblk + l32 * EP + d0) = vv4;
         }
+      // Claim the next item before the global stores: waiting for the atomic's
+      // result then waits for no store (the memory counter drains in order).
+      if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
+      __syncthreads();
+      constexpr int CPR = DC / 8;                // 16-byte chunks per row
+      static_assert(CPR % 2 == 0, "whole chunks per lane");
+#pragma unroll 1
+      for (int i = 0; i < CPR / 2; ++i) {   // not unrolled: per-lane addresses are not kept across items
+        const int id = lane + 64 * i, row = id / CPR, col = id % CPR;
+        const int key = kt0 + 32 * w + row;
+        if (key < lk) {
+          const int64_t dst = ((int64_t)(k_base + key) * a.hkv + g) * D + c0 + 8 * col;
+          *(u32x4*)(a.dk + dst) = *(const u32x4*)(kblk + row * EP + 8 * col);
+          *(u32x4*)(a.dv + dst) = *(const u32x4*)(vblk + row * EP + 8 * col);
+        }
+      }
     }
-    __syncthreads();   // the LDS buffers are reused by the next item
-    if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
-    __syncthreads();
+    __syncthreads();   // next item published; the epilogue blocks are read
     item = __builtin_amdgcn_readfirstlane(s_item);
   }
 }
