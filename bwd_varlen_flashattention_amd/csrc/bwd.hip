@@ -562,42 +562,6 @@ __global__ __launch_bounds__(256, DqTile<D>::WG_PER_CU) void bwd_dq_kernel(BwdAr
       }
       if (BCAST && n_tiles == 0) continue;   // uniform
 
-      // per-row state: Q and dO fragments (B operands of S^T = K Q^T, dP^T = V dO^T), LSE, delta
-      bf16x8 qf[KS], df[KS];
-      float lse2 = INF, dlt = 0.f;
-      {
-        const __bf16* qp = a.q + ((int64_t)(q_base + my_row) * a.hq + h) * D + 8 * hh;
-        const int64_t orow = BCAST ? (int64_t)b * lq + my_row : (int64_t)(q_base + my_row);
-        const __bf16* op = a.dout + (orow * a.hq + h) * D + 8 * hh;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          qf[ks] = row_ok ? *(const bf16x8*)(qp + 16 * ks) : zero_bf16x8();
-          df[ks] = row_ok ? *(const bf16x8*)(op + 16 * ks) : zero_bf16x8();
-        }
-        const int64_t li = BCAST ? ((int64_t)b * a.hq + h) * lq + my_row : (int64_t)h * a.total_q + q_base + my_row;
-        if (BCAST) {
-          if (row_ok) dlt = a.delta[li];   // written by bwd_pre_kernel
-        } else {
-          // delta = rowsum(dO * O): each lane holds half of the row, its partner lane the other half.
-          // Written for every row, also of tiles that see no key, for the dK/dV kernel.
-          const __bf16* orp = a.o + ((int64_t)(q_base + my_row) * a.hq + h) * D + 8 * hh;
-          float part = 0.f;
-#pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 ov = row_ok ? *(const bf16x8*)(orp + 16 * ks) : zero_bf16x8();
-#pragma unroll
-            for (int e = 0; e < 8; ++e) part = fmaf((float)ov[e], (float)df[ks][e], part);
-          }
-          dlt = xhalf_sum(part);
-          if (row_ok && hh == 0) a.delta[li] = dlt;
-        }
-        if (row_ok) {
-          const float l = a.lse[li];
-          lse2 = (l == NEG_INF) ? INF : l * kLog2e;
-        }
-      }
-      if (!BCAST && n_tiles == 0) continue;   // uniform; delta is written
-
       const __bf16* kbase = a.k + ((int64_t)k_base * a.hkv + g) * D;
       const __bf16* vbase = a.v + ((int64_t)k_base * a.hkv + g) * D;
       u32x4 kr[4], vr[T::VLOADS];
@@ -638,6 +602,45 @@ __global__ __launch_bounds__(256, DqTile<D>::WG_PER_CU) void bwd_dq_kernel(BwdAr
         const int j = s + rot;
         return j >= n_bulk ? j - n_bulk : j;
       };
+      // the first K/V tile travels with the Q / dO / O fragments: one round trip
+      if (n_tiles > 0) load_regs(tile_of(0));
+
+      // per-row state: Q and dO fragments (B operands of S^T = K Q^T, dP^T = V dO^T), LSE, delta
+      bf16x8 qf[KS], df[KS];
+      float lse2 = INF, dlt = 0.f;
+      {
+        const __bf16* qp = a.q + ((int64_t)(q_base + my_row) * a.hq + h) * D + 8 * hh;
+        const int64_t orow = BCAST ? (int64_t)b * lq + my_row : (int64_t)(q_base + my_row);
+        const __bf16* op = a.dout + (orow * a.hq + h) * D + 8 * hh;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          qf[ks] = row_ok ? *(const bf16x8*)(qp + 16 * ks) : zero_bf16x8();
+          df[ks] = row_ok ? *(const bf16x8*)(op + 16 * ks) : zero_bf16x8();
+        }
+        const int64_t li = BCAST ? ((int64_t)b * a.hq + h) * lq + my_row : (int64_t)h * a.total_q + q_base + my_row;
+        if (BCAST) {
+          if (row_ok) dlt = a.delta[li];   // written by bwd_pre_kernel
+        } else {
+          // delta = rowsum(dO * O): each lane holds half of the row, its partner lane the other half.
+          // Written for every row, also of tiles that see no key, for the dK/dV kernel.
+          const __bf16* orp = a.o + ((int64_t)(q_base + my_row) * a.hq + h) * D + 8 * hh;
+          float part = 0.f;
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const bf16x8 ov = row_ok ? *(const bf16x8*)(orp + 16 * ks) : zero_bf16x8();
+#pragma unroll
+            for (int e = 0; e < 8; ++e) part = fmaf((float)ov[e], (float)df[ks][e], part);
+          }
+          dlt = xhalf_sum(part);
+          if (row_ok && hh == 0) a.delta[li] = dlt;
+        }
+        if (row_ok) {
+          const float l = a.lse[li];
+          lse2 = (l == NEG_INF) ? INF : l * kLog2e;
+        }
+      }
+      if (!BCAST && n_tiles == 0) continue;   // uniform; delta is written
+
 
       auto tile = [&](int s, auto mask_tag) {
         constexpr bool MASK = decltype(mask_tag)::value;
@@ -685,7 +688,6 @@ __global__ __launch_bounds__(256, DqTile<D>::WG_PER_CU) void bwd_dq_kernel(BwdAr
         __syncthreads();
       };
 
-      load_regs(tile_of(0));
       if (NSTAGE == 2) {
         store_lds(0);
         __syncthreads();
@@ -694,35 +696,48 @@ __global__ __launch_bounds__(256, DqTile<D>::WG_PER_CU) void bwd_dq_kernel(BwdAr
       for (int s = n_bulk; s < n_tiles; ++s) tile(s, std::true_type{});
     }
 
-    // epilogue: dQ = scale * dQ^T; 4 consecutive d per store
-    const int lq_e = BCAST ? a.bcast_nq : e_lq;
-    if (my_row < lq_e) {
-      if (BCAST) {
-        // this chunk's partial, 4 consecutive d per store (summed in order by dq_convert)
-        float* dst = a.dq_part + (((int64_t)chunk * a.bcast_nq + my_row) * a.hq + h) * D;
+    // epilogue: dQ = scale * dQ^T
+    if (BCAST && my_row < a.bcast_nq) {
+      // this chunk's partial, 4 consecutive d per store (summed in order by dq_convert)
+      float* dst = a.dq_part + (((int64_t)chunk * a.bcast_nq + my_row) * a.hq + h) * D;
 #pragma unroll
-        for (int db = 0; db < DB; ++db)
+      for (int db = 0; db < DB; ++db)
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4)
-            *(f32x4*)(dst + 32 * db + 8 * r4 + 4 * hh) =
-                f32x4{dqt[db][4 * r4], dqt[db][4 * r4 + 1], dqt[db][4 * r4 + 2], dqt[db][4 * r4 + 3]};
-      } else {
-        __bf16* dst = a.dq + ((int64_t)(e_qbase + my_row) * a.hq + h) * D;
-#pragma unroll
-        for (int db = 0; db < DB; ++db)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            bf16x4 v4;
-#pragma unroll
-            for (int x = 0; x < 4; ++x) v4[x] = (__bf16)(dqt[db][4 * r4 + x] * a.scale);
-            *(bf16x4*)(dst + 32 * db + 8 * r4 + 4 * hh) = v4;
-          }
-      }
+        for (int r4 = 0; r4 < 4; ++r4)
+          *(f32x4*)(dst + 32 * db + 8 * r4 + 4 * hh) =
+              f32x4{dqt[db][4 * r4], dqt[db][4 * r4 + 1], dqt[db][4 * r4 + 2], dqt[db][4 * r4 + 3]};
     }
     if (!BCAST) {
-      __syncthreads();   // every thread has read s_item before it is rewritten
+      // A lane holds 4 consecutive columns of its row per register quad; the
+      // wave's 32 x D block goes through LDS (free after the last tile's closing
+      // barrier: waves 0-1 use the K stages, 2-3 the V stages) and out 16 bytes
+      // per lane, D / 8 lanes covering one row.
+      constexpr int EP = D + 8;
+      static_assert(2 * 32 * EP <= NSTAGE * BN * KP, "epilogue blocks fit");
+      __bf16* blk = (w < 2 ? &k_lds[0][0] : &v_lds[0][0]) + (w & 1) * 32 * EP;
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          bf16x4 v4;
+#pragma unroll
+          for (int x = 0; x < 4; ++x) v4[x] = (__bf16)(dqt[db][4 * r4 + x] * a.scale);
+          *(bf16x4*)(blk + l32 * EP + 32 * db + 8 * r4 + 4 * hh) = v4;
+        }
+      // claim the next item before any global store: waiting for the atomic's
+      // result then waits for no store (the memory counter drains in order)
       if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
       __syncthreads();
+      constexpr int CPR = D / 8;             // 16-byte chunks per row
+      static_assert(CPR % 2 == 0, "whole chunks per lane");
+#pragma unroll 1
+      for (int i = 0; i < CPR / 2; ++i) {    // not unrolled: per-lane addresses are not kept across items
+        const int id = lane + 64 * i, row = id / CPR, col = id % CPR;
+        const int r = row0 + 32 * w + row;
+        if (r < e_lq)
+          *(u32x4*)(a.dq + ((int64_t)(e_qbase + r) * a.hq + h) * D + 8 * col) = *(const u32x4*)(blk + row * EP + 8 * col);
+      }
+      __syncthreads();   // next item published; the LDS blocks are read
       item = __builtin_amdgcn_readfirstlane(s_item);
     }
   }

@@ -339,9 +339,22 @@ __global__ __launch_bounds__(256, FwdTile<D>::WG_PER_CU) void fwd_kernel(FwdArgs
     // epilogue: O = acc / l, LSE = (m + log2 l) * ln 2
     const float l_tot = xhalf_sum(l_run);
     const float inv = l_tot > 0.f ? (FP8 ? a.v_scale : 1.f) / l_tot : 0.f;
-    if (row_ok) {
-      __bf16* op = BCAST ? a.o + (((int64_t)b * lq + my_row) * a.hq + h) * D
-                         : a.o + ((int64_t)(q_base + my_row) * a.hq + h) * D;
+    const float m_fin = (m_run == NEG_INF) ? 0.f : m_run;
+    const float lse = l_tot > 0.f ? (m_fin + __log2f(l_tot)) * kLn2 : NEG_INF;
+    auto o_row = [&](int r) -> __bf16* {   // output row r of this item
+      return BCAST ? a.o + (((int64_t)b * lq + r) * a.hq + h) * D : a.o + ((int64_t)(q_base + r) * a.hq + h) * D;
+    };
+    // A lane holds 4 consecutive columns of its row per register quad, so direct
+    // stores write 32 rows in 8-byte pieces per instruction.  Where the stages
+    // hold the four 32 x D blocks, they go through LDS (free after the last tile's
+    // barrier) and out 16 bytes per lane, D / 8 lanes covering one row.
+    constexpr int EP = D + 8;
+    constexpr int VT_EL = 2 * D * VTP, K_EL = T::K_LDS_BYTES;   // stage capacities in bf16 elements
+    constexpr bool ALL_VT = 4 * 32 * EP <= VT_EL;
+    constexpr bool VIA_LDS = ALL_VT || (2 * 32 * EP <= VT_EL && 2 * 32 * EP <= K_EL);
+    if constexpr (VIA_LDS) {
+      __bf16* blk = (ALL_VT || w < 2) ? &vt_lds[0][0] + (ALL_VT ? w : (w & 1)) * 32 * EP
+                                      : (__bf16*)&k_raw[0][0] + (w & 1) * 32 * EP;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -349,19 +362,41 @@ __global__ __launch_bounds__(256, FwdTile<D>::WG_PER_CU) void fwd_kernel(FwdArgs
           bf16x4 ov;
 #pragma unroll
           for (int x = 0; x < 4; ++x) ov[x] = (__bf16)(acc[db][4 * r4 + x] * inv);
-          *(bf16x4*)(op + 32 * db + 8 * r4 + 4 * hh) = ov;
+          *(bf16x4*)(blk + l32 * EP + 32 * db + 8 * r4 + 4 * hh) = ov;
         }
-      if (hh == 0) {
-        const float m_sub = (m_run == NEG_INF) ? 0.f : m_run;
-        const float lse = l_tot > 0.f ? (m_sub + __log2f(l_tot)) * kLn2 : NEG_INF;
-        const int64_t li = BCAST ? ((int64_t)b * a.hq + h) * lq + my_row
-                                 : (int64_t)h * a.total_q + q_base + my_row;
-        a.lse[li] = lse;
+      // claim the next item before any global store: waiting for the atomic's
+      // result then waits for no store (the memory counter drains in order)
+      if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
+      __syncthreads();
+      constexpr int CPR = D / 8;             // 16-byte chunks per row
+      static_assert(CPR % 2 == 0, "whole chunks per lane");
+#pragma unroll 1
+      for (int i = 0; i < CPR / 2; ++i) {    // not unrolled: per-lane addresses are not kept across items
+        const int id = lane + 64 * i, row = id / CPR, col = id % CPR;
+        const int r = row0 + 32 * w + row;
+        if (r < lq) *(u32x4*)(o_row(r) + 8 * col) = *(const u32x4*)(blk + row * EP + 8 * col);
+      }
+    } else {
+      if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
+      if (row_ok) {
+        __bf16* op = o_row(my_row);
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            bf16x4 ov;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) ov[x] = (__bf16)(acc[db][4 * r4 + x] * inv);
+            *(bf16x4*)(op + 32 * db + 8 * r4 + 4 * hh) = ov;
+          }
       }
     }
-    __syncthreads();   // the LDS buffers are reused by the next item
-    if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
-    __syncthreads();
+    if (row_ok && hh == 0) {
+      const int64_t li = BCAST ? ((int64_t)b * a.hq + h) * lq + my_row
+                               : (int64_t)h * a.total_q + q_base + my_row;
+      a.lse[li] = lse;
+    }
+    __syncthreads();   // next item published; the LDS buffers are free for it
     item = __builtin_amdgcn_readfirstlane(s_item);
   }
 }
