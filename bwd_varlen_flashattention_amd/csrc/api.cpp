@@ -116,7 +116,7 @@ SchedLayout sched_layout(size_t base, int64_t max_items, int64_t groups) {
 }
 
 int64_t fwd_max_entries(const jfa_attn_params_t* p) {
-  const int bm = fwd_block_rows();
+  const int bm = fwd_block_rows(p->head_dim, p->qkv_dtype == JFA_DTYPE_FP8_E4M3);
   if (p->broadcast_q) return (int64_t)p->batch * cdiv_i(p->total_q, bm);
   return cdiv_i(p->total_q, bm) + (int64_t)p->batch;
 }
@@ -272,7 +272,7 @@ jfa_status_t jfa_fwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   sa.cu_q = cu_seqlens_q;
   sa.cu_k = cu_seqlens_k;
   sa.batch = p->batch;
-  sa.stat_tile = fwd_block_rows();
+  sa.stat_tile = fwd_block_rows(p->head_dim, p->qkv_dtype == JFA_DTYPE_FP8_E4M3);
   sa.loop_tile = bn;
   sa.mode = 0;
   sa.causal = p->causal;
@@ -302,7 +302,7 @@ jfa_status_t jfa_fwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   fa.fp8 = fp8;
   fa.v_scale = fp8 ? p->v_scale : 1.f;
   const int64_t max_items = L.max_items;
-  const int grid = (int)std::min<int64_t>((int64_t)cu_count() * fwd_blocks_per_cu(p->head_dim), max_items);
+  const int grid = (int)std::min<int64_t>((int64_t)cu_count() * fwd_blocks_per_cu(p->head_dim, fp8), max_items);
   TimedRegion tr(JFA_TIMING_FWD, stream);
   e = launch_fwd(fa, p->head_dim, std::max(grid, 1), stream);
   tr.finish();

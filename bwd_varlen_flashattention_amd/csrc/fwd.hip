@@ -44,14 +44,19 @@ namespace jfa {
 // transposed, so P V is the bf16 contraction of the bf16 path.
 template <int D, bool FP8 = false>
 struct FwdTile {
-  static constexpr int NT = 256;            // 4 waves
-  static constexpr int BM = 128;            // query rows per item (32 per wave)
   static constexpr int BN = D <= 192 ? 64 : 32;   // keys per KV tile (d = 256: 32, so nothing spills)
   static constexpr int KB = BN / 32;        // 32-key blocks per tile
   static constexpr int EB = FP8 ? 1 : 2;    // bytes per Q/K/V element in memory
   static constexpr int KP = FP8 ? D + 16 : D + 8;   // K row pitch in LDS (elements): +16 B staggers banks
   static constexpr int VTP = BN + 8;        // V^T row pitch (elements): 144 B rows at 64 keys
   static constexpr int CH = D * EB / 16;    // 16-byte chunks per K row
+  // d <= 128: one workgroup of 8 waves per CU (2 per SIMD) owning 256 query
+  // rows, so that every K/V tile brought into the CU serves 256 rows (the L2 ->
+  // CU path, not the HBM, limits the staging); otherwise 4 waves, 128 rows.
+  // d = 96 and e4m3 at d = 64 keep 4 waves: their K tile does not split evenly
+  // over 512 threads.
+  static constexpr int NT = (D <= 128 && (BN * CH) % 512 == 0) ? 512 : 256;
+  static constexpr int BM = NT / 2;         // query rows per item (32 per wave)
   static constexpr int KLOADS = BN * CH / NT;
   static constexpr int VBLOCKS = (BN / 4) * (D / 8);   // 4-key x 8-column blocks of V
   static constexpr int VPER = (VBLOCKS + NT - 1) / NT;  // V blocks per thread (2 for d > 128)
@@ -59,9 +64,9 @@ struct FwdTile {
   static constexpr int KS8 = D / 64;        // k-steps of K Q^T (e4m3)
   static constexpr int DB = D / 32;         // 32-wide output column blocks
   static constexpr int K_LDS_BYTES = BN * KP * EB;
-  // d <= 128: two workgroups per CU; larger heads need the whole register file of
-  // one wave per SIMD (Q fragment + output accumulator) and most of the LDS
-  static constexpr int WG_PER_CU = D <= 128 ? 2 : 1;
+  // 4-wave workgroups at d <= 128: two per CU; larger heads need the whole
+  // register file of one wave per SIMD (Q fragment + output accumulator)
+  static constexpr int WG_PER_CU = (NT == 256 && D <= 128) ? 2 : 1;
   static_assert(BN * CH % NT == 0, "tile load split");
   static_assert(!FP8 || D % 64 == 0, "e4m3 k-steps are 64 deep");
   static_assert(WG_PER_CU * 2 * (K_LDS_BYTES + D * VTP * 2) <= 160 * 1024, "LDS budget");
@@ -85,7 +90,7 @@ __device__ __forceinline__ int vt_quarter_pos(int q) { return ((q & 1) << 1) | (
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 
 template <int D, bool CAUSAL, bool BCAST, bool FP8>
-__global__ __launch_bounds__(256, FwdTile<D>::WG_PER_CU) void fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__((FwdTile<D, FP8>::NT), (FwdTile<D, FP8>::WG_PER_CU)) void fwd_kernel(FwdArgs a) {
   using T = FwdTile<D, FP8>;
   constexpr int BM = T::BM, BN = T::BN, KB = T::KB, KP = T::KP, VTP = T::VTP, KS = T::KS, DB = T::DB;
   constexpr int EB = T::EB;
@@ -139,6 +144,7 @@ __global__ __launch_bounds__(256, FwdTile<D>::WG_PER_CU) void fwd_kernel(FwdArgs
     const int row0 = e.t * BM;
     const int my_row = row0 + w * 32 + l32;
     const bool row_ok = my_row < lq;
+    const bool wave_rows = row0 + w * 32 < lq;   // uniform per wave
     const int off = lk - lq;                 // bottom-right causal alignment
 
     // Q fragment: B operand of S^T = K Q^T, lane holds row my_row, d-slots
@@ -248,6 +254,8 @@ __global__ __launch_bounds__(256, FwdTile<D>::WG_PER_CU) void fwd_kernel(FwdArgs
       const int buf = step & 1;
       const int j = tile_of(step);
       if (step + 1 < n_tiles) load_regs(tile_of(step + 1));
+      // a wave whose 32 rows all lie past the sequence end only stages and syncs
+      if (wave_rows) {
 
       // S^T[key][query] for the tile's 32-key blocks
       f32x16 s[KB];
@@ -321,6 +329,7 @@ __global__ __launch_bounds__(256, FwdTile<D>::WG_PER_CU) void fwd_kernel(FwdArgs
           for (int t = 0; t < 2; ++t)
             acc[db] = mfma32x32x16(*(const bf16x8*)(vp + 16 * (2 * kb + t)), pb[kb][t], acc[db]);
       }
+      }   // wave_rows
 
       if (step + 1 < n_tiles) store_lds(buf ^ 1);
       __syncthreads();
@@ -349,12 +358,13 @@ __global__ __launch_bounds__(256, FwdTile<D>::WG_PER_CU) void fwd_kernel(FwdArgs
     // hold the four 32 x D blocks, they go through LDS (free after the last tile's
     // barrier) and out 16 bytes per lane, D / 8 lanes covering one row.
     constexpr int EP = D + 8;
+    constexpr int NW = T::NT / 64;           // waves
     constexpr int VT_EL = 2 * D * VTP, K_EL = T::K_LDS_BYTES;   // stage capacities in bf16 elements
-    constexpr bool ALL_VT = 4 * 32 * EP <= VT_EL;
-    constexpr bool VIA_LDS = ALL_VT || (2 * 32 * EP <= VT_EL && 2 * 32 * EP <= K_EL);
+    constexpr bool ALL_VT = NW * 32 * EP <= VT_EL;
+    constexpr bool VIA_LDS = ALL_VT || ((NW / 2) * 32 * EP <= VT_EL && (NW / 2) * 32 * EP <= K_EL);
     if constexpr (VIA_LDS) {
-      __bf16* blk = (ALL_VT || w < 2) ? &vt_lds[0][0] + (ALL_VT ? w : (w & 1)) * 32 * EP
-                                      : (__bf16*)&k_raw[0][0] + (w & 1) * 32 * EP;
+      __bf16* blk = (ALL_VT || w < NW / 2) ? &vt_lds[0][0] + (ALL_VT ? w : w % (NW / 2)) * 32 * EP
+                                           : (__bf16*)&k_raw[0][0] + (w % (NW / 2)) * 32 * EP;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -401,11 +411,29 @@ __global__ __launch_bounds__(256, FwdTile<D>::WG_PER_CU) void fwd_kernel(FwdArgs
   }
 }
 
-int fwd_block_rows() { return FwdTile<128>::BM; }
-int fwd_kv_tile(int head_dim) { return head_dim <= 128 ? FwdTile<128>::BN : head_dim <= 192 ? FwdTile<192>::BN : FwdTile<256>::BN; }
-int fwd_blocks_per_cu(int head_dim) {
-  return head_dim <= 128 ? FwdTile<128>::WG_PER_CU : head_dim <= 192 ? FwdTile<192>::WG_PER_CU : FwdTile<256>::WG_PER_CU;
+template <bool FP8>
+static int fwd_rows_t(int head_dim) {
+  switch (head_dim) {
+    case 64: return FwdTile<64, FP8>::BM;
+    case 96: return FwdTile<96, false>::BM;
+    case 128: return FwdTile<128, FP8>::BM;
+    case 192: return FwdTile<192, FP8>::BM;
+    default: return FwdTile<256, FP8>::BM;
+  }
 }
+template <bool FP8>
+static int fwd_wgs_t(int head_dim) {
+  switch (head_dim) {
+    case 64: return FwdTile<64, FP8>::WG_PER_CU;
+    case 96: return FwdTile<96, false>::WG_PER_CU;
+    case 128: return FwdTile<128, FP8>::WG_PER_CU;
+    case 192: return FwdTile<192, FP8>::WG_PER_CU;
+    default: return FwdTile<256, FP8>::WG_PER_CU;
+  }
+}
+int fwd_block_rows(int head_dim, bool fp8) { return fp8 ? fwd_rows_t<true>(head_dim) : fwd_rows_t<false>(head_dim); }
+int fwd_kv_tile(int head_dim) { return head_dim <= 128 ? FwdTile<128>::BN : head_dim <= 192 ? FwdTile<192>::BN : FwdTile<256>::BN; }
+int fwd_blocks_per_cu(int head_dim, bool fp8) { return fp8 ? fwd_wgs_t<true>(head_dim) : fwd_wgs_t<false>(head_dim); }
 
 template <int D, bool FP8>
 static hipError_t launch_fwd_dt(const FwdArgs& a, int grid, hipStream_t stream) {

@@ -88,9 +88,9 @@ struct FwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t stream);
-int fwd_block_rows();       // BM of the forward kernel
+int fwd_block_rows(int head_dim, bool fp8);   // BM of the forward kernel
 int fwd_kv_tile(int head_dim);   // BN of the forward kernel
-int fwd_blocks_per_cu(int head_dim);
+int fwd_blocks_per_cu(int head_dim, bool fp8);
 
 // Backward.
 struct BwdPreArgs {
