@@ -127,7 +127,7 @@ int64_t dkdv_max_entries(const jfa_attn_params_t* p) {
 
 int64_t dq_max_entries(const jfa_attn_params_t* p) {
   if (p->broadcast_q) return 0;   // broadcast-Q dQ work is indexed directly
-  return cdiv_i(p->total_q, bwd_dq_rows()) + (int64_t)p->batch;
+  return cdiv_i(p->total_q, bwd_dq_rows(p->head_dim)) + (int64_t)p->batch;
 }
 
 SchedLayout fwd_list(const jfa_attn_params_t* p) {
@@ -141,7 +141,7 @@ int64_t lse_elems(const jfa_attn_params_t* p) {
 // Broadcast-Q dQ: items split into chunks, enough (query tile, head, chunk) units
 // for two per CU; each chunk owns an fp32 partial of dQ.
 int bcast_dq_chunks(const jfa_attn_params_t* p) {
-  const int64_t tiles_heads = (int64_t)cdiv_i(p->total_q, bwd_dq_rows()) * p->num_heads_q;
+  const int64_t tiles_heads = (int64_t)cdiv_i(p->total_q, bwd_dq_rows(p->head_dim)) * p->num_heads_q;
   const int64_t want = std::max<int64_t>(1, (2LL * cu_count() + tiles_heads - 1) / tiles_heads);
   const int per = cdiv_i(p->batch, std::min<int64_t>(p->batch, want));
   return cdiv_i(p->batch, per);
@@ -376,7 +376,7 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
     dq_sa.cu_q = cu_seqlens_q;
     dq_sa.cu_k = cu_seqlens_k;
     dq_sa.batch = p->batch;
-    dq_sa.stat_tile = bwd_dq_rows();
+    dq_sa.stat_tile = bwd_dq_rows(p->head_dim);
     dq_sa.loop_tile = bwd_dq_tile(p->head_dim);
     dq_sa.mode = 0;
     dq_sa.causal = p->causal;
@@ -421,7 +421,7 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
 
     // dQ: query-stationary
     if (p->broadcast_q) {
-      const int qtiles = cdiv_i(p->total_q, bwd_dq_rows());
+      const int qtiles = cdiv_i(p->total_q, bwd_dq_rows(p->head_dim));
       const int64_t tiles_heads = (int64_t)qtiles * p->num_heads_q;
       ba.bcast_chunks = L.chunks;
       ba.bcast_chunk = cdiv_i(p->batch, L.chunks);

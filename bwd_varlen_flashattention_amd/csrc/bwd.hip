@@ -445,36 +445,43 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 // ============================================================================= dQ
 template <int D>
 struct DqTile {
-  static constexpr int NT = 256;             // 4 waves, 32 query rows each
-  static constexpr int BM = 128;             // query rows per item
   // keys per tile: 32, with the LDS stage double-buffered (one barrier per tile;
   // the next tile's stores leave the critical path); d = 96 splits evenly over
   // the 256 staging threads only with 64-key tiles, of which two workgroups per
   // CU fit a single stage
   static constexpr int BN = D == 96 ? 64 : 32;
   static constexpr int NSTAGE = BN == 32 ? 2 : 1;
-  // d <= 128: two workgroups per CU; d = 192 / 256 keep Q, dO and dQ^T of the
-  // whole head in the registers of one wave per SIMD
-  static constexpr int WG_PER_CU = D <= 128 ? 2 : 1;
+  static constexpr int CH = D / 8;
+  // d = 128: one workgroup of 8 waves per CU owning 256 query rows, so that each
+  // K/V tile brought into the CU serves 256 rows (as in the forward); d = 64 /
+  // 96: two 4-wave workgroups of 128 rows (their tiles do not split over 512
+  // threads); d = 192 / 256 keep Q, dO and dQ^T of the whole head in the
+  // registers of one wave per SIMD
+  static constexpr int NT = (D <= 128 && (BN * CH) % 512 == 0) ? 512 : 256;
+  static constexpr int BM = NT / 2;          // query rows per item (32 per wave)
+  static constexpr int WG_PER_CU = (NT == 256 && D <= 128) ? 2 : 1;
   static constexpr int KP = D + 8;           // row pitch of K / V tiles
   static constexpr int KTP = BN + 8;         // row pitch of the K^T tile
-  static constexpr int CH = D / 8;
   static constexpr int VLOADS = BN * CH / NT;
   static constexpr int KBLOCKS = (BN / 4) * (D / 8);
   static constexpr int KS = D / 16;
   static constexpr int DB = D / 32;
+  static constexpr int EP = D + 8;           // row pitch of the epilogue blocks
+  // the 8-wave epilogue blocks get LDS of their own (one workgroup per CU)
+  static constexpr int EP_EL = NT == 512 ? (NT / 64) * 32 * EP : 1;
   static_assert(BN * CH % NT == 0 && KBLOCKS <= NT, "tile load split");
-  static_assert(WG_PER_CU * NSTAGE * (2 * BN * KP + D * KTP) * 2 <= 160 * 1024, "LDS budget");
+  static_assert(WG_PER_CU * (NSTAGE * (2 * BN * KP + D * KTP) + EP_EL) * 2 <= 160 * 1024, "LDS budget");
 };
 
 template <int D, bool CAUSAL, bool BCAST>
-__global__ __launch_bounds__(256, DqTile<D>::WG_PER_CU) void bwd_dq_kernel(BwdArgs a) {
+__global__ __launch_bounds__((DqTile<D>::NT), (DqTile<D>::WG_PER_CU)) void bwd_dq_kernel(BwdArgs a) {
   using T = DqTile<D>;
   constexpr int BM = T::BM, BN = T::BN, KP = T::KP, KTP = T::KTP, KS = T::KS, DB = T::DB;
   constexpr int NSTAGE = T::NSTAGE;
   __shared__ __attribute__((aligned(16))) __bf16 k_lds[NSTAGE][BN * KP];
   __shared__ __attribute__((aligned(16))) __bf16 v_lds[NSTAGE][BN * KP];
   __shared__ __attribute__((aligned(16))) __bf16 kt_lds[NSTAGE][D * KTP];
+  __shared__ __attribute__((aligned(16))) __bf16 ep_lds[T::EP_EL];
   __shared__ int s_item;
   __shared__ int s_queue[2 * kQueues];
 
@@ -498,8 +505,8 @@ __global__ __launch_bounds__(256, DqTile<D>::WG_PER_CU) void bwd_dq_kernel(BwdAr
     voff[i] = (uint32_t)(((id / T::CH) * rs + (id % T::CH) * 8) * 2);
   }
 
-  // Work: self-attention pulls (sequence, 128-row query tile, head) items from the
-  // per-XCD work queues; broadcast-Q owns (query tile, head, chunk of items) by block index.
+  // Work: self-attention pulls (sequence, query tile, head) items from the per-XCD
+  // work queues; broadcast-Q owns (query tile, head, chunk of items) by block index.
   int bcast_item = blockIdx.x;
   int home_q = blockIdx.x % kQueues, drained = 0;   // work-queue state (thread 0)
   int item = -1;
@@ -548,6 +555,7 @@ __global__ __launch_bounds__(256, DqTile<D>::WG_PER_CU) void bwd_dq_kernel(BwdAr
       if (BCAST) { lq = a.bcast_nq; q_base = 0; k_base = a.cu_k[b]; lk = a.cu_k[b + 1] - k_base; }
       else { lq = e_lq; q_base = e_qbase; k_base = e_kbase; lk = e_lk; }
       const bool row_ok = my_row < lq;
+      const bool wave_rows = row0 + w * 32 < lq;   // uniform per wave
       const int off = lk - lq;
 
       int n_tiles, n_bulk;
@@ -652,8 +660,9 @@ __global__ __launch_bounds__(256, DqTile<D>::WG_PER_CU) void bwd_dq_kernel(BwdAr
         }
         if (s + 1 < n_tiles) load_regs(tile_of(s + 1));
         const int kmax_ok = CAUSAL ? min(lk - 1, my_row + off) : lk - 1;
+        // a wave whose 32 rows all lie past the sequence end only stages and syncs
 #pragma unroll
-        for (int kb = 0; kb < BN / 32; ++kb) {
+        for (int kb = 0; kb < (wave_rows ? BN / 32 : 0); ++kb) {
           // S^T[key][q] = K Q^T and dP^T[key][q] = V dO^T for 32 keys
           f32x16 st = f32x16{}, pt = f32x16{};
           const __bf16* kp = &k_lds[stg][(32 * kb + l32) * KP + 8 * hh];
@@ -709,12 +718,14 @@ __global__ __launch_bounds__(256, DqTile<D>::WG_PER_CU) void bwd_dq_kernel(BwdAr
     }
     if (!BCAST) {
       // A lane holds 4 consecutive columns of its row per register quad; the
-      // wave's 32 x D block goes through LDS (free after the last tile's closing
-      // barrier: waves 0-1 use the K stages, 2-3 the V stages) and out 16 bytes
-      // per lane, D / 8 lanes covering one row.
-      constexpr int EP = D + 8;
-      static_assert(2 * 32 * EP <= NSTAGE * BN * KP, "epilogue blocks fit");
-      __bf16* blk = (w < 2 ? &k_lds[0][0] : &v_lds[0][0]) + (w & 1) * 32 * EP;
+      // wave's 32 x D block goes through LDS (4 waves: the stages, free after the
+      // last tile's closing barrier, waves 0-1 in the K stages and 2-3 in the V
+      // stages; 8 waves: LDS of their own) and out 16 bytes per lane, D / 8 lanes
+      // covering one row.
+      constexpr int EP = T::EP;
+      static_assert(T::NT == 512 || 2 * 32 * EP <= NSTAGE * BN * KP, "epilogue blocks fit");
+      __bf16* blk = T::NT == 512 ? &ep_lds[0] + w * 32 * EP
+                                 : (w < 2 ? &k_lds[0][0] : &v_lds[0][0]) + (w & 1) * 32 * EP;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -748,11 +759,16 @@ int bwd_dkdv_rows(int head_dim) { return head_dim <= 128 ? DkvTile<128>::BM : Dk
 int bwd_dkdv_slices(int head_dim) {
   return head_dim <= 128 ? DkvTile<128>::NC : head_dim <= 192 ? DkvTile<192>::NC : DkvTile<256>::NC;
 }
-int bwd_dq_rows() { return DqTile<128>::BM; }
-int bwd_dq_tile(int head_dim) {
-  return head_dim == 96 ? DqTile<96>::BN : head_dim <= 128 ? DqTile<128>::BN : DqTile<256>::BN;
+int bwd_dq_rows(int head_dim) {
+  return head_dim == 64 ? DqTile<64>::BM : head_dim == 96 ? DqTile<96>::BM : head_dim == 128 ? DqTile<128>::BM : DqTile<256>::BM;
 }
-int bwd_dq_blocks_per_cu(int head_dim) { return head_dim <= 128 ? DqTile<128>::WG_PER_CU : DqTile<256>::WG_PER_CU; }
+int bwd_dq_tile(int head_dim) {
+  return head_dim == 64 ? DqTile<64>::BN : head_dim == 96 ? DqTile<96>::BN : head_dim == 128 ? DqTile<128>::BN : DqTile<256>::BN;
+}
+int bwd_dq_blocks_per_cu(int head_dim) {
+  return head_dim == 64 ? DqTile<64>::WG_PER_CU : head_dim == 96 ? DqTile<96>::WG_PER_CU
+       : head_dim == 128 ? DqTile<128>::WG_PER_CU : DqTile<256>::WG_PER_CU;
+}
 
 template <int D>
 static hipError_t launch_dkdv_d(const BwdArgs& a, int grid, hipStream_t stream) {

@@ -8,14 +8,15 @@
 // customising FlashAttention-4 on B300").
 //
 // How it maps to CDNA4:
-//   * persistent workgroups pull (sequence, 128-row query tile, head) items from
-//     the per-XCD queues built by sched.hip, where the tiles sharing one K/V run
+//   * persistent workgroups pull (sequence, query tile, head) items from the
+//     per-XCD queues built by sched.hip, where the tiles sharing one K/V run
 //     back to back on one XCD and so share its L2;
-//   * 4 waves, each owning 32 query rows whose Q fragment stays in VGPRs for the
-//     whole key loop;
-//   * two workgroups per CU (two waves per SIMD) for d <= 128, so one wave's
-//     softmax VALU work overlaps the other's MFMAs; d = 192 and 256 run one
-//     workgroup per CU, whose Q fragment and accumulator fill a SIMD's registers;
+//   * waves of 32 query rows whose Q fragment stays in VGPRs for the whole key
+//     loop; two waves per SIMD for d <= 128 (one 8-wave workgroup of 256 rows
+//     per CU, or two 4-wave ones of 128 rows where the K tile does not split
+//     over 512 threads), so one wave's softmax VALU work overlaps the other's
+//     MFMAs; d = 192 and 256 run one 4-wave workgroup per CU, whose Q fragment
+//     and accumulator fill a SIMD's registers;
 //   * K/V tiles of 64 keys are double-buffered in LDS: the global loads of tile
 //     j+1 are in flight while tile j is consumed;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 so each lane owns one query column:

@@ -137,7 +137,7 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int grid, hipStream_t s
 int bwd_dkdv_tile();                       // keys per dK/dV item
 int bwd_dkdv_rows(int head_dim);           // query rows per dK/dV step
 int bwd_dkdv_slices(int head_dim);         // head-dim slices (dK/dV items) per key tile
-int bwd_dq_rows();                         // query rows per dQ item
+int bwd_dq_rows(int head_dim);              // query rows per dQ item
 int bwd_dq_tile(int head_dim);             // keys per dQ tile
 int bwd_dq_blocks_per_cu(int head_dim);    // resident dQ workgroups per CU
 
