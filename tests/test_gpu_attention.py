@@ -95,6 +95,19 @@ def test_ragged(jfa, d, causal, hq, hkv):
     _compare_full(_run_self(jfa, inp), _oracle_self(inp))
 
 
+# Lengths around the 256-row query tiles of the 8-wave forward / dQ workgroups (d = 64, 128):
+# every count of waves past the sequence end (0..7) occurs in some tile.
+WIDE_TILE = [255, 256, 257, 288, 289, 320, 352, 384, 416, 448, 480, 511, 512, 513, 40]
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_wide_query_tiles(jfa, d, causal):
+    inp = workloads.jagged(300 + d, WIDE_TILE, None, 4, 2, d, causal)
+    _say(f"wide tiles d={d} causal={causal}")
+    _compare_full(_run_self(jfa, inp), _oracle_self(inp))
+
+
 def test_cross_lengths_bottom_right_causal(jfa):
     """Lq != Lk per sequence, causal aligned bottom-right (rows with no key get O=0, LSE=-inf)."""
     lq = [5, 130, 64, 1, 77, 300]
