@@ -202,6 +202,7 @@ def _oracle_bcast(inp):
     (37, [5, 0, 64, 129, 1], 2, 2),
     (256, [300, 17, 0, 128, 64, 1000, 3], 4, 4),
     (130, [70, 70, 200], 4, 2),
+    (300, [33, 0, 257, 512], 2, 1),   # a second 256-row query tile with 44 rows
 ])
 def test_broadcast_q(jfa, nq, lengths, hq, hkv):
     inp = workloads.broadcast(3, nq, lengths, hq, hkv, 128)
