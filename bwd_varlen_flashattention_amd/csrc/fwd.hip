@@ -65,12 +65,20 @@ struct FwdTile {
   static constexpr int KS8 = D / 64;        // k-steps of K Q^T (e4m3)
   static constexpr int DB = D / 32;         // 32-wide output column blocks
   static constexpr int K_LDS_BYTES = BN * KP * EB;
+  // epilogue: each wave's 32 x D output block goes through LDS.  The K and V^T
+  // stages hold them except for e4m3 with 8 waves (a smaller K stage); that case
+  // has LDS of its own (one workgroup per CU).
+  static constexpr int NW = NT / 64;
+  static constexpr int EP = D + 8;
+  static constexpr bool EP_ALL_VT = NW * 32 * EP <= 2 * D * VTP;
+  static constexpr bool EP_SPLIT = (NW / 2) * 32 * EP <= 2 * D * VTP && (NW / 2) * 32 * EP <= K_LDS_BYTES;
+  static constexpr int EP_OWN = (!EP_ALL_VT && !EP_SPLIT && NT == 512) ? NW * 32 * EP : 1;
   // 4-wave workgroups at d <= 128: two per CU; larger heads need the whole
   // register file of one wave per SIMD (Q fragment + output accumulator)
   static constexpr int WG_PER_CU = (NT == 256 && D <= 128) ? 2 : 1;
   static_assert(BN * CH % NT == 0, "tile load split");
   static_assert(!FP8 || D % 64 == 0, "e4m3 k-steps are 64 deep");
-  static_assert(WG_PER_CU * 2 * (K_LDS_BYTES + D * VTP * 2) <= 160 * 1024, "LDS budget");
+  static_assert(WG_PER_CU * (2 * (K_LDS_BYTES + D * VTP * 2) + 2 * EP_OWN) <= 160 * 1024, "LDS budget");
 };
 
 typedef int i32x8 __attribute__((ext_vector_type(8)));
@@ -97,6 +105,7 @@ __global__ __launch_bounds__((FwdTile<D, FP8>::NT), (FwdTile<D, FP8>::WG_PER_CU)
   constexpr int EB = T::EB;
   __shared__ __attribute__((aligned(16))) unsigned char k_raw[2][T::K_LDS_BYTES];
   __shared__ __attribute__((aligned(16))) __bf16 vt_lds[2][D * VTP];
+  __shared__ __attribute__((aligned(16))) __bf16 ep_lds[T::EP_OWN];
   __shared__ int s_item;
   __shared__ int s_queue[2 * kQueues];
 
@@ -355,16 +364,16 @@ __global__ __launch_bounds__((FwdTile<D, FP8>::NT), (FwdTile<D, FP8>::WG_PER_CU)
       return BCAST ? a.o + (((int64_t)b * lq + r) * a.hq + h) * D : a.o + ((int64_t)(q_base + r) * a.hq + h) * D;
     };
     // A lane holds 4 consecutive columns of its row per register quad, so direct
-    // stores write 32 rows in 8-byte pieces per instruction.  Where the stages
-    // hold the four 32 x D blocks, they go through LDS (free after the last tile's
-    // barrier) and out 16 bytes per lane, D / 8 lanes covering one row.
-    constexpr int EP = D + 8;
-    constexpr int NW = T::NT / 64;           // waves
-    constexpr int VT_EL = 2 * D * VTP, K_EL = T::K_LDS_BYTES;   // stage capacities in bf16 elements
-    constexpr bool ALL_VT = NW * 32 * EP <= VT_EL;
-    constexpr bool VIA_LDS = ALL_VT || ((NW / 2) * 32 * EP <= VT_EL && (NW / 2) * 32 * EP <= K_EL);
+    // stores write 32 rows in 8-byte pieces per instruction.  The waves' 32 x D
+    // blocks go through LDS instead (the stages, free after the last tile's
+    // barrier, or LDS of their own, see FwdTile) and out 16 bytes per lane, D / 8
+    // lanes covering one row; direct stores remain only where neither fits.
+    constexpr int EP = T::EP, NW = T::NW;
+    constexpr bool ALL_VT = T::EP_ALL_VT, OWN = T::EP_OWN > 1;
+    constexpr bool VIA_LDS = ALL_VT || T::EP_SPLIT || OWN;
     if constexpr (VIA_LDS) {
-      __bf16* blk = (ALL_VT || w < NW / 2) ? &vt_lds[0][0] + (ALL_VT ? w : w % (NW / 2)) * 32 * EP
+      __bf16* blk = OWN ? &ep_lds[0] + w * 32 * EP
+                  : (ALL_VT || w < NW / 2) ? &vt_lds[0][0] + (ALL_VT ? w : w % (NW / 2)) * 32 * EP
                                            : (__bf16*)&k_raw[0][0] + (w % (NW / 2)) * 32 * EP;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
