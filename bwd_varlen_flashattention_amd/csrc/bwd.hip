@@ -242,9 +242,29 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     const int n_qt = (CAUSAL && max(0, kt0 - off) >= lq) ? 0 : ntq - i_first;
     const int n_steps = n_qt * a.group;
 
-    // K/V fragments for this wave's 32 keys: B operands of S = Q K^T and dP = dO V^T
+    // K/V fragments for this wave's 32 keys: B operands of S = Q K^T and dP = dO V^T.
+    // Up to d = 128 the rows are loaded whole (D / 8 lanes per row, rows past Lk
+    // read as zero through the buffer range) and moved into the fragment layout
+    // through LDS stage 1, which the item's first tile leaves alone; a fragment
+    // load would touch 32 rows per instruction.
     bf16x8 kf[KS], vf[KS];
-    {
+    constexpr bool KV_VIA_LDS = D <= 128;
+    constexpr int KV_CPR = D / 8, KV_PER = 32 * KV_CPR / 64;   // 16-byte chunks per row / per lane
+    u32x4 kraw[KV_VIA_LDS ? KV_PER : 1], vraw[KV_VIA_LDS ? KV_PER : 1];
+    if constexpr (KV_VIA_LDS) {
+      const int key0 = kt0 + 32 * w;
+      const uint32_t nbytes = (uint32_t)(max(0, min(32, lk - key0)) * a.hkv * D * 2);
+      const int64_t off0 = ((int64_t)(k_base + key0) * a.hkv + g) * D;
+      const auto krs = uniform_rsrc(a.k + off0, nbytes);
+      const auto vrs = uniform_rsrc(a.v + off0, nbytes);
+#pragma unroll
+      for (int i = 0; i < KV_PER; ++i) {
+        const int id = lane + 64 * i, row = id / KV_CPR, col = id % KV_CPR;
+        const uint32_t voff = (uint32_t)((row * a.hkv * D + 8 * col) * 2);
+        kraw[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, voff, 0, 0));
+        vraw[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(vrs, voff, 0, 0));
+      }
+    } else {
       const int64_t base = ((int64_t)(k_base + min(my_key, lk - 1)) * a.hkv + g) * D + 8 * hh;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
@@ -387,10 +407,30 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     };
 
     if (n_steps > 0) {
-      load_regs(0);   // in flight together with the K/V fragments: one round trip
+      load_regs(0);   // in flight together with the K/V rows: one round trip
       wait_vmem_all();
-      store_lds(0);
-      __syncthreads();
+      if constexpr (KV_VIA_LDS) {
+        // wave w's K and V blocks (32 rows, pitch D + 8) in one stage-1 array
+        constexpr int EP = D + 8;
+        static_assert(2 * 32 * EP <= BM * QP && 2 * 32 * EP <= DC * QTP, "K/V blocks fit a stage");
+        __bf16* kvb = w == 0 ? &q_lds[1][0] : w == 1 ? &do_lds[1][0] : w == 2 ? &qt_lds[1][0] : &dot_lds[1][0];
+#pragma unroll
+        for (int i = 0; i < KV_PER; ++i) {
+          const int id = lane + 64 * i, row = id / KV_CPR, col = id % KV_CPR;
+          *(u32x4*)(kvb + row * EP + 8 * col) = kraw[i];
+          *(u32x4*)(kvb + (32 + row) * EP + 8 * col) = vraw[i];
+        }
+        store_lds(0);
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          kf[ks] = *(const bf16x8*)(kvb + l32 * EP + 16 * ks + 8 * hh);
+          vf[ks] = *(const bf16x8*)(kvb + (32 + l32) * EP + 16 * ks + 8 * hh);
+        }
+      } else {
+        store_lds(0);
+        __syncthreads();
+      }
       // causal masking is one compare per element in every step: a single step
       // body keeps the register allocation of the causal kernel free of spills
       for (int s = 0; s < n_steps; ++s) step(s);
