@@ -209,14 +209,32 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   const int l32 = lane & 31, hh = lane >> 5;
   const float INF = __builtin_inff();
 
-  // staging: thread owns rows 4*sq..4*sq+3, columns 8*sd..8*sd+7 of the Q and dO tiles
+  // Staging.  Up to d = 128 (64-row steps) a thread owns 8 rows x 8 columns of
+  // one tile (threads 0-127 Q, 128-255 dO): rows 16*(sq/2) + 4*(sq%2) + {0-3,
+  // 8-11}, the two quarters an S/dP accumulator hands one lane half, so each
+  // transposed column is 16 contiguous bytes and every LDS store is b128 (16 per
+  // thread instead of 8 b128 + 16 b64).  Bank map: transposed stores need sq
+  // distinct in each 8-lane group (sq = thread bits 0-2); row-major stores need
+  // 4*(sq%2) + sd distinct mod 8, which sd gets from bits 0-2 xor 3-5 plus
+  // 4*(sq%2) (bit 6 gives its high half).  Above d = 128 (32-row steps) a thread
+  // owns rows 4*sq..4*sq+3 of both tiles.
+  constexpr bool ST8 = D <= 128;
   int sq, sd;
-  staging_block(tid, BM / 4, sq, sd);
+  const int ts = ST8 ? __builtin_amdgcn_readfirstlane(tid >> 7) : 0;   // staged tile (8-row map)
+  if constexpr (ST8) {
+    static_assert(BM == 64, "8-row staging map covers 64 rows");
+    const int lt = tid & 127;
+    sq = lt & 7;
+    sd = ((((sq ^ (lt >> 3)) & 7) + 4 * (sq & 1)) & 7) | ((lt >> 6) << 3);
+  } else {
+    staging_block(tid, BM / 4, sq, sd);
+  }
   const bool stager = sd < D / 8;
   const int qrs = a.hq * D;                           // elements between query rows
-  uint32_t qoff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) qoff[i] = (uint32_t)(((4 * sq + i) * qrs + 8 * sd) * 2);
+  const int srow0 = ST8 ? 16 * (sq >> 1) + 4 * (sq & 1) : 4 * sq;   // first staged row
+  const uint32_t qoff = (uint32_t)((srow0 * qrs + 8 * sd) * 2);   // byte offsets stay in the
+  // vector offset: the buffer range check that zeroes rows past Lq covers only that
+  auto srow = [&](int i) { return ST8 ? (i & 3) + 8 * (i >> 2) : i; };   // row of register i - srow0
 
   int home_q = blockIdx.x % kQueues, drained = 0;   // work-queue state (thread 0)
   load_queues(a.queues, s_queue);
@@ -285,7 +303,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       const int u = s + rot;
       return u >= n_steps ? u - n_steps : u;
     };
-    u32x4 qr[4], dr[4];
+    u32x4 sr[8];   // staged rows: 8 rows of one tile, or 4 rows of Q then 4 of dO
     // LSE and delta travel raw (range-checked buffer loads) and are only looked
     // at when they are written to LDS: consuming them right after the load would
     // make the in-order vmcnt wait cover this step's Q/dO prefetch as well.
@@ -312,26 +330,53 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       const auto qrsrc = uniform_rsrc(qb, nbytes);
       const auto orsrc = uniform_rsrc(ob, nbytes);
       if (stager) {
+        if constexpr (ST8) {
+          const auto rs = ts == 0 ? qrsrc : orsrc;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          qr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrsrc, qoff[i], 0, 0));
-          dr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(orsrc, qoff[i], 0, 0));
+          for (int i = 0; i < 8; ++i)
+            sr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, qoff + (uint32_t)(srow(i) * qrs * 2), 0, 0));
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sr[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(qrsrc, qoff + (uint32_t)(i * qrs * 2), 0, 0));
+            sr[4 + i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(orsrc, qoff + (uint32_t)(i * qrs * 2), 0, 0));
+          }
         }
       }
     };
     auto store_lds = [&](int buf) {
       if (stager) {
+        if constexpr (ST8) {
+          __bf16* rm = ts == 0 ? &q_lds[buf][0] : &do_lds[buf][0];
+          __bf16* tr = ts == 0 ? &qt_lds[buf][0] : &dot_lds[buf][0];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          *(u32x4*)&q_lds[buf][(4 * sq + i) * QP + 8 * sd] = qr[i];
-          *(u32x4*)&do_lds[buf][(4 * sq + i) * QP + 8 * sd] = dr[i];
-        }
-        // the transposed tiles hold the owned slice only (whole 8-column blocks)
-        const int col = 16 * (sq >> 2) + 4 * quarter_pos(sq & 3);
-        const int trow = 8 * sd - c0;
-        if (trow >= 0 && trow < DC) {
-          store_transposed_4x8(&qt_lds[buf][trow * QTP + col], QTP, qr);
-          store_transposed_4x8(&dot_lds[buf][trow * QTP + col], QTP, dr);
+          for (int i = 0; i < 8; ++i) *(u32x4*)&rm[(srow0 + srow(i)) * QP + 8 * sd] = sr[i];
+          // column c of the block: its 8 values in register order, at transposed
+          // row 8*sd + c, columns 16*(sq/2) + 8*(sq%2) + 0..7
+          __bf16* tp = &tr[(8 * sd) * QTP + 8 * sq];
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const uint32_t sel = (c & 1) ? 0x07060302u : 0x05040100u;
+            u32x4 col;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) col[j] = __builtin_amdgcn_perm(sr[2 * j + 1][c >> 1], sr[2 * j][c >> 1], sel);
+            *(u32x4*)(tp + c * QTP) = col;
+          }
+        } else {
+          const u32x4 qr[4] = {sr[0], sr[1], sr[2], sr[3]};
+          const u32x4 dr[4] = {sr[4], sr[5], sr[6], sr[7]};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            *(u32x4*)&q_lds[buf][(4 * sq + i) * QP + 8 * sd] = qr[i];
+            *(u32x4*)&do_lds[buf][(4 * sq + i) * QP + 8 * sd] = dr[i];
+          }
+          // the transposed tiles hold the owned slice only (whole 8-column blocks)
+          const int col = 16 * (sq >> 2) + 4 * quarter_pos(sq & 3);
+          const int trow = 8 * sd - c0;
+          if (trow >= 0 && trow < DC) {
+            store_transposed_4x8(&qt_lds[buf][trow * QTP + col], QTP, qr);
+            store_transposed_4x8(&dot_lds[buf][trow * QTP + col], QTP, dr);
+          }
         }
       }
       if (tid < BM) {
