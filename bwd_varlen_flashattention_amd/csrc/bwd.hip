@@ -472,6 +472,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
           kf[ks] = *(const bf16x8*)(kvb + l32 * EP + 16 * ks + 8 * hh);
           vf[ks] = *(const bf16x8*)(kvb + (32 + l32) * EP + 16 * ks + 8 * hh);
         }
+        __syncthreads();   // every wave holds its fragments before step 0 restages stage 1
       } else {
         store_lds(0);
         __syncthreads();
