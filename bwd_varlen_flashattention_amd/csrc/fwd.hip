@@ -421,6 +421,12 @@ __global__ __launch_bounds__((FwdTile<D, FP8>::NT), (FwdTile<D, FP8>::WG_PER_CU)
   }
 }
 
+// The causal instantiations are compiled in a unit of their own (fwd_causal.hip
+// includes this file with JFA_FWD_CAUSAL_TU defined) under LLVM's iterative ILP
+// scheduler, which suits long causal rows; this unit keeps the latency-first
+// scheduler, which suits short non-causal rows.  No instantiation is emitted by
+// both units.
+#ifndef JFA_FWD_CAUSAL_TU
 template <bool FP8>
 static int fwd_rows_t(int head_dim) {
   switch (head_dim) {
@@ -451,7 +457,7 @@ static hipError_t launch_fwd_dt(const FwdArgs& a, int grid, hipStream_t stream) 
   if (a.bcast_nq > 0)
     hipLaunchKernelGGL((fwd_kernel<D, false, true, FP8>), g, blk, 0, stream, a);
   else if (a.causal)
-    hipLaunchKernelGGL((fwd_kernel<D, true, false, FP8>), g, blk, 0, stream, a);
+    return launch_fwd_causal(a, D, FP8, grid, stream);   // instantiated in fwd_causal.hip
   else
     hipLaunchKernelGGL((fwd_kernel<D, false, false, FP8>), g, blk, 0, stream, a);
   return hipGetLastError();
@@ -477,5 +483,24 @@ hipError_t launch_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t stre
     default: return hipErrorInvalidValue;
   }
 }
+
+#else
+template <int D, bool FP8>
+static hipError_t launch_fwd_causal_dt(const FwdArgs& a, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((fwd_kernel<D, true, false, FP8>), dim3(grid), dim3(FwdTile<D, FP8>::NT), 0, stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_causal(const FwdArgs& a, int head_dim, bool fp8, int grid, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return fp8 ? launch_fwd_causal_dt<64, true>(a, grid, stream) : launch_fwd_causal_dt<64, false>(a, grid, stream);
+    case 96: return fp8 ? hipErrorInvalidValue : launch_fwd_causal_dt<96, false>(a, grid, stream);
+    case 128: return fp8 ? launch_fwd_causal_dt<128, true>(a, grid, stream) : launch_fwd_causal_dt<128, false>(a, grid, stream);
+    case 192: return fp8 ? launch_fwd_causal_dt<192, true>(a, grid, stream) : launch_fwd_causal_dt<192, false>(a, grid, stream);
+    case 256: return fp8 ? launch_fwd_causal_dt<256, true>(a, grid, stream) : launch_fwd_causal_dt<256, false>(a, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+#endif
 
 }  // namespace jfa
