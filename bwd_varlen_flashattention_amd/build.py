@@ -17,18 +17,18 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libjfa.so")
-SOURCES = ["api.cpp", "sched.hip", "fwd.hip", "fwd_causal.hip", "bwd.hip", "decode.hip"]
+SOURCES = ["api.cpp", "sched.hip", "fwd.hip", "fwd_ilp.hip", "bwd.hip", "decode.hip"]
 ARCH = "gfx950"
 # Per-source code-generation options.  The backward's key-stationary kernel runs
 # one wave per SIMD, so its LDS reads must be issued well ahead of the MFMAs that
 # consume them; LLVM's iterative ILP scheduler does that (about 20% faster there).
-# The forward takes the latency-first scheduler for its non-causal and
-# broadcast-Q kernels (3% faster on short sequences than the iterative one) and
-# the iterative ILP scheduler for its causal kernels, built from the same source
-# in a unit of their own (3.5% faster on long causal rows).
+# The forward's kernels are split over two units built from the same source:
+# the latency-first scheduler for d <= 96 and the non-causal d = 128 kernels
+# (3-7% faster there), the iterative ILP scheduler for the causal d = 128 and
+# all d >= 192 kernels (3-13% faster there).
 EXTRA_FLAGS = {"bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
                "fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
-               "fwd_causal.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
+               "fwd_ilp.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
 
 def _hipcc() -> str:

@@ -421,12 +421,15 @@ __global__ __launch_bounds__((FwdTile<D, FP8>::NT), (FwdTile<D, FP8>::WG_PER_CU)
   }
 }
 
-// The causal instantiations are compiled in a unit of their own (fwd_causal.hip
-// includes this file with JFA_FWD_CAUSAL_TU defined) under LLVM's iterative ILP
-// scheduler, which suits long causal rows; this unit keeps the latency-first
-// scheduler, which suits short non-causal rows.  No instantiation is emitted by
-// both units.
-#ifndef JFA_FWD_CAUSAL_TU
+// Scheduling units.  LLVM's iterative ILP scheduler suits the long-row kernels
+// (causal at d = 128: 3-4 % faster; every kernel at d >= 192: 9-13 % faster)
+// and the latency-first one the rest (non-causal d = 128: 3 % faster; d = 64:
+// 2-7 % faster; d = 96: equal), measured in interleaved runs.  The first group
+// is instantiated only by fwd_ilp.hip (this file included with JFA_FWD_ILP_UNIT
+// defined), the second only here, so no kernel is emitted by both units.
+constexpr bool fwd_in_ilp_unit(int d, bool causal) { return d >= 192 || (causal && d == 128); }
+
+#ifndef JFA_FWD_ILP_UNIT
 template <bool FP8>
 static int fwd_rows_t(int head_dim) {
   switch (head_dim) {
@@ -453,13 +456,16 @@ int fwd_blocks_per_cu(int head_dim, bool fp8) { return fp8 ? fwd_wgs_t<true>(hea
 
 template <int D, bool FP8>
 static hipError_t launch_fwd_dt(const FwdArgs& a, int grid, hipStream_t stream) {
+  if (fwd_in_ilp_unit(D, a.causal && a.bcast_nq == 0)) return launch_fwd_ilp(a, D, FP8, grid, stream);
   const dim3 g(grid), blk(FwdTile<D, FP8>::NT);
-  if (a.bcast_nq > 0)
-    hipLaunchKernelGGL((fwd_kernel<D, false, true, FP8>), g, blk, 0, stream, a);
-  else if (a.causal)
-    return launch_fwd_causal(a, D, FP8, grid, stream);   // instantiated in fwd_causal.hip
-  else
-    hipLaunchKernelGGL((fwd_kernel<D, false, false, FP8>), g, blk, 0, stream, a);
+  if constexpr (!fwd_in_ilp_unit(D, false)) {
+    if (a.bcast_nq > 0)
+      hipLaunchKernelGGL((fwd_kernel<D, false, true, FP8>), g, blk, 0, stream, a);
+    else if (a.causal) {
+      if constexpr (!fwd_in_ilp_unit(D, true)) hipLaunchKernelGGL((fwd_kernel<D, true, false, FP8>), g, blk, 0, stream, a);
+    } else
+      hipLaunchKernelGGL((fwd_kernel<D, false, false, FP8>), g, blk, 0, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -486,18 +492,27 @@ hipError_t launch_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t stre
 
 #else
 template <int D, bool FP8>
-static hipError_t launch_fwd_causal_dt(const FwdArgs& a, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((fwd_kernel<D, true, false, FP8>), dim3(grid), dim3(FwdTile<D, FP8>::NT), 0, stream, a);
+static hipError_t launch_fwd_ilp_dt(const FwdArgs& a, int grid, hipStream_t stream) {
+  const dim3 g(grid), blk(FwdTile<D, FP8>::NT);
+  const bool causal = a.causal && a.bcast_nq == 0;
+  if (!fwd_in_ilp_unit(D, causal)) return hipErrorInvalidValue;
+  if constexpr (fwd_in_ilp_unit(D, false)) {
+    if (a.bcast_nq > 0)
+      hipLaunchKernelGGL((fwd_kernel<D, false, true, FP8>), g, blk, 0, stream, a);
+    else if (!causal)
+      hipLaunchKernelGGL((fwd_kernel<D, false, false, FP8>), g, blk, 0, stream, a);
+  }
+  if constexpr (fwd_in_ilp_unit(D, true)) {
+    if (causal) hipLaunchKernelGGL((fwd_kernel<D, true, false, FP8>), g, blk, 0, stream, a);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_causal(const FwdArgs& a, int head_dim, bool fp8, int grid, hipStream_t stream) {
+hipError_t launch_fwd_ilp(const FwdArgs& a, int head_dim, bool fp8, int grid, hipStream_t stream) {
   switch (head_dim) {
-    case 64: return fp8 ? launch_fwd_causal_dt<64, true>(a, grid, stream) : launch_fwd_causal_dt<64, false>(a, grid, stream);
-    case 96: return fp8 ? hipErrorInvalidValue : launch_fwd_causal_dt<96, false>(a, grid, stream);
-    case 128: return fp8 ? launch_fwd_causal_dt<128, true>(a, grid, stream) : launch_fwd_causal_dt<128, false>(a, grid, stream);
-    case 192: return fp8 ? launch_fwd_causal_dt<192, true>(a, grid, stream) : launch_fwd_causal_dt<192, false>(a, grid, stream);
-    case 256: return fp8 ? launch_fwd_causal_dt<256, true>(a, grid, stream) : launch_fwd_causal_dt<256, false>(a, grid, stream);
+    case 128: return fp8 ? launch_fwd_ilp_dt<128, true>(a, grid, stream) : launch_fwd_ilp_dt<128, false>(a, grid, stream);
+    case 192: return fp8 ? launch_fwd_ilp_dt<192, true>(a, grid, stream) : launch_fwd_ilp_dt<192, false>(a, grid, stream);
+    case 256: return fp8 ? launch_fwd_ilp_dt<256, true>(a, grid, stream) : launch_fwd_ilp_dt<256, false>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -88,8 +88,8 @@ struct FwdArgs {
 };
 
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t stream);
-// causal forward (compiled in its own unit; called by launch_fwd)
-hipError_t launch_fwd_causal(const FwdArgs& a, int head_dim, bool fp8, int grid, hipStream_t stream);
+// forward kernels of the iterative-ILP unit (causal d = 128, all d >= 192); called by launch_fwd
+hipError_t launch_fwd_ilp(const FwdArgs& a, int head_dim, bool fp8, int grid, hipStream_t stream);
 int fwd_block_rows(int head_dim, bool fp8);   // BM of the forward kernel
 int fwd_kv_tile(int head_dim);   // BN of the forward kernel
 int fwd_blocks_per_cu(int head_dim, bool fp8);
