@@ -2,15 +2,17 @@
 """Throughput of the jagged attention hot path on one MI355X.
 
 One step = one pass of the whole path over resident synthetic inputs:
-  * jagged forward + backward on the GEM workload (256 sequences, max_len 1024,
-    sparsity 0.5, 8 heads, d = 128, bf16, non-causal): work-list build,
-    forward, backward preprocess, backward, dQ convert;
+  * jagged forward + backward on the dense causal workload (4 sequences of
+    8192 tokens, 32 heads, d = 128, bf16, causal): work-list build, forward,
+    backward (dQ with delta, dK/dV);
   * split-KV paged decode on the decode workload (B = 32, Hq 32 / Hkv 8,
     d = 128, KV lengths U{4096..16384}, page size 16, automatic splits) with
     its LSE-weighted combine.
-`value` is the useful (unpadded) fwd+bwd TFLOP/s: 4*d*Hq*pairs + 10*d*Hq*pairs
-over the fwd+bwd time, pairs = sum_b Lq_b*Lk_b.  The decode rate is reported
-beside it in TB/s of algorithmic HBM bytes.
+`value` is the useful (unpadded) fwd+bwd TFLOP/s of the dense causal part:
+4*d*Hq*pairs + 10*d*Hq*pairs over its fwd+bwd time, pairs = visible
+query-key pairs.  The decode rate is reported beside it in TB/s of
+algorithmic HBM bytes, and the GEM (sparsity 0.5) and broadcast-Q (sparsity
+0.5) jagged workloads as extra keys, timed after the steps.
 
 Prints ONE JSON line.  --sweep prints one extra line per workload instead.
 """
@@ -66,6 +68,8 @@ def dev(x, torch):
 
 
 class JaggedCase:
+    """One jagged workload resident on the GPU, with outputs and workspaces allocated once."""
+
     def __init__(self, torch, jfa, inp=None, bcast=None):
         self.torch, self.jfa = torch, jfa
         self.bcast = bcast is not None
@@ -77,27 +81,35 @@ class JaggedCase:
         self.causal = False if self.bcast else x.causal
         self.mq = x.q.shape[0] if self.bcast else x.max_len_q
         self.mk = x.max_len_k
-        d, hq = x.q.shape[2], x.q.shape[1]
+        self.d, self.hq = x.q.shape[2], x.q.shape[1]
         self.pairs = pairs_of(None if self.bcast else x.cu_q, x.cu_k, self.causal, x.q.shape[0] if self.bcast else None)
-        self.fwd_flops = 4.0 * d * hq * self.pairs
-        self.bwd_flops = 10.0 * d * hq * self.pairs
+        self.fwd_flops = 4.0 * self.d * self.hq * self.pairs
+        self.bwd_flops = 10.0 * self.d * self.hq * self.pairs
+        # Algorithmic flops per launch of each main kernel (per visible query-key pair, times Hq):
+        #   fwd       4d  (S = Q K^T, O = P V)
+        #   bwd_dkdv  8d  (S recomputed, dP, dV, dK: the backward's contractions except dQ)
+        #   bwd_dq    2d  (dQ = dS K; its own S/dP recomputation is not counted)
+        u = self.d * self.hq * self.pairs
+        self.kernel_flops = {"fwd": 4.0 * u, "bwd_dkdv": 8.0 * u, "bwd_dq": 2.0 * u}
+        sizes = (self.q, self.k, self.ck, self.mq, self.mk, self.causal, self.bcast)
+        self.ws_f = torch.empty(max(1, jfa.jfa_fwd_workspace_size(*sizes)), dtype=torch.uint8, device="cuda")
+        self.ws_b = torch.empty(max(1, jfa.jfa_bwd_workspace_size(*sizes)), dtype=torch.uint8, device="cuda")
         self.o, self.lse = jfa.jfa_fwd(self.q, self.k, self.v, self.cq, self.ck, self.mq, self.mk, self.causal,
-                                       broadcast_q=self.bcast)
+                                       broadcast_q=self.bcast, workspace=self.ws_f)
         self.dq, self.dk, self.dv = (torch.empty_like(t) for t in (self.q, self.k, self.v))
-        from bwd_varlen_flashattention_amd import _lib
-        import ctypes
-        p = jfa._attn_params(self.q, self.k, self.cq, self.ck, self.mq, self.mk, self.causal, None, self.bcast,
-                             self.ck.numel() - 1)
-        lib = _lib.load()
-        self.ws_f = torch.empty(max(1, lib.jfa_fwd_workspace_size(ctypes.byref(p))), dtype=torch.uint8, device="cuda")
-        self.ws_b = torch.empty(max(1, lib.jfa_bwd_workspace_size(ctypes.byref(p))), dtype=torch.uint8, device="cuda")
 
-    def step(self):
-        j = self.jfa
-        j.jfa_fwd(self.q, self.k, self.v, self.cq, self.ck, self.mq, self.mk, self.causal, broadcast_q=self.bcast,
-                  out=self.o, lse=self.lse, workspace=self.ws_f)
-        j.jfa_bwd(self.q, self.k, self.v, self.o, self.lse, self.do, self.cq, self.ck, self.mq, self.mk, self.causal,
-                  broadcast_q=self.bcast, dq=self.dq, dk=self.dk, dv=self.dv, workspace=self.ws_b)
+    def fwd(self, events=None):
+        self.jfa.jfa_fwd(self.q, self.k, self.v, self.cq, self.ck, self.mq, self.mk, self.causal,
+                         broadcast_q=self.bcast, out=self.o, lse=self.lse, workspace=self.ws_f, events=events)
+
+    def bwd(self, events=None):
+        self.jfa.jfa_bwd(self.q, self.k, self.v, self.o, self.lse, self.do, self.cq, self.ck, self.mq, self.mk,
+                         self.causal, broadcast_q=self.bcast, dq=self.dq, dk=self.dk, dv=self.dv,
+                         workspace=self.ws_b, events=events)
+
+    def step(self, events=None):
+        self.fwd(events)
+        self.bwd(events)
 
 
 class DecodeCase:
@@ -114,21 +126,33 @@ class DecodeCase:
         self.splits = splits
         self.nsplits = jfa.jfa_decode_num_splits(self.q, self.kc, self.pt, splits)
         self.bytes = decode_bytes(inp)
-        self.o, self.lse = jfa.jfa_decode_paged(self.q, self.kc, self.vc, self.pt, self.sl, splits, causal=causal)
-        import ctypes
-        from bwd_varlen_flashattention_amd import _lib
-        p = jfa._decode_params(self.q, self.kc, self.pt, splits, None, causal)
-        n = _lib.load().jfa_decode_workspace_size(ctypes.byref(p))
+        n = jfa.jfa_decode_workspace_size(self.q, self.kc, self.pt, splits)
         self.ws = torch.empty(max(1, n), dtype=torch.uint8, device="cuda")
+        self.o, self.lse = jfa.jfa_decode_paged(self.q, self.kc, self.vc, self.pt, self.sl, splits, causal=causal,
+                                                workspace=self.ws)
 
-    def step(self):
+    def step(self, events=None):
         self.jfa.jfa_decode_paged(self.q, self.kc, self.vc, self.pt, self.sl, self.splits, out=self.o, lse=self.lse,
-                                  workspace=self.ws, causal=self.causal)
+                                  workspace=self.ws, causal=self.causal, events=events)
 
 
-TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_gem_s0.5_bench_step.txt")
-KERNEL_SLOTS = (("bwd_dkdv_kernel", "bwd_dkdv"), ("bwd_dq_kernel", "bwd_dq"), ("fwd_kernel", "fwd"),
-                ("decode_kernel", "decode"))
+# ----------------------------------------------------------------------------- stored counter data
+KERNEL_SLOTS = ("fwd", "bwd_dq", "bwd_dkdv", "decode")
+# kernel name prefixes of the slots
+SLOT_KERNEL = {"fwd": "fwd_kernel", "bwd_dq": "bwd_dq_kernel", "bwd_dkdv": "bwd_dkdv_kernel", "decode": "decode_kernel"}
+# template arguments that tell the bench step's workloads apart (head dim, causal, broadcast[, fp8])
+WORKLOAD_KERNELS = {
+    "dense_causal_d128": {"fwd": "fwd_kernel<128, true, false, false>", "bwd_dq": "bwd_dq_kernel<128, true, false>",
+                          "bwd_dkdv": "bwd_dkdv_kernel<128, true, false>"},
+    "gem_s0.5": {"fwd": "fwd_kernel<128, false, false, false>", "bwd_dq": "bwd_dq_kernel<128, false, false>",
+                 "bwd_dkdv": "bwd_dkdv_kernel<128, false, false>"},
+    "bcast_s0.5": {"fwd": "fwd_kernel<128, false, true, false>", "bwd_dq": "bwd_dq_kernel<128, false, true>",
+                   "bwd_dkdv": "bwd_dkdv_kernel<128, false, true>"},
+    "decode_ps16": {"decode": "decode_kernel<128, 1, false>"},
+}
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_bench_step.txt")
+COUNTER_PROFILE = os.path.join(ROOT, "profiles", "mfma_lds_counters_bench_step.md")
+BENCH_CMD = "python3 $REPO/bench.py --steps 2 --warmup 1 --cpu-sample 0"
 
 
 def source_digest() -> str:
@@ -145,62 +169,80 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def stored_traffic(sparsity: float):
-    """HBM bytes per launch of each main kernel from the committed counter summary, or None."""
-    if abs(sparsity - 0.5) > 1e-9 or not os.path.exists(TRAFFIC_PROFILE):
+def stored_traffic(workload: str):
+    """HBM bytes per launch of each main kernel of `workload` from the committed
+    counter summary, or None when the summary describes other kernel sources."""
+    if not os.path.exists(TRAFFIC_PROFILE):
         return None
     for line in open(TRAFFIC_PROFILE):
         if line.startswith('{"source_digest"'):
             rec = json.loads(line)
-            return rec["bytes_per_launch"] if rec["source_digest"] == source_digest() else None
+            if rec["source_digest"] != source_digest():
+                return None
+            return rec["bytes_per_launch"].get(workload)
     return None
+
+
+def _per_dispatch(db, counters):
+    """{dispatch: {counter: value}} (instances of one dispatch summed), {dispatch: kernel name},
+    {dispatch: duration ns}."""
+    import collections
+    import sqlite3
+    val = collections.defaultdict(lambda: collections.defaultdict(float))
+    name, dur = {}, {}
+    con = sqlite3.connect(db)
+    q = "select kernel_name, counter_name, value, dispatch_id, duration from counters_collection"
+    for kname, cname, v, disp, d in con.execute(q):
+        if cname in counters:
+            val[disp][cname] += v
+            name[disp] = kname
+            dur[disp] = d
+    return val, name, dur
+
+
+def _workload_dispatches(name):
+    """{(workload, slot): [dispatch ids]} for the bench step's main kernels."""
+    out = {}
+    for disp, kname in name.items():
+        for wl, slots in WORKLOAD_KERNELS.items():
+            for slot, key in slots.items():
+                if key + "(" in kname.replace("jfa::", ""):
+                    out.setdefault((wl, slot), []).append(disp)
+    return out
 
 
 def pmc_summary(fetch_db: str, write_db: str, copy_mib: int, out: str):
     """Turn two rocprofv3 --pmc databases of this benchmark (FETCH_SIZE, then WRITE_SIZE)
     into per-launch byte counts, scaled by what the same counters read for the plain
     device copy of copy_mib MiB that the benchmark runs after timing."""
-    import collections
-    import sqlite3
-
-    def per_dispatch(db, counter):
-        val, name = collections.defaultdict(float), {}
-        con = sqlite3.connect(db)
-        q = "select kernel_name, counter_name, value, dispatch_id from counters_collection"
-        for kname, cname, v, disp in con.execute(q):
-            if cname == counter:
-                val[disp] += v           # sum the per-XCD / per-channel instances of one dispatch
-                name[disp] = kname
-        return val, name
-
     known = copy_mib * float(1 << 20)
     res = {}
     for counter, db in (("FETCH_SIZE", fetch_db), ("WRITE_SIZE", write_db)):
-        val, name = per_dispatch(db, counter)
+        val, name, _ = _per_dispatch(db, {counter})
         copies = [d for d in val if "copy" in name[d].lower()]
         if not copies:
             raise SystemExit(f"no copy kernel among the dispatches of {db}")
-        cal = max(copies, key=lambda d: val[d])
-        factor = known / (val[cal] * 1024.0)
-        kib = collections.defaultdict(list)
-        for d, v in val.items():
-            for key, slot in KERNEL_SLOTS:
-                if key in name[d]:
-                    kib[slot].append(v)
-        res[counter] = (factor, val[cal], {k: sum(v) / len(v) for k, v in kib.items()})
+        cal = max(copies, key=lambda d: val[d][counter])
+        factor = known / (val[cal][counter] * 1024.0)
+        per = {k: sum(val[d][counter] for d in ds) / len(ds) for k, ds in _workload_dispatches(name).items()}
+        res[counter] = (factor, val[cal][counter], per)
     ff, fcal, fk = res["FETCH_SIZE"]
     wf, wcal, wk = res["WRITE_SIZE"]
-    bytes_per = {s: fk.get(s, 0.0) * 1024.0 * ff + wk.get(s, 0.0) * 1024.0 * wf for _, s in KERNEL_SLOTS if s in fk}
+    keys = sorted(set(fk) | set(wk))
+    bytes_per = {}
+    for wl, slot in keys:
+        bytes_per.setdefault(wl, {})[slot] = fk.get((wl, slot), 0.0) * 1024.0 * ff + wk.get((wl, slot), 0.0) * 1024.0 * wf
     lines = [
-        "# HBM traffic per launch: bench step (GEM jagged fwd+bwd, sparsity 0.5, + paged decode, page 16)",
+        "# HBM traffic per launch: bench step kernels (dense causal d = 128, GEM s = 0.5, broadcast-Q s = 0.5, "
+        "paged decode page 16)",
         "",
         "Commands (repository root on the MI355X box = $REPO; one counter per run):",
         "",
         "```",
-        "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc FETCH_SIZE -d $REPO/gpurun_out/pmc_fetch -o fetch "
-        "-- python3 $REPO/bench.py --steps 2 --warmup 1 --cpu-seqs 0",
-        "cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc WRITE_SIZE -d $REPO/gpurun_out/pmc_write -o write "
-        "-- python3 $REPO/bench.py --steps 2 --warmup 1 --cpu-seqs 0",
+        f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE -d $REPO/gpurun_out/pmc_fetch "
+        f"-o fetch -- {BENCH_CMD}",
+        f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE -d $REPO/gpurun_out/pmc_write "
+        f"-o write -- {BENCH_CMD}",
         "python3 bench.py --pmc-summary gpurun_out/pmc_fetch/fetch_results.db gpurun_out/pmc_write/write_results.db",
         "```",
         "",
@@ -209,39 +251,216 @@ def pmc_summary(fetch_db: str, write_db: str, copy_mib: int, out: str):
         "counters to bytes.  FETCH_SIZE counts L2 misses served by the memory side, so reads that hit the "
         "last-level MALL count too.",
         "",
-        "| kernel | FETCH_SIZE (KiB/launch) | WRITE_SIZE (KiB/launch) | scaled bytes/launch |",
-        "|---|---|---|---|",
+        "| workload | kernel | FETCH_SIZE (KiB/launch) | WRITE_SIZE (KiB/launch) | scaled bytes/launch |",
+        "|---|---|---|---|---|",
     ]
-    for _, s in KERNEL_SLOTS:
-        if s in bytes_per:
-            lines.append(f"| {s} | {fk[s]:.0f} | {wk.get(s, 0.0):.0f} | {bytes_per[s]:.4g} |")
+    for wl, slot in keys:
+        lines.append(f"| {wl} | {slot} | {fk.get((wl, slot), 0.0):.0f} | {wk.get((wl, slot), 0.0):.0f} | "
+                     f"{bytes_per[wl][slot]:.4g} |")
     lines += ["", "Machine-readable line (the digest covers the kernel sources and build options):", ""]
-    lines.append(json.dumps({"source_digest": source_digest(), "workload": "gem_s0.5",
-                             "fetch_factor": ff, "write_factor": wf, "bytes_per_launch": bytes_per}))
+    lines.append(json.dumps({"source_digest": source_digest(), "fetch_factor": ff, "write_factor": wf,
+                             "bytes_per_launch": bytes_per}))
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
 
 
-def cpu_baseline(inp, n_seq: int):
-    """Time the fp64 oracle on the first n_seq sequences of the same workload (fwd + bwd)."""
+COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
+            "SQ_INSTS_VALU_TRANS_F32", "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CU_CYCLES", "SQ_WAVES", "GRBM_GUI_ACTIVE")
+
+
+def counter_summary(db: str, out: str):
+    """Summarise one rocprofv3 --pmc run (the COUNTERS above) of this benchmark: per main
+    kernel of each workload, the counters per launch and what follows from them."""
+    import workloads
+    val, name, dur = _per_dispatch(db, set(COUNTERS))
+    groups = _workload_dispatches(name)
+    # algorithmic flops per launch, from the same seeded workloads the benchmark runs
+    alg = {}
+    for wl, make in (("dense_causal_d128", lambda: workloads.dense_causal(0, head_dim=128)),
+                     ("gem_s0.5", lambda: workloads.gem(0, 0.5)), ("bcast_s0.5", lambda: workloads.broadcast_q(0, 0.5))):
+        x = make()
+        bc = wl.startswith("bcast")
+        pairs = pairs_of(None if bc else x.cu_q, x.cu_k, False if bc else x.causal, x.q.shape[0] if bc else None)
+        u = x.q.shape[2] * x.q.shape[1] * pairs
+        alg[wl] = {"fwd": 4.0 * u, "bwd_dkdv": 8.0 * u, "bwd_dq": 2.0 * u}
+        del x
+    peak = MFMA_BF16_PEAK_TFLOPS * 1e12
+    lines = [
+        "# MFMA, LDS and transcendental counters: bench step kernels",
+        "",
+        "Command (repository root on the MI355X box = $REPO):",
+        "",
+        "```",
+        "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc " + " ".join(COUNTERS)
+        + f" --kernel-trace -d $REPO/gpurun_out/pmc_mfma -o mfma -- {BENCH_CMD}",
+        "python3 bench.py --counter-summary gpurun_out/pmc_mfma/mfma_results.db",
+        "```",
+        "",
+        "Per launch (mean over the run's launches of each kernel).  Derived columns:",
+        "",
+        "* `MFMA TFLOP/s` = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 / launch duration (executed bf16 MFMA work; the "
+        "duration is the dispatch's own, taken with the counters on);",
+        "* `MFMA util` = that rate / 2516.6 TFLOP/s (dense bf16 peak);",
+        "* `MFMA busy` = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 256 CUs x 4 SIMDs);",
+        "* `exec/alg` = executed MFMA flops / the kernel's algorithmic flops (fwd 4d, dK/dV 8d, dQ 2d per pair "
+        "and head: the dQ kernel recomputes S and dP, 6d executed);",
+        "* `LDS/MFMA` = SQ_INSTS_LDS / SQ_INSTS_MFMA; `exp/MFMA` = SQ_INSTS_VALU_TRANS_F32 / SQ_INSTS_MFMA;",
+        "* `bank confl/LDS` = SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS (conflict cycles per LDS instruction).",
+        "",
+        "| workload | kernel | ms | MFMA TFLOP/s | MFMA util | MFMA busy | exec/alg | SQ_INSTS_MFMA | LDS/MFMA | "
+        "exp/MFMA | bank confl/LDS |",
+        "|---|---|---|---|---|---|---|---|---|---|---|",
+    ]
+    rec = {}
+    for (wl, slot), ds in sorted(groups.items()):
+        m = {c: sum(val[d][c] for d in ds) / len(ds) for c in COUNTERS}
+        ms = sum(dur[d] for d in ds) / len(ds) * 1e-6
+        flops = 512.0 * m["SQ_INSTS_VALU_MFMA_MOPS_BF16"]
+        rate = flops / (ms * 1e-3) if ms > 0 else 0.0
+        busy = m["SQ_VALU_MFMA_BUSY_CYCLES"] / max(1.0, m["GRBM_GUI_ACTIVE"] * 256 * 4)
+        a = alg.get(wl, {}).get(slot)
+        mf = max(1.0, m["SQ_INSTS_MFMA"])
+        row = {"ms": ms, "mfma_tflops": rate / 1e12, "mfma_util": rate / peak, "mfma_busy": busy,
+               "exec_over_alg": flops / a if a else None, "lds_per_mfma": m["SQ_INSTS_LDS"] / mf,
+               "exp_per_mfma": m["SQ_INSTS_VALU_TRANS_F32"] / mf,
+               "bank_conflict_per_lds": m["SQ_LDS_BANK_CONFLICT"] / max(1.0, m["SQ_INSTS_LDS"]),
+               "counters": m}
+        rec.setdefault(wl, {})[slot] = row
+        ea = f"{row['exec_over_alg']:.2f}" if a else "-"
+        lines.append(f"| {wl} | {slot} | {ms:.3f} | {rate / 1e12:.1f} | {rate / peak:.3f} | {busy:.3f} | {ea} | "
+                     f"{m['SQ_INSTS_MFMA']:.4g} | {row['lds_per_mfma']:.2f} | {row['exp_per_mfma']:.2f} | "
+                     f"{row['bank_conflict_per_lds']:.3f} |")
+    lines += ["", "Raw counters per launch:", "", "| workload | kernel | " + " | ".join(COUNTERS) + " |",
+              "|---|---|" + "---|" * len(COUNTERS)]
+    for wl in sorted(rec):
+        for slot, row in sorted(rec[wl].items()):
+            lines.append(f"| {wl} | {slot} | " + " | ".join(f"{row['counters'][c]:.4g}" for c in COUNTERS) + " |")
+    lines += ["", "Machine-readable line (the digest covers the kernel sources and build options):", ""]
+    lines.append(json.dumps({"source_digest": source_digest(),
+                             "per_launch": {wl: {s: {k: v for k, v in r.items() if k != "counters"}
+                                                 for s, r in d.items()} for wl, d in rec.items()}}))
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def trace_summary(db: str, timed: str, out: str):
+    """Summarise a rocprofv3 --kernel-trace --stats run of this benchmark: per kernel the
+    calls and durations, plus the mean of the timed launches of the bench step's main
+    kernels (the last `steps` launches), next to what bench.py measured itself in that run
+    (`timed`: its JSON output line)."""
+    import sqlite3
+    con = sqlite3.connect(db)
+    rows = list(con.execute("select name, total_calls, total_duration, average, percentage from top_kernels"))
+    bench = json.loads(open(timed).read().strip().splitlines()[-1])
+    steps = bench["steps"]
+    per = {}
+    for name, dur in con.execute("select name, duration from kernels order by start"):
+        per.setdefault(name, []).append(dur)
+    lines = [
+        "# Kernel trace: bench step (dense causal d = 128 fwd+bwd + paged decode page 16; then GEM s = 0.5 and "
+        "broadcast-Q s = 0.5 extras)",
+        "",
+        "Command (repository root on the MI355X box; $REPO = that root):",
+        "",
+        "```",
+        "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --kernel-trace --stats -d "
+        "$REPO/gpurun_out/prof_bench -o bench -- python3 $REPO/bench.py --steps 10 --warmup 3 --cpu-sample 0 "
+        "> $REPO/gpurun_out/prof_bench.json",
+        "python3 bench.py --trace-summary gpurun_out/prof_bench/bench_results.db gpurun_out/prof_bench.json",
+        "```",
+        "",
+        "Per-kernel summary (top_kernels view of the rocpd database; all launches, warmup included):",
+        "",
+        "| kernel | calls | total (us) | average (us) | % of GPU time |",
+        "|---|---|---|---|---|",
+    ]
+    for name, calls, tot, avg, pct in rows:
+        lines.append(f"| `{name}` | {calls} | {tot:.1f} | {avg:.1f} | {pct:.2f} |")
+    lines += ["", f"Timed launches of the step's main kernels (the first {steps} launches after the "
+              f"warmup of each; bench.py's own HIP-event means from the same run beside them):", "",
+              "| workload | kernel | trace mean (ms) | bench.py events (ms) |", "|---|---|---|---|"]
+    warm = bench.get("warmup", 0)
+    measured = {"dense_causal_d128": bench.get("kernels_ms", {}),
+                "gem_s0.5": bench.get("gem_s0.5", {}).get("kernels_ms", {}),
+                "bcast_s0.5": bench.get("bcast_s0.5", {}).get("kernels_ms", {})}
+    for wl, slots in WORKLOAD_KERNELS.items():
+        for slot, key in slots.items():
+            durs = [d for n, ds in per.items() if key + "(" in n.replace("jfa::", "") for d in ds]
+            if not durs:
+                continue
+            if wl in ("dense_causal_d128", "decode_ps16"):
+                setup = 1 if slot in ("fwd", "decode") else 0   # the case's setup call launches these once
+                t = durs[setup + warm:setup + warm + steps]
+                ref = measured["dense_causal_d128"].get(slot)
+            else:
+                t = durs[-bench.get("extra_steps", 10):]
+                ref = measured[wl].get(slot)
+            lines.append(f"| {wl} | {slot} | {sum(t) / len(t) * 1e-6:.4f} | {ref if ref is not None else '-'} |")
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(inp, heads):
+    """Time the fp64 oracle, as it stands, on a bounded sample of the headline workload:
+    forward + backward of sequence 0 for the given heads (all its rows and keys)."""
     import oracle
     from threadpoolctl import threadpool_info
-    cu = inp.cu_q
-    te = int(cu[n_seq])
-    sub = [x[:te].astype(np.float64) for x in (inp.q, inp.k, inp.v, inp.do)]
-    cs = cu[:n_seq + 1]
+    L = int(inp.cu_q[1])
+    cu = np.array([0, L])
     t0 = time.perf_counter()
-    oracle.attention_forward(sub[0], sub[1], sub[2], cs, cs, False)
-    oracle.attention_backward(*sub, cs, cs, False)
+    for h in heads:
+        args = [x[:L, h:h + 1].astype(np.float64) for x in (inp.q, inp.k, inp.v, inp.do)]
+        oracle.attention_forward(*args[:3], cu, cu, inp.causal)
+        oracle.attention_backward(*args, cu, cu, inp.causal)
     dt = time.perf_counter() - t0
-    pairs = pairs_of(cs, cs, False)
-    flops = 14.0 * inp.q.shape[2] * inp.q.shape[1] * pairs
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"fp64 numpy oracle, fwd+bwd of the first {n_seq} of 256 sequences "
-                      f"({te} tokens, {pairs * inp.q.shape[1]} query-key pairs) of the same workload; "
-                      f"{dt:.1f} s wall"}
+    pairs = pairs_of(cu, cu, inp.causal) * len(heads)
+    flops = 14.0 * inp.q.shape[2] * pairs
+    blas = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    affinity = len(os.sched_getaffinity(0))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(min(blas, affinity)), "kind": "oracle",
+            "affinity_cores": affinity, "blas_threads": int(blas), "cpu_model": cpu_model(),
+            "sample": f"fp64 numpy oracle (BLAS matmuls on {blas} threads, the rest on one), fwd+bwd of sequence 0 "
+                      f"(8192 causal rows) for {len(heads)} of 32 heads of the same dense causal workload, "
+                      f"{pairs} visible query-key pairs; {dt:.1f} s wall"}
+
+
+def _time_case(torch, jfa, case, steps, warmup):
+    """fwd and bwd of one jagged case, `steps` times after `warmup`: mean ms of each call
+    and of each main kernel (the library's caller-owned events on the launch stream)."""
+    for _ in range(warmup):
+        case.step()
+    evs = [jfa.KernelEvents() for _ in range(steps)]
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        marks[i][0].record()
+        case.fwd(evs[i])
+        marks[i][1].record()
+        case.bwd(evs[i])
+        marks[i][2].record()
+    torch.cuda.synchronize()
+    f_ms = sum(m[0].elapsed_time(m[1]) for m in marks) / steps
+    b_ms = sum(m[1].elapsed_time(m[2]) for m in marks) / steps
+    kern = {s: sum(e.elapsed_ms(s) for e in evs) / steps for s in ("fwd", "bwd_dq", "bwd_dkdv")}
+    return f_ms, b_ms, kern
+
+
+def _pct(flops, ms):
+    return round(100.0 * flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 2)
 
 
 def main():
@@ -249,21 +468,31 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--sparsity", type=float, default=0.5)
     ap.add_argument("--page-size", type=int, default=16)
-    ap.add_argument("--cpu-seqs", type=int, default=256, help="sequences in the oracle timing sample (0 = skip)")
+    ap.add_argument("--extra-steps", type=int, default=10, help="timed calls of each extra workload (GEM, broadcast-Q)")
+    ap.add_argument("--cpu-sample", type=int, default=1, help="heads of sequence 0 in the oracle timing sample (0 = skip)")
     ap.add_argument("--sweep", action="store_true", help="one JSON line per workload (GEM s, broadcast-Q, dense, decode)")
     ap.add_argument("--copy-calibration-mib", type=int, default=1024,
                     help="run one device copy of this size after timing (reference for HBM byte counters)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="summarise two rocprofv3 --pmc runs of this benchmark into the traffic profile and exit")
+    ap.add_argument("--counter-summary", metavar="DB",
+                    help="summarise a rocprofv3 --pmc run of the MFMA/LDS counters into the counter profile and exit")
+    ap.add_argument("--trace-summary", nargs=2, metavar=("DB", "BENCH_JSON"),
+                    help="summarise a rocprofv3 --kernel-trace run of this benchmark and exit")
     args = ap.parse_args()
     if args.pmc_summary:
         return pmc_summary(*args.pmc_summary, args.copy_calibration_mib, TRAFFIC_PROFILE)
+    if args.counter_summary:
+        return counter_summary(args.counter_summary, COUNTER_PROFILE)
+    if args.trace_summary:
+        return trace_summary(*args.trace_summary,
+                             os.path.join(ROOT, "profiles", "kernel_trace_bench_step_dense_causal_d128.md"))
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only: --gpus must be 1 (there is no "
+                                   "multi-GPU path; each GPU's share is the single-GPU workload)"}))
         sys.exit(2)
 
     import torch
@@ -279,10 +508,10 @@ def main():
         return sweep(torch, jfa, workloads, args, log)
 
     t0 = time.time()
-    gem_inp = workloads.gem(0, args.sparsity)
+    dense_inp = workloads.dense_causal(0, head_dim=128)
     dec_inp = workloads.decode_paged(0, args.page_size, tail_fill=0.0)
     log(f"inputs generated in {time.time() - t0:.1f}s")
-    jc = JaggedCase(torch, jfa, gem_inp)
+    jc = JaggedCase(torch, jfa, dense_inp)
     dc = DecodeCase(torch, jfa, dec_inp)
     del dec_inp
 
@@ -291,37 +520,49 @@ def main():
         dc.step()
     torch.cuda.synchronize()
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    jfa.timing.enable(True)
+    evs = [jfa.KernelEvents() for _ in range(args.steps)]
+    marks = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t_start = time.perf_counter()
     for i in range(args.steps):
-        ev[i][0].record()
-        jc.step()
-        ev[i][1].record()
-        dc.step()
-        ev[i][2].record()
+        marks[i][0].record()
+        jc.fwd(evs[i])
+        marks[i][1].record()
+        jc.bwd(evs[i])
+        marks[i][2].record()
+        dc.step(evs[i])
+        marks[i][3].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
-    jfa.timing.enable(False)
-    kt = jfa.timing.collect()
-    fb_ms = sum(e[0].elapsed_time(e[1]) for e in ev)
-    dec_ms = sum(e[1].elapsed_time(e[2]) for e in ev)
-    step_ms = wall * 1e3 / args.steps
+    K = args.steps
+    f_ms = sum(m[0].elapsed_time(m[1]) for m in marks) / K
+    b_ms = sum(m[1].elapsed_time(m[2]) for m in marks) / K
+    dec_ms = sum(m[2].elapsed_time(m[3]) for m in marks) / K
+    kern = {s: sum(e.elapsed_ms(s) for e in evs) / K for s in ("fwd", "bwd_dq", "bwd_dkdv", "decode")}
+    step_ms = wall * 1e3 / K
 
-    tflops = (jc.fwd_flops + jc.bwd_flops) * args.steps / (fb_ms * 1e-3) / 1e12
-    dec_tbs = dc.bytes * args.steps / (dec_ms * 1e-3) / 1e12
-    avg = {k: (ms / n if n else 0.0) for k, (ms, n) in kt.items()}
-    # Algorithmic flops per launch of each main kernel (per query-key pair, times Hq):
-    #   fwd       4d  (S = Q K^T, O = P V)
-    #   bwd_dkdv  8d  (S recomputed, dP, dV, dK: the backward's contractions except dQ)
-    #   bwd_dq    2d  (dQ = dS K; its own S/dP recomputation is not counted)
-    d, hq = 128, 8
-    alg = {"fwd": 4.0 * d * hq * jc.pairs, "bwd_dkdv": 8.0 * d * hq * jc.pairs, "bwd_dq": 2.0 * d * hq * jc.pairs}
-    dominant = max(alg, key=lambda k: avg[k])
-    ach = alg[dominant] / (avg[dominant] * 1e-3) / 1e12
+    tflops = (jc.fwd_flops + jc.bwd_flops) / ((f_ms + b_ms) * 1e-3) / 1e12
+    dec_tbs = dc.bytes / (dec_ms * 1e-3) / 1e12
+    dominant = max(jc.kernel_flops, key=lambda k: kern[k])
+    ach = jc.kernel_flops[dominant] / (kern[dominant] * 1e-3) / 1e12
     names = {"fwd": "fwd_kernel (jagged forward)", "bwd_dkdv": "bwd_dkdv_kernel (key-stationary dK/dV)",
              "bwd_dq": "bwd_dq_kernel (query-stationary dQ)"}
+
+    # extra workloads, timed after the steps (not part of `value`)
+    extras = {}
+    for name, make, bc in (("gem_s0.5", lambda: workloads.gem(0, 0.5), False),
+                           ("bcast_s0.5", lambda: workloads.broadcast_q(0, 0.5), True)):
+        x = make()
+        case = JaggedCase(torch, jfa, bcast=x) if bc else JaggedCase(torch, jfa, x)
+        del x
+        ef, eb, ek = _time_case(torch, jfa, case, args.extra_steps, 3)
+        extras[name] = {"fwd_ms": round(ef, 4), "bwd_ms": round(eb, 4),
+                        "tflops": round((case.fwd_flops + case.bwd_flops) / ((ef + eb) * 1e-3) / 1e12, 2),
+                        "fwd_pct_peak": _pct(case.fwd_flops, ef), "bwd_pct_peak": _pct(case.bwd_flops, eb),
+                        "fwd_gflop": round(case.fwd_flops / 1e9, 2), "bwd_gflop": round(case.bwd_flops / 1e9, 2),
+                        "kernels_ms": {k: round(v, 4) for k, v in ek.items()}}
+        del case
+        torch.cuda.empty_cache()
 
     # plain device copy of known size: reference for FETCH_SIZE / WRITE_SIZE scaling
     if args.copy_calibration_mib > 0:
@@ -332,20 +573,19 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    stored = stored_traffic(args.sparsity)
+    stored = stored_traffic("dense_causal_d128")
     traffic = round(stored[dominant]) if stored and dominant in stored else None
 
     cpu = None
-    if args.cpu_seqs > 0:
-        cpu = cpu_baseline(gem_inp, min(args.cpu_seqs, gem_inp.batch))
+    if args.cpu_sample > 0:
+        cpu = cpu_baseline(dense_inp, list(range(min(args.cpu_sample, 32))))
 
-    meta = gem_inp.meta
     out = {
         "metric": METRIC,
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
+        "steps": K,
         "warmup": args.warmup,
         "ms_per_step": round(step_ms, 4),
         "higher_is_better": True,
@@ -355,22 +595,27 @@ def main():
         "data": "synthetic",
         "pct_mfma_peak": round(100 * tflops / MFMA_BF16_PEAK_TFLOPS, 2),
         "config": {
-            "workload": f"GEM jagged self-attention fwd+bwd (sparsity {args.sparsity}) + paged split-KV decode",
-            "jagged": {"batch": 256, "max_len": 1024, "sparsity": args.sparsity,
-                       "realised_sparsity": round(meta["realised_sparsity"], 4), "heads": 8, "head_dim": 128,
-                       "total_tokens": int(gem_inp.q.shape[0]), "causal": False,
-                       "fwd_gflop": round(jc.fwd_flops / 1e9, 2), "bwd_gflop": round(jc.bwd_flops / 1e9, 2)},
+            "workload": "dense causal jagged self-attention fwd+bwd, 4 x 8192 tokens, 32 heads, d = 128 "
+                        "+ paged split-KV decode",
+            "jagged": {"batch": 4, "seq_len": 8192, "heads": 32, "head_dim": 128, "total_tokens": 32768,
+                       "causal": True, "fwd_gflop": round(jc.fwd_flops / 1e9, 2),
+                       "bwd_gflop": round(jc.bwd_flops / 1e9, 2)},
             "decode": {"batch": 32, "heads_q": 32, "heads_kv": 8, "head_dim": 128, "page_size": args.page_size,
                        "splits": dc.nsplits, "kv_len": "U{4096..16384}", "gbytes": round(dc.bytes / 1e9, 4)},
         },
-        "fwd_bwd_ms": round(fb_ms / args.steps, 4),
+        "fwd_ms": round(f_ms, 4),
+        "bwd_ms": round(b_ms, 4),
+        "fwd_pct_peak": _pct(jc.fwd_flops, f_ms),
+        "bwd_pct_peak": _pct(jc.bwd_flops, b_ms),
         "decode": {"value": round(dec_tbs, 3), "unit": "TB/s", "pct_hbm_peak": round(100 * dec_tbs * 1e3 / HBM_PEAK_GBS, 2),
-                   "ms": round(dec_ms / args.steps, 4)},
-        "kernels_ms": {k: round(v, 4) for k, v in avg.items()},
+                   "ms": round(dec_ms, 4)},
+        "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
+        "extra_steps": args.extra_steps,
+        **extras,
         "roofline": {"kernel": names[dominant], "bound": "mfma",
                      "achieved": round(ach, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(ach / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": traffic,
-                     "algorithmic_flop_per_launch": alg[dominant]},
+                     "algorithmic_flop_per_launch": jc.kernel_flops[dominant]},
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
@@ -423,9 +668,10 @@ def sweep(torch, jfa, workloads, args, log):
         q8, k8, v8 = (torch.from_numpy(enc[n]).to("cuda").view(torch.float8_e4m3fn) for n in ("q", "k", "v"))
         sc = dict(q_scale=enc["q_scale"], k_scale=enc["k_scale"], v_scale=enc["v_scale"])
         del inp, enc
-        # the forward's workspace (its work list) does not depend on the element type
+        ws8 = torch.empty(max(1, jfa.jfa_fwd_workspace_size(q8, k8, jc.ck, jc.mq, jc.mk, jc.causal)),
+                          dtype=torch.uint8, device="cuda")
         f8_ms = timeit(lambda: jfa.jfa_fwd(q8, k8, v8, jc.cq, jc.ck, jc.mq, jc.mk, jc.causal, out=jc.o, lse=jc.lse,
-                                           workspace=jc.ws_f, **sc))
+                                           workspace=ws8, **sc))
         bf_ms = timeit(lambda: jfa.jfa_fwd(jc.q, jc.k, jc.v, jc.cq, jc.ck, jc.mq, jc.mk, jc.causal,
                                            out=jc.o, lse=jc.lse, workspace=jc.ws_f))
         print(json.dumps({"workload": name + "_fp8_fwd", "fwd_ms": round(f8_ms, 4), "bf16_fwd_ms": round(bf_ms, 4),

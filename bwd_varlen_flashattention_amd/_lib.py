@@ -22,8 +22,16 @@ JFA_ERR_HIP = 4
 EXPORTS = (
     "jfa_fwd_workspace_size", "jfa_fwd", "jfa_bwd_workspace_size", "jfa_bwd",
     "jfa_decode_workspace_size", "jfa_decode_paged", "jfa_decode_num_splits",
-    "jfa_status_string", "jfa_abi_version", "jfa_timing_enable", "jfa_timing_collect",
+    "jfa_status_string", "jfa_abi_version",
 )
+ABI_VERSION = 4
+
+
+class KernelEventsStruct(ctypes.Structure):
+    """jfa_kernel_events_t: caller-created hipEvent_t handles (or NULL)."""
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "fwd_start", "fwd_stop", "bwd_dq_start", "bwd_dq_stop",
+        "bwd_dkdv_start", "bwd_dkdv_stop", "decode_start", "decode_stop")]
 
 
 class AttnParams(ctypes.Structure):
@@ -43,6 +51,7 @@ class AttnParams(ctypes.Structure):
         ("q_scale", ctypes.c_float),
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
+        ("events", ctypes.POINTER(KernelEventsStruct)),
     ]
 
 
@@ -64,6 +73,7 @@ class DecodeParams(ctypes.Structure):
         ("v_scale", ctypes.c_float),
         ("q_dtype", ctypes.c_int32),
         ("q_scale", ctypes.c_float),
+        ("events", ctypes.POINTER(KernelEventsStruct)),
     ]
 
 
@@ -104,10 +114,9 @@ def load() -> ctypes.CDLL:
     lib.jfa_status_string.restype = ctypes.c_char_p
     lib.jfa_abi_version.argtypes = []
     lib.jfa_abi_version.restype = ctypes.c_int
-    lib.jfa_timing_enable.argtypes = [ctypes.c_int]
-    lib.jfa_timing_enable.restype = ctypes.c_int
-    lib.jfa_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
-    lib.jfa_timing_collect.restype = ctypes.c_int
+    if lib.jfa_abi_version() != ABI_VERSION:
+        raise ImportError(f"{LIB_PATH} has ABI version {lib.jfa_abi_version()}, the binding expects "
+                          f"{ABI_VERSION}; rebuild it")
     _lib = lib
     return lib
 

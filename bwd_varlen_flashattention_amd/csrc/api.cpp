@@ -8,8 +8,6 @@
 
 #include <math.h>
 #include <algorithm>
-#include <mutex>
-#include <vector>
 
 #include "jfa.h"
 #include "jfa_internal.h"
@@ -41,37 +39,9 @@ int cu_count() {
 bool supported_dim(int d) { return d == 64 || d == 96 || d == 128 || d == 192 || d == 256; }
 
 // ------------------------------------------------------------------ timing
-struct Timing {
-  std::mutex mu;
-  bool enabled = false;
-  std::vector<hipEvent_t> start[JFA_TIMING_SLOTS], stop[JFA_TIMING_SLOTS];
-};
-Timing& timing() {
-  static Timing t;
-  return t;
-}
-
-struct TimedRegion {
-  int which;
-  hipStream_t stream;
-  hipEvent_t e0 = nullptr, e1 = nullptr;
-  TimedRegion(int w, hipStream_t s) : which(w), stream(s) {
-    Timing& t = timing();
-    std::lock_guard<std::mutex> g(t.mu);
-    if (!t.enabled) return;
-    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) { e0 = e1 = nullptr; return; }
-    hipEventRecord(e0, stream);
-  }
-  void finish() {
-    if (!e0) return;
-    hipEventRecord(e1, stream);
-    Timing& t = timing();
-    std::lock_guard<std::mutex> g(t.mu);
-    t.start[which].push_back(e0);
-    t.stop[which].push_back(e1);
-    e0 = e1 = nullptr;
-  }
-};
+// The caller's events (jfa_kernel_events_t): recorded on the call's stream around
+// one kernel launch; the library keeps no reference to them.
+hipError_t record(void* ev, hipStream_t s) { return ev ? hipEventRecord((hipEvent_t)ev, s) : hipSuccess; }
 
 // ------------------------------------------------------------------ validation
 bool positive_finite(float x) { return x > 0.f && !isinf(x); }   // false for NaN as well
@@ -142,6 +112,7 @@ int64_t lse_elems(const jfa_attn_params_t* p) {
 // for two per CU; each chunk owns an fp32 partial of dQ.
 int bcast_dq_chunks(const jfa_attn_params_t* p) {
   const int64_t tiles_heads = (int64_t)cdiv_i(p->total_q, bwd_dq_rows(p->head_dim)) * p->num_heads_q;
+  if (tiles_heads == 0) return 0;   // no query rows: no dQ work
   const int64_t want = std::max<int64_t>(1, (2LL * cu_count() + tiles_heads - 1) / tiles_heads);
   const int per = cdiv_i(p->batch, std::min<int64_t>(p->batch, want));
   return cdiv_i(p->batch, per);
@@ -276,6 +247,7 @@ jfa_status_t jfa_fwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   sa.loop_tile = bn;
   sa.mode = 0;
   sa.causal = p->causal;
+  sa.bcast = p->broadcast_q;
   sa.bcast_nq = p->broadcast_q ? p->total_q : 0;
   set_lists(sa, p, workspace, L);
   hipError_t e = launch_sched(&sa, 1, stream);
@@ -294,6 +266,7 @@ jfa_status_t jfa_fwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   fa.hq = p->num_heads_q;
   fa.hkv = p->num_heads_kv;
   fa.group = p->num_heads_q / p->num_heads_kv;
+  fa.bcast = sa.bcast;
   fa.bcast_nq = sa.bcast_nq;
   fa.total_q = p->total_q;
   fa.causal = p->causal;
@@ -303,10 +276,12 @@ jfa_status_t jfa_fwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   fa.v_scale = fp8 ? p->v_scale : 1.f;
   const int64_t max_items = L.max_items;
   const int grid = (int)std::min<int64_t>((int64_t)cu_count() * fwd_blocks_per_cu(p->head_dim, fp8), max_items);
-  TimedRegion tr(JFA_TIMING_FWD, stream);
+  const jfa_kernel_events_t* ev = p->events;
+  if (ev && record(ev->fwd_start, stream) != hipSuccess) return JFA_ERR_HIP;
   e = launch_fwd(fa, p->head_dim, std::max(grid, 1), stream);
-  tr.finish();
-  return hip_status(e);
+  if (e != hipSuccess) return JFA_ERR_HIP;
+  if (ev && record(ev->fwd_stop, stream) != hipSuccess) return JFA_ERR_HIP;
+  return JFA_OK;
 }
 
 // The backward is a bf16 computation (e4m3 is an inference input format).
@@ -335,6 +310,14 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   if (!workspace || ((uintptr_t)workspace % kAlign) != 0) return JFA_ERR_INVALID_ARGUMENT;
   if (workspace_bytes < L.end) return JFA_ERR_WORKSPACE_TOO_SMALL;
   hipStream_t stream = (hipStream_t)stream_;
+  const jfa_kernel_events_t* ev = p->events;
+  if (p->broadcast_q && p->total_q == 0) {
+    // no query rows: no key is seen by any query, so dK = dV = 0 (there is no dQ)
+    const int64_t bytes = (int64_t)p->total_k * p->num_heads_kv * p->head_dim * 2;
+    if (launch_zero_fill(dk, bytes, stream) != hipSuccess || launch_zero_fill(dv, bytes, stream) != hipSuccess)
+      return JFA_ERR_HIP;
+    return JFA_OK;
+  }
   const float scale = eff_scale(p->softmax_scale, p->head_dim);
   float* delta = at<float>(workspace, L.delta);
   float* dq_part = p->broadcast_q ? at<float>(workspace, L.dq_part) : nullptr;
@@ -360,6 +343,7 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   ba.hq = p->num_heads_q;
   ba.hkv = p->num_heads_kv;
   ba.group = p->num_heads_q / p->num_heads_kv;
+  ba.bcast = p->broadcast_q;
   ba.bcast_nq = p->broadcast_q ? p->total_q : 0;
   ba.total_q = p->total_q;
   ba.causal = p->causal;
@@ -380,6 +364,7 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
     dq_sa.loop_tile = bwd_dq_tile(p->head_dim);
     dq_sa.mode = 0;
     dq_sa.causal = p->causal;
+    dq_sa.bcast = 0;
     dq_sa.bcast_nq = 0;
     set_lists(dq_sa, p, workspace, L.dq_list);
     lists[n_lists++] = dq_sa;
@@ -392,6 +377,7 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
     dkdv_sa.loop_tile = bwd_dkdv_rows(p->head_dim);
     dkdv_sa.mode = 1;
     dkdv_sa.causal = p->causal;
+    dkdv_sa.bcast = p->broadcast_q;
     dkdv_sa.bcast_nq = p->broadcast_q ? p->total_q : 0;
     set_lists(dkdv_sa, p, workspace, L.dkdv_list);
     lists[n_lists++] = dkdv_sa;
@@ -426,18 +412,18 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
       ba.bcast_chunks = L.chunks;
       ba.bcast_chunk = cdiv_i(p->batch, L.chunks);
       ba.bcast_units = (int)(tiles_heads * ba.bcast_chunks);
-      TimedRegion tr(JFA_TIMING_BWD_DQ, stream);
+      if (ev && record(ev->bwd_dq_start, stream) != hipSuccess) return JFA_ERR_HIP;
       e = launch_bwd_dq(ba, p->head_dim, std::max(1, std::min(ba.bcast_units, dq_per_cu * cus)), stream);
-      tr.finish();
       if (e != hipSuccess) return JFA_ERR_HIP;
+      if (ev && record(ev->bwd_dq_stop, stream) != hipSuccess) return JFA_ERR_HIP;
     } else {
       ba.items = dq_sa.items;
       ba.queues = dq_sa.queues;
       const int64_t max_items = L.dq_list.max_items;
-      TimedRegion tr(JFA_TIMING_BWD_DQ, stream);
+      if (ev && record(ev->bwd_dq_start, stream) != hipSuccess) return JFA_ERR_HIP;
       e = launch_bwd_dq(ba, p->head_dim, (int)std::max<int64_t>(1, std::min<int64_t>((int64_t)dq_per_cu * cus, max_items)), stream);
-      tr.finish();
       if (e != hipSuccess) return JFA_ERR_HIP;
+      if (ev && record(ev->bwd_dq_stop, stream) != hipSuccess) return JFA_ERR_HIP;
     }
   }
 
@@ -446,10 +432,10 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
     ba.items = dkdv_sa.items;
     ba.queues = dkdv_sa.queues;
     const int64_t max_items = L.dkdv_list.max_items;
-    TimedRegion tr(JFA_TIMING_BWD_DKDV, stream);
+    if (ev && record(ev->bwd_dkdv_start, stream) != hipSuccess) return JFA_ERR_HIP;
     e = launch_bwd_dkdv(ba, p->head_dim, (int)std::max<int64_t>(1, std::min<int64_t>(cus, max_items)), stream);
-    tr.finish();
     if (e != hipSuccess) return JFA_ERR_HIP;
+    if (ev && record(ev->bwd_dkdv_stop, stream) != hipSuccess) return JFA_ERR_HIP;
   }
 
   if (p->broadcast_q && p->total_q > 0) {
@@ -514,49 +500,16 @@ jfa_status_t jfa_decode_paged(const jfa_decode_params_t* p, const void* q, const
   const float q_scale = (a.q_fp8 && p->q_scale > 0.f) ? p->q_scale : 1.f;
   a.v_scale = (a.kv_fp8 && p->v_scale > 0.f) ? p->v_scale : 1.f;
   a.scale_log2 = eff_scale(p->softmax_scale, p->head_dim) * 1.4426950408889634f * k_scale * q_scale;
-  TimedRegion tr(JFA_TIMING_DECODE, stream);
+  const jfa_kernel_events_t* ev = p->events;
+  if (ev && record(ev->decode_start, stream) != hipSuccess) return JFA_ERR_HIP;
   hipError_t e = launch_decode(a, p->head_dim, stream);
-  tr.finish();
   if (e != hipSuccess) return JFA_ERR_HIP;
+  if (ev && record(ev->decode_stop, stream) != hipSuccess) return JFA_ERR_HIP;
   if (splits > 1) {
     e = launch_decode_combine(a, p->head_dim, stream);
     if (e != hipSuccess) return JFA_ERR_HIP;
   }
   return JFA_OK;
-}
-
-jfa_status_t jfa_timing_enable(int enable) {
-  Timing& t = timing();
-  std::lock_guard<std::mutex> g(t.mu);
-  t.enabled = enable != 0;
-  return JFA_OK;
-}
-
-jfa_status_t jfa_timing_collect(double total_ms[JFA_TIMING_SLOTS], int64_t count[JFA_TIMING_SLOTS]) {
-  Timing& t = timing();
-  std::lock_guard<std::mutex> g(t.mu);
-  jfa_status_t st = JFA_OK;
-  for (int w = 0; w < JFA_TIMING_SLOTS; ++w) {
-    double ms_sum = 0.0;
-    int64_t n = 0;
-    for (size_t i = 0; i < t.start[w].size(); ++i) {
-      float ms = 0.f;
-      if (hipEventSynchronize(t.stop[w][i]) != hipSuccess ||
-          hipEventElapsedTime(&ms, t.start[w][i], t.stop[w][i]) != hipSuccess) {
-        st = JFA_ERR_HIP;
-      } else {
-        ms_sum += ms;
-        ++n;
-      }
-      hipEventDestroy(t.start[w][i]);
-      hipEventDestroy(t.stop[w][i]);
-    }
-    t.start[w].clear();
-    t.stop[w].clear();
-    if (total_ms) total_ms[w] = ms_sum;
-    if (count) count[w] = n;
-  }
-  return st;
 }
 
 }  // extern "C"

@@ -38,6 +38,7 @@
 // more than the repeated MFMA work.  Neither kernel refills an LDS stage while
 // any reader of it is unfinished (one barrier per stage), the single-buffer
 // K hazard described in the bug-hunting section of the B300 page.
+#include <algorithm>
 #include <type_traits>
 
 #include "jfa_internal.h"
@@ -88,6 +89,24 @@ hipError_t launch_bwd_pre(const BwdPreArgs& a, hipStream_t stream) {
   if (blocks < 1) blocks = 1;
   if (blocks > (1 << 30)) return hipErrorInvalidValue;
   hipLaunchKernelGGL(bwd_pre_kernel, dim3((unsigned)blocks), dim3(kPreThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------------------- zero fill
+// dK = dV = 0 for a broadcast-Q backward without query rows (no key sees a query).
+// n16 16-byte chunks; a fill kernel rather than a memset, so that a caller may
+// capture the call in a graph.
+__global__ __launch_bounds__(256) void zero_fill_kernel(u32x4* p, int64_t n16) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (int64_t)gridDim.x * 256)
+    p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+hipError_t launch_zero_fill(void* p, int64_t bytes, hipStream_t stream) {
+  if (bytes <= 0) return hipSuccess;
+  if (bytes % 16 != 0 || ((uintptr_t)p % 16) != 0) return hipErrorInvalidValue;
+  const int64_t n16 = bytes / 16;
+  const int64_t blocks = std::min<int64_t>((n16 + 255) / 256, 4096);
+  hipLaunchKernelGGL(zero_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, (u32x4*)p, n16);
   return hipGetLastError();
 }
 
@@ -162,10 +181,6 @@ __device__ __forceinline__ void staging_block(int tid, int row_blocks, int& rb, 
 }
 
 // ============================================================================= dK / dV
-#ifndef JFA_DKDV_PIPE
-#define JFA_DKDV_PIPE 1
-#endif
-
 // Head-dim chunking ("Cutting edge isn't plug-and-play: customising
 // FlashAttention-4 on B300", Phase 2): for d = 256 one work item owns the dK/dV
 // columns of one DC-wide slice of the head dimension.  S = Q K^T and dP = dO V^T
@@ -201,7 +216,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 dot_lds[2][DC * QTP];
   __shared__ __attribute__((aligned(16))) float lse_lds[2][BM];
   __shared__ __attribute__((aligned(16))) float dlt_lds[2][BM];
-  __shared__ int s_item;
+  __shared__ int s_item[2];   // claims alternate between the entries: a wave still
+  // reading claim k's entry has not passed the barrier that follows claim k + 1, so
+  // claim k + 2, the next write to that entry, cannot overtake the read even when
+  // item k + 1 has no tiles (and so no barrier of its own)
   __shared__ int s_queue[2 * kQueues];
 
   const int tid = threadIdx.x;
@@ -239,9 +257,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
   int home_q = blockIdx.x % kQueues, drained = 0;   // work-queue state (thread 0)
   load_queues(a.queues, s_queue);
   __syncthreads();
-  if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
+  if (tid == 0) s_item[0] = next_work_item(a.queues, s_queue, home_q, drained);
   __syncthreads();
-  int item = __builtin_amdgcn_readfirstlane(s_item);   // uniform: the item loads are scalar
+  int slot = 0;   // s_item entry of the current claim (uniform)
+  int item = __builtin_amdgcn_readfirstlane(s_item[0]);   // uniform: the item loads are scalar
   while (item >= 0) {
     const WorkItem e = a.items[item];
     const int g = e.h / T::NC;
@@ -431,7 +450,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
           dkt[db] = mfma32x32x16(*(const bf16x8*)(qtp + 16), sb1, dkt[db]);
         }
       };
-      if constexpr (BM == 64 && JFA_DKDV_PIPE) {
+      if constexpr (BM == 64) {
         // both query blocks' S/dP first: the second block's MFMAs run while the
         // first block's softmax occupies the VALU
         f32x16 s0, p0, s1, p1;
@@ -508,7 +527,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         }
       // Claim the next item before the global stores: waiting for the atomic's
       // result then waits for no store (the memory counter drains in order).
-      if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
+      if (tid == 0) s_item[slot ^ 1] = next_work_item(a.queues, s_queue, home_q, drained);
       __syncthreads();
       constexpr int CPR = DC / 8;                // 16-byte chunks per row
       static_assert(CPR % 2 == 0, "whole chunks per lane");
@@ -524,7 +543,8 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       }
     }
     __syncthreads();   // next item published; the epilogue blocks are read
-    item = __builtin_amdgcn_readfirstlane(s_item);
+    slot ^= 1;
+    item = __builtin_amdgcn_readfirstlane(s_item[slot]);
   }
 }
 
@@ -568,7 +588,10 @@ __global__ __launch_bounds__((DqTile<D>::NT), (DqTile<D>::WG_PER_CU)) void bwd_d
   __shared__ __attribute__((aligned(16))) __bf16 v_lds[NSTAGE][BN * KP];
   __shared__ __attribute__((aligned(16))) __bf16 kt_lds[NSTAGE][D * KTP];
   __shared__ __attribute__((aligned(16))) __bf16 ep_lds[T::EP_EL];
-  __shared__ int s_item;
+  __shared__ int s_item[2];   // claims alternate between the entries: a wave still
+  // reading claim k's entry has not passed the barrier that follows claim k + 1, so
+  // claim k + 2, the next write to that entry, cannot overtake the read even when
+  // item k + 1 has no tiles (and so no barrier of its own)
   __shared__ int s_queue[2 * kQueues];
 
   const int tid = threadIdx.x;
@@ -595,13 +618,13 @@ __global__ __launch_bounds__((DqTile<D>::NT), (DqTile<D>::WG_PER_CU)) void bwd_d
   // work queues; broadcast-Q owns (query tile, head, chunk of items) by block index.
   int bcast_item = blockIdx.x;
   int home_q = blockIdx.x % kQueues, drained = 0;   // work-queue state (thread 0)
-  int item = -1;
+  int item = -1, slot = 0;   // slot: s_item entry of the current claim (uniform)
   if (!BCAST) {   // broadcast-Q runs without a work list (a.queues is null)
     load_queues(a.queues, s_queue);
     __syncthreads();
-    if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
+    if (tid == 0) s_item[0] = next_work_item(a.queues, s_queue, home_q, drained);
     __syncthreads();
-    item = __builtin_amdgcn_readfirstlane(s_item);   // uniform: the item loads are scalar
+    item = __builtin_amdgcn_readfirstlane(s_item[0]);   // uniform: the item loads are scalar
   }
   for (;;) {
     int b_lo, b_hi, h, qtile, chunk = 0;
@@ -823,7 +846,7 @@ __global__ __launch_bounds__((DqTile<D>::NT), (DqTile<D>::WG_PER_CU)) void bwd_d
         }
       // claim the next item before any global store: waiting for the atomic's
       // result then waits for no store (the memory counter drains in order)
-      if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
+      if (tid == 0) s_item[slot ^ 1] = next_work_item(a.queues, s_queue, home_q, drained);
       __syncthreads();
       constexpr int CPR = D / 8;             // 16-byte chunks per row
       static_assert(CPR % 2 == 0, "whole chunks per lane");
@@ -835,7 +858,8 @@ __global__ __launch_bounds__((DqTile<D>::NT), (DqTile<D>::WG_PER_CU)) void bwd_d
           *(u32x4*)(a.dq + ((int64_t)(e_qbase + r) * a.hq + h) * D + 8 * col) = *(const u32x4*)(blk + row * EP + 8 * col);
       }
       __syncthreads();   // next item published; the LDS blocks are read
-      item = __builtin_amdgcn_readfirstlane(s_item);
+      slot ^= 1;
+      item = __builtin_amdgcn_readfirstlane(s_item[slot]);
     }
   }
 }
@@ -859,7 +883,7 @@ int bwd_dq_blocks_per_cu(int head_dim) {
 template <int D>
 static hipError_t launch_dkdv_d(const BwdArgs& a, int grid, hipStream_t stream) {
   const dim3 g(grid), blk(DkvTile<D>::NT);
-  if (a.bcast_nq > 0) hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true>), g, blk, 0, stream, a);
+  if (a.bcast) hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, true>), g, blk, 0, stream, a);
   else if (a.causal) hipLaunchKernelGGL((bwd_dkdv_kernel<D, true, false>), g, blk, 0, stream, a);
   else hipLaunchKernelGGL((bwd_dkdv_kernel<D, false, false>), g, blk, 0, stream, a);
   return hipGetLastError();
@@ -868,7 +892,7 @@ static hipError_t launch_dkdv_d(const BwdArgs& a, int grid, hipStream_t stream) 
 template <int D>
 static hipError_t launch_dq_d(const BwdArgs& a, int grid, hipStream_t stream) {
   const dim3 g(grid), blk(DqTile<D>::NT);
-  if (a.bcast_nq > 0) hipLaunchKernelGGL((bwd_dq_kernel<D, false, true>), g, blk, 0, stream, a);
+  if (a.bcast) hipLaunchKernelGGL((bwd_dq_kernel<D, false, true>), g, blk, 0, stream, a);
   else if (a.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true, false>), g, blk, 0, stream, a);
   else hipLaunchKernelGGL((bwd_dq_kernel<D, false, false>), g, blk, 0, stream, a);
   return hipGetLastError();

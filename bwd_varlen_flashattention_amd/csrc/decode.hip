@@ -48,9 +48,6 @@ struct DecOcc {
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
-#ifndef JFA_DECODE_LPT
-#define JFA_DECODE_LPT 1
-#endif
 constexpr int kLptMaxBatch = 256;   // one rank per thread
 
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -103,7 +100,7 @@ __global__ __launch_bounds__(256, (DecOcc<D, NCG>::WG_PER_CU)) void decode_kerne
   // kLptMaxBatch; larger ones keep the given order).
   __shared__ int s_b;
   int b = b_rank;
-  if (JFA_DECODE_LPT && a.batch <= kLptMaxBatch) {
+  if (a.batch <= kLptMaxBatch) {
     if (tid < a.batch) {
       const int lt = a.seqlens[tid];
       int rank = 0;

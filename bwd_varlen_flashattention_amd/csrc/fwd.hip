@@ -106,7 +106,10 @@ __global__ __launch_bounds__((FwdTile<D, FP8>::NT), (FwdTile<D, FP8>::WG_PER_CU)
   __shared__ __attribute__((aligned(16))) unsigned char k_raw[2][T::K_LDS_BYTES];
   __shared__ __attribute__((aligned(16))) __bf16 vt_lds[2][D * VTP];
   __shared__ __attribute__((aligned(16))) __bf16 ep_lds[T::EP_OWN];
-  __shared__ int s_item;
+  __shared__ int s_item[2];   // claims alternate between the entries: a wave still
+  // reading claim k's entry has not passed the barrier that follows claim k + 1, so
+  // claim k + 2, the next write to that entry, cannot overtake the read even when
+  // item k + 1 has no tiles (and so no barrier of its own)
   __shared__ int s_queue[2 * kQueues];
 
   const int tid = threadIdx.x;
@@ -141,9 +144,10 @@ __global__ __launch_bounds__((FwdTile<D, FP8>::NT), (FwdTile<D, FP8>::WG_PER_CU)
   int home_q = blockIdx.x % kQueues, drained = 0;   // work-queue state (thread 0)
   load_queues(a.queues, s_queue);
   __syncthreads();
-  if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
+  if (tid == 0) s_item[0] = next_work_item(a.queues, s_queue, home_q, drained);
   __syncthreads();
-  int item = __builtin_amdgcn_readfirstlane(s_item);   // uniform: the item loads are scalar
+  int slot = 0;   // s_item entry of the current claim (uniform)
+  int item = __builtin_amdgcn_readfirstlane(s_item[0]);   // uniform: the item loads are scalar
   while (item >= 0) {
     const WorkItem e = a.items[item];
     const int h = e.h;
@@ -386,7 +390,7 @@ __global__ __launch_bounds__((FwdTile<D, FP8>::NT), (FwdTile<D, FP8>::WG_PER_CU)
         }
       // claim the next item before any global store: waiting for the atomic's
       // result then waits for no store (the memory counter drains in order)
-      if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
+      if (tid == 0) s_item[slot ^ 1] = next_work_item(a.queues, s_queue, home_q, drained);
       __syncthreads();
       constexpr int CPR = D / 8;             // 16-byte chunks per row
       static_assert(CPR % 2 == 0, "whole chunks per lane");
@@ -397,7 +401,7 @@ __global__ __launch_bounds__((FwdTile<D, FP8>::NT), (FwdTile<D, FP8>::WG_PER_CU)
         if (r < lq) *(u32x4*)(o_row(r) + 8 * col) = *(const u32x4*)(blk + row * EP + 8 * col);
       }
     } else {
-      if (tid == 0) s_item = next_work_item(a.queues, s_queue, home_q, drained);
+      if (tid == 0) s_item[slot ^ 1] = next_work_item(a.queues, s_queue, home_q, drained);
       if (row_ok) {
         __bf16* op = o_row(my_row);
 #pragma unroll
@@ -417,7 +421,8 @@ __global__ __launch_bounds__((FwdTile<D, FP8>::NT), (FwdTile<D, FP8>::WG_PER_CU)
       a.lse[li] = lse;
     }
     __syncthreads();   // next item published; the LDS buffers are free for it
-    item = __builtin_amdgcn_readfirstlane(s_item);
+    slot ^= 1;
+    item = __builtin_amdgcn_readfirstlane(s_item[slot]);
   }
 }
 
@@ -456,10 +461,10 @@ int fwd_blocks_per_cu(int head_dim, bool fp8) { return fp8 ? fwd_wgs_t<true>(hea
 
 template <int D, bool FP8>
 static hipError_t launch_fwd_dt(const FwdArgs& a, int grid, hipStream_t stream) {
-  if (fwd_in_ilp_unit(D, a.causal && a.bcast_nq == 0)) return launch_fwd_ilp(a, D, FP8, grid, stream);
+  if (fwd_in_ilp_unit(D, a.causal && !a.bcast)) return launch_fwd_ilp(a, D, FP8, grid, stream);
   const dim3 g(grid), blk(FwdTile<D, FP8>::NT);
   if constexpr (!fwd_in_ilp_unit(D, false)) {
-    if (a.bcast_nq > 0)
+    if (a.bcast)
       hipLaunchKernelGGL((fwd_kernel<D, false, true, FP8>), g, blk, 0, stream, a);
     else if (a.causal) {
       if constexpr (!fwd_in_ilp_unit(D, true)) hipLaunchKernelGGL((fwd_kernel<D, true, false, FP8>), g, blk, 0, stream, a);
@@ -494,10 +499,10 @@ hipError_t launch_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t stre
 template <int D, bool FP8>
 static hipError_t launch_fwd_ilp_dt(const FwdArgs& a, int grid, hipStream_t stream) {
   const dim3 g(grid), blk(FwdTile<D, FP8>::NT);
-  const bool causal = a.causal && a.bcast_nq == 0;
+  const bool causal = a.causal && !a.bcast;
   if (!fwd_in_ilp_unit(D, causal)) return hipErrorInvalidValue;
   if constexpr (fwd_in_ilp_unit(D, false)) {
-    if (a.bcast_nq > 0)
+    if (a.bcast)
       hipLaunchKernelGGL((fwd_kernel<D, false, true, FP8>), g, blk, 0, stream, a);
     else if (!causal)
       hipLaunchKernelGGL((fwd_kernel<D, false, false, FP8>), g, blk, 0, stream, a);

@@ -52,7 +52,8 @@ struct SchedArgs {
   int32_t loop_tile;        // rows per tile on the inner-loop axis
   int32_t mode;             // 0: query-stationary (one item per query head), 1: key-stationary (per KV head)
   int32_t causal;
-  int32_t bcast_nq;         // > 0: broadcast-Q, every item has Lq = bcast_nq
+  int32_t bcast;            // 1: broadcast-Q (cu_q is not read)
+  int32_t bcast_nq;         // broadcast-Q: every item has Lq = bcast_nq
   int32_t n_buckets;        // cost buckets (costs above are clamped into the last one)
   int32_t max_items;        // capacity of `items`
   int32_t* scratch;         // 4 * batch * groups_per_seq ints (used when they do not fit in LDS)
@@ -79,7 +80,8 @@ struct FwdArgs {
   const WorkItem* items;
   WorkQueues* queues;
   int32_t hq, hkv, group;   // group = hq / hkv
-  int32_t bcast_nq;         // > 0: broadcast-Q
+  int32_t bcast;            // 1: broadcast-Q
+  int32_t bcast_nq;         // broadcast-Q: query rows shared by every item
   int32_t total_q;          // LSE row stride for self-attention
   int32_t causal;
   float scale_log2;         // softmax scale * log2(e) (e4m3: times the Q and K scales)
@@ -125,7 +127,8 @@ struct BwdArgs {
   WorkQueues* queues;
   int32_t batch;
   int32_t hq, hkv, group;
-  int32_t bcast_nq;
+  int32_t bcast;            // 1: broadcast-Q
+  int32_t bcast_nq;         // broadcast-Q: query rows shared by every item
   int32_t bcast_chunk;      // broadcast-Q dQ: items per chunk
   int32_t bcast_chunks;     // number of chunks
   int32_t bcast_units;      // query tiles * heads * chunks
@@ -151,6 +154,8 @@ struct DqConvertArgs {
   float scale;
 };
 hipError_t launch_dq_convert(const DqConvertArgs& a, hipStream_t stream);
+// bytes (a multiple of 16, 16-byte aligned) of zeros at p
+hipError_t launch_zero_fill(void* p, int64_t bytes, hipStream_t stream);
 
 // Decode.
 struct DecodeArgs {

@@ -115,7 +115,7 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedBatch batch) 
   // down so the scan sorts longest first)
   for (int gi = tid; gi < n_groups; gi += kSchedThreads) {
     const int b = gi / a.groups_per_seq;
-    const int lq = a.bcast_nq > 0 ? a.bcast_nq : a.cu_q[b + 1] - a.cu_q[b];
+    const int lq = a.bcast ? a.bcast_nq : a.cu_q[b + 1] - a.cu_q[b];
     const int lk = a.cu_k[b + 1] - a.cu_k[b];
     const int nt = cdiv(a.mode == 0 ? lq : lk, a.stat_tile);
     const int cost = tiles_cost(a, lq, lk, nt);
@@ -205,8 +205,8 @@ __global__ __launch_bounds__(kSchedThreads) void sched_kernel(SchedBatch batch) 
     const int nt = n / per_tile;
     const int base = q_start[q] + r_off[r];
     const int end = min(q_start[q] + q_size[q], base + n);
-    const int q_base = a.bcast_nq > 0 ? 0 : a.cu_q[b];
-    const int lq = a.bcast_nq > 0 ? a.bcast_nq : a.cu_q[b + 1] - q_base;
+    const int q_base = a.bcast ? 0 : a.cu_q[b];
+    const int lq = a.bcast ? a.bcast_nq : a.cu_q[b + 1] - q_base;
     const int k_base = a.cu_k[b];
     const int lk = a.cu_k[b + 1] - k_base;
     for (int idx = 0; base + idx < end; ++idx) {

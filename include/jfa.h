@@ -25,9 +25,9 @@
  *   - The workspace pointer must be aligned to 256 bytes (torch and hipMalloc
  *     allocations are); a misaligned one is rejected with
  *     JFA_ERR_INVALID_ARGUMENT.
- *   - The caller owns all memory (inputs, outputs, workspace).  The library
- *     allocates no device memory and keeps no state beyond a per-device cache of
- *     the compute-unit count.  Calls with distinct workspaces may run
+ *   - The caller owns all memory (inputs, outputs, workspace) and the optional
+ *     timing events.  The library allocates no device memory and keeps no state
+ *     beyond a per-device cache of the compute-unit count.  Calls with distinct workspaces may run
  *     concurrently on different streams.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     runs asynchronously: no call synchronises with the host.
@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define JFA_ABI_VERSION 3
+#define JFA_ABI_VERSION 4
 
 /* Same type as hipStream_t, declared without including the HIP headers. */
 struct ihipStream_t;
@@ -67,6 +67,26 @@ typedef enum {
 
 /* Element types of the q/k/v (and KV-cache) tensors. */
 enum { JFA_DTYPE_BF16 = 0, JFA_DTYPE_FP8_E4M3 = 1 };
+
+/*
+ * Optional kernel timing, owned by the caller.  Every member is a hipEvent_t that
+ * the caller created (passed as void*), or NULL.  A call whose params point at
+ * this struct records `*_start` on its stream right before it launches the named
+ * kernel and `*_stop` right after, so hipEventElapsedTime(start, stop) is that
+ * kernel's time; a call never launches the named kernel leaves its pair alone.
+ * The library keeps no reference to the events.  A failed record returns
+ * JFA_ERR_HIP.
+ */
+typedef struct {
+  void* fwd_start;        /* jfa_fwd: the attention kernel */
+  void* fwd_stop;
+  void* bwd_dq_start;     /* jfa_bwd: the dQ kernel */
+  void* bwd_dq_stop;
+  void* bwd_dkdv_start;   /* jfa_bwd: the dK/dV kernel */
+  void* bwd_dkdv_stop;
+  void* decode_start;     /* jfa_decode_paged: the split-KV kernel */
+  void* decode_stop;
+} jfa_kernel_events_t;
 
 /*
  * Problem description for jfa_fwd / jfa_bwd.
@@ -104,6 +124,7 @@ typedef struct {
   float q_scale;          /* e4m3 only: per-tensor scales, each tensor's value = scale x its */
   float k_scale;          /* e4m3 value; finite and > 0.  Ignored for bf16 */
   float v_scale;
+  const jfa_kernel_events_t* events;   /* optional kernel timing (NULL: none) */
 } jfa_attn_params_t;
 
 /* Bytes of workspace jfa_fwd needs for this problem (0 if the params are invalid). */
@@ -141,7 +162,10 @@ size_t jfa_bwd_workspace_size(const jfa_attn_params_t* p);
  * are deterministic (no atomics): in broadcast-Q mode dQ, the sum over all
  * items, is accumulated per chunk of items in fp32 and the chunk partials are
  * added in a fixed order.  Keys that no query sees get dK = dV = 0; queries
- * that see no key get dQ = 0.  For d = 256 the dK/dV work is split along the
+ * that see no key get dQ = 0.  A broadcast-Q problem with Nq = total_q = 0
+ * writes dK = dV = 0 (q, o, lse, dout, dq and cu_seqlens_q are not read and may
+ * be NULL); a self-attention problem with total_q = 0 likewise writes dK = dV =
+ * 0 through the regular kernels.  For d = 256 the dK/dV work is split along the
  * head dimension ("Cutting edge isn't plug-and-play", Phase 2 chunked
  * backward): each slice of 128 columns is a work item of its own that rebuilds
  * S and dP from the whole head; the results are the same.
@@ -202,6 +226,7 @@ typedef struct {
   float v_scale;              /* fp8 caches: V = v_scale * e4m3 value (<= 0 means 1) */
   int32_t q_dtype;            /* JFA_DTYPE_BF16 or JFA_DTYPE_FP8_E4M3 (q element type) */
   float q_scale;              /* e4m3 q: Q = q_scale * e4m3 value (<= 0 means 1) */
+  const jfa_kernel_events_t* events;   /* optional kernel timing (NULL: none) */
 } jfa_decode_params_t;
 
 size_t jfa_decode_workspace_size(const jfa_decode_params_t* p);
@@ -220,21 +245,6 @@ const char* jfa_status_string(jfa_status_t s);
 
 /* JFA_ABI_VERSION of the built library. */
 int jfa_abi_version(void);
-
-/*
- * Optional kernel timing.  While enabled, every call records a pair of HIP
- * events on its stream around the launch of each of its main kernels: the
- * attention kernel of jfa_fwd (slot JFA_TIMING_FWD), the dQ and the dK/dV
- * kernels of jfa_bwd (JFA_TIMING_BWD_DQ, JFA_TIMING_BWD_DKDV) and the split
- * kernel of jfa_decode_paged (JFA_TIMING_DECODE).  jfa_timing_collect() waits
- * for the recorded events, writes per slot the summed elapsed milliseconds into
- * total_ms[slot] and the number of launches into count[slot], then releases
- * them.  Either output may be NULL.  Intended for benchmarks; off by default.
- */
-enum { JFA_TIMING_FWD = 0, JFA_TIMING_BWD_DQ = 1, JFA_TIMING_BWD_DKDV = 2, JFA_TIMING_DECODE = 3,
-       JFA_TIMING_SLOTS = 4 };
-jfa_status_t jfa_timing_enable(int enable);
-jfa_status_t jfa_timing_collect(double total_ms[JFA_TIMING_SLOTS], int64_t count[JFA_TIMING_SLOTS]);
 
 #ifdef __cplusplus
 }

@@ -29,7 +29,7 @@ def test_header_declares_and_library_exports():
     for n in names:
         assert hasattr(lib, n), f"missing export {n}"
     assert set(names) == set(L.EXPORTS)
-    assert lib.jfa_abi_version() == 3
+    assert lib.jfa_abi_version() == L.ABI_VERSION == 4
 
 
 def test_header_compiles_as_c(tmp_path):
@@ -176,3 +176,38 @@ def test_fp8_forward_only():
     d = ctypes.c_void_p(256)
     st = lib.jfa_bwd(ctypes.byref(p), d, d, d, d, d, d, d, d, d, d, d, d, 1 << 20, None)
     assert st == L.JFA_ERR_UNSUPPORTED
+
+
+def test_empty_broadcast_query_workspace_query():
+    """Broadcast-Q with Nq = 0 (and keys present): the workspace queries answer without
+    dividing by the zero query-tile count, and the call's host checks pass."""
+    L, lib = _lib()
+    p = _params(L, broadcast_q=1, total_q=0, total_k=10)
+    assert lib.jfa_fwd_workspace_size(ctypes.byref(p)) > 0
+    assert lib.jfa_bwd_workspace_size(ctypes.byref(p)) > 0
+    # nothing to write in the forward: returns before any launch
+    assert lib.jfa_fwd(ctypes.byref(p), None, None, None, None, ctypes.c_void_p(256), None, None,
+                       ctypes.c_void_p(256), 1 << 20, None) == L.JFA_OK
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """The ctypes structs have the sizes and field offsets the C compiler gives the header's."""
+    L, _ = _lib()
+    structs = {"jfa_attn_params_t": L.AttnParams, "jfa_decode_params_t": L.DecodeParams,
+               "jfa_kernel_events_t": L.KernelEventsStruct}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "jfa.h"', "int main(void) {"]
+    for cname, cls in structs.items():
+        lines.append(f'  printf("{cname} size %zu\\n", sizeof({cname}));')
+        for f, _t in cls._fields_:
+            lines.append(f'  printf("{cname} {f} %zu\\n", offsetof({cname}, {f}));')
+    lines += ["  return 0;", "}"]
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines) + "\n")
+    exe = tmp_path / "layout"
+    assert os.system(f"gcc -std=c99 -I {os.path.dirname(HEADER)} {src} -o {exe}") == 0
+    out = os.popen(str(exe)).read().split("\n")
+    got = {tuple(l.split()[:2]): int(l.split()[2]) for l in out if l.strip()}
+    for cname, cls in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(cls), cname
+        for f, _t in cls._fields_:
+            assert got[(cname, f)] == getattr(cls, f).offset, (cname, f)

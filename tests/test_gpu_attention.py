@@ -7,7 +7,7 @@ import pytest
 
 import oracle
 import workloads
-from parity import check_grad, check_lse, check_o, dev, host
+from parity import check_grad, check_lse, check_o, dev, host, oracle_bcast_full, oracle_self_full
 
 pytestmark = pytest.mark.gpu
 
@@ -148,37 +148,95 @@ def test_outputs_overwritten(jfa):
     _compare_full((host(o), host(lse), host(dq), host(dk), host(dv)), _oracle_self(inp))
 
 
+# ----------------------------------------------------------------------------- guarded outputs
+# Every output (and the workspace) lives in the middle of a larger buffer whose
+# guard bands before and after must come back untouched: NaN for the outputs,
+# a byte pattern for the workspace.  The outputs themselves start as NaN, so a
+# row the kernels never write fails the comparison.
+GUARD_ELEMS = 1 << 16
+GUARD_BYTES = 1 << 16
+WS_PATTERN = 0xA5
+
+
+class Guarded:
+    def __init__(self, shape, dtype, fill=float("nan")):
+        n = int(np.prod(shape))
+        g = GUARD_BYTES if dtype == torch.uint8 else GUARD_ELEMS
+        self.full = torch.full((n + 2 * g,), fill, dtype=dtype, device="cuda")
+        self.lo, self.hi = g, g + n
+        self.fill = fill
+        self.t = self.full[self.lo:self.hi].view(shape)
+
+    def intact(self):
+        outside = torch.cat([self.full[:self.lo], self.full[self.hi:]])
+        if self.full.dtype == torch.uint8:
+            return bool((outside == self.fill).all())
+        return bool(torch.isnan(outside.float()).all())
+
+
+def _run_guarded(jfa, inp, bcast=False):
+    """Forward + backward into guarded NaN-filled outputs and guarded workspaces."""
+    q, k, v, do = (dev(x, torch) for x in (inp.q, inp.k, inp.v, inp.do))
+    ck = dev(inp.cu_k, torch)
+    cq = None if bcast else dev(inp.cu_q, torch)
+    causal = False if bcast else inp.causal
+    mq = inp.q.shape[0] if bcast else inp.max_len_q
+    nb = len(inp.cu_k) - 1
+    o_shape = (nb,) + tuple(q.shape) if bcast else tuple(q.shape)
+    lse_shape = (nb, q.shape[1], q.shape[0]) if bcast else (q.shape[1], q.shape[0])
+    o, lse = Guarded(o_shape, torch.bfloat16), Guarded(lse_shape, torch.float32)
+    wsf = Guarded((jfa.jfa_fwd_workspace_size(q, k, ck, mq, inp.max_len_k, causal, bcast),), torch.uint8, WS_PATTERN)
+    wsb = Guarded((jfa.jfa_bwd_workspace_size(q, k, ck, mq, inp.max_len_k, causal, bcast),), torch.uint8, WS_PATTERN)
+    jfa.jfa_fwd(q, k, v, cq, ck, mq, inp.max_len_k, causal, broadcast_q=bcast, out=o.t, lse=lse.t, workspace=wsf.t)
+    dq, dk, dv = Guarded(tuple(q.shape), torch.bfloat16), Guarded(tuple(k.shape), torch.bfloat16), \
+        Guarded(tuple(v.shape), torch.bfloat16)
+    jfa.jfa_bwd(q, k, v, o.t, lse.t, do, cq, ck, mq, inp.max_len_k, causal, broadcast_q=bcast,
+                dq=dq.t, dk=dk.t, dv=dv.t, workspace=wsb.t)
+    torch.cuda.synchronize()
+    for name, g in (("O", o), ("LSE", lse), ("dQ", dq), ("dK", dk), ("dV", dv), ("fwd workspace", wsf),
+                    ("bwd workspace", wsb)):
+        assert g.intact(), f"{name}: guard band overwritten"
+    return host(o.t), host(lse.t), host(dq.t), host(dk.t), host(dv.t)
+
+
 @pytest.mark.parametrize("s", [0.9, 0.5, 0.1])
-def test_gem_full_size_sampled(jfa, s):
-    """GEM config at full size (256 sequences, 8 heads, d=128); oracle on a sample of sequences."""
+def test_gem_full_size(jfa, s):
+    """GEM config at full size (256 sequences, 8 heads, d = 128): O, LSE, dQ, dK and dV
+    of every sequence against the oracle, outputs guarded and NaN-prefilled."""
     inp = workloads.gem(0, s)
     _say(f"gem s={s} T={inp.q.shape[0]}")
-    got = _run_self(jfa, inp)
-    lens = np.diff(inp.cu_q)
-    order = np.argsort(lens)
-    seqs = sorted(set(order[:3].tolist() + order[-3:].tolist() + [0, 1, 128, 255]))
-    _compare_sampled(inp, got, _oracle_self(inp, seqs=seqs))
-    assert np.isfinite(got[0]).all() and np.isfinite(got[2]).all()
+    got = _run_guarded(jfa, inp)
+    _compare_full(got, oracle_self_full(oracle, inp))
 
 
 @pytest.mark.parametrize("d", [128, 96])
 def test_dense_causal_full_size_sampled(jfa, d):
-    """4 x 8192 causal, 32 heads, at full size; oracle on sequence 0, heads {0, 17, 31}."""
+    """4 x 8192 causal, 32 heads, at full size; the oracle on one head of every
+    sequence (and two more of sequence 0), whole rows and keys of each."""
     inp = workloads.dense_causal(0, head_dim=d)
     _say(f"dense causal d={d}")
     got = _run_self(jfa, inp)
     L = 8192
-    for h in (0, 17, 31):
-        args = [x[:L, h:h + 1].astype(np.float64) for x in (inp.q, inp.k, inp.v)]
+    picks = [(0, 0), (0, 17), (0, 31), (1, 9), (2, 22), (3, 5)]
+
+    def one(bh):
+        b, h = bh
+        sl = slice(b * L, (b + 1) * L)
+        args = [x[sl, h:h + 1].astype(np.float64) for x in (inp.q, inp.k, inp.v)]
         cu = np.array([0, L])
         ro, rl = oracle.attention_forward(*args, cu, cu, True)
-        rdq, rdk, rdv = oracle.attention_backward(*args, inp.do[:L, h:h + 1].astype(np.float64), cu, cu, True)
-        check_o(got[0][:L, h:h + 1], ro, f"O[h{h}]")
-        check_lse(got[1][h:h + 1, :L], rl, f"LSE[h{h}]")
-        check_grad(got[2][:L, h:h + 1], rdq, f"dQ[h{h}]")
-        check_grad(got[3][:L, h:h + 1], rdk, f"dK[h{h}]")
-        check_grad(got[4][:L, h:h + 1], rdv, f"dV[h{h}]")
-        _say(f"  head {h} ok")
+        rdq, rdk, rdv = oracle.attention_backward(*args, inp.do[sl, h:h + 1].astype(np.float64), cu, cu, True)
+        return ro, rl, rdq, rdk, rdv
+
+    from parity import _pool_map
+    for (b, h), (ro, rl, rdq, rdk, rdv) in zip(picks, _pool_map(one, picks)):
+        sl = slice(b * L, (b + 1) * L)
+        check_o(got[0][sl, h:h + 1], ro, f"O[seq {b} h{h}]")
+        check_lse(got[1][h:h + 1, sl], rl, f"LSE[seq {b} h{h}]")
+        check_grad(got[2][sl, h:h + 1], rdq, f"dQ[seq {b} h{h}]")
+        check_grad(got[3][sl, h:h + 1], rdk, f"dK[seq {b} h{h}]")
+        check_grad(got[4][sl, h:h + 1], rdv, f"dV[seq {b} h{h}]")
+        _say(f"  seq {b} head {h} ok")
 
 
 def _run_bcast(jfa, inp):
@@ -210,11 +268,27 @@ def test_broadcast_q(jfa, nq, lengths, hq, hkv):
     _compare_full(_run_bcast(jfa, inp), _oracle_bcast(inp))
 
 
-def test_broadcast_q_config_s09(jfa):
-    """Broadcast-Q config (Nq=256, 512 items, 4 heads, d=128) at sparsity 0.9, full tensors."""
-    inp = workloads.broadcast_q(0, 0.9)
-    _say(f"broadcast config s=0.9 Tk={inp.k.shape[0]}")
-    _compare_full(_run_bcast(jfa, inp), _oracle_bcast(inp))
+@pytest.mark.parametrize("s", [0.9, 0.5, 0.1])
+def test_broadcast_q_config(jfa, s):
+    """Broadcast-Q config (Nq = 256, 512 items, 4 heads, d = 128) at full size, whole
+    tensors, outputs guarded and NaN-prefilled."""
+    inp = workloads.broadcast_q(0, s)
+    _say(f"broadcast config s={s} Tk={inp.k.shape[0]}")
+    _compare_full(_run_guarded(jfa, inp, bcast=True), oracle_bcast_full(oracle, inp))
+
+
+def test_broadcast_q_without_queries(jfa):
+    """Nq = 0: no key is seen by a query, so dK = dV = 0 (outputs start as NaN)."""
+    inp = workloads.broadcast(8, 1, [5, 0, 130], 4, 2, 128)
+    k, v = dev(inp.k, torch), dev(inp.v, torch)
+    q = torch.empty((0, 4, 128), dtype=torch.bfloat16, device="cuda")
+    ck = dev(inp.cu_k, torch)
+    o = torch.empty((3, 0, 4, 128), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((3, 4, 0), dtype=torch.float32, device="cuda")
+    dk, dv = torch.full_like(k, float("nan")), torch.full_like(v, float("nan"))
+    jfa.jfa_bwd(q, k, v, o, lse, o, None, ck, 0, 130, False, broadcast_q=True, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    assert (dk == 0).all() and (dv == 0).all()
 
 
 def test_broadcast_dq_is_sum_of_items(jfa):
