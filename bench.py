@@ -265,8 +265,9 @@ def pmc_summary(fetch_db: str, write_db: str, copy_mib: int, out: str):
     print("\n".join(lines))
 
 
-COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_MFMA", "SQ_INSTS_LDS",
-            "SQ_INSTS_VALU_TRANS_F32", "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CU_CYCLES", "SQ_WAVES", "GRBM_GUI_ACTIVE")
+COUNTERS = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16", "SQ_INSTS_MFMA",
+            "SQ_INSTS_LDS", "SQ_INSTS_VALU_TRANS_F32", "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE")
+XCDS, CUS, SIMDS_PER_CU = 8, 256, 4
 
 
 def counter_summary(db: str, out: str):
@@ -299,36 +300,41 @@ def counter_summary(db: str, out: str):
         "",
         "Per launch (mean over the run's launches of each kernel).  Derived columns:",
         "",
-        "* `MFMA TFLOP/s` = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16 / launch duration (executed bf16 MFMA work; the "
-        "duration is the dispatch's own, taken with the counters on);",
-        "* `MFMA util` = that rate / 2516.6 TFLOP/s (dense bf16 peak);",
-        "* `MFMA busy` = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 256 CUs x 4 SIMDs);",
+        "* `MFMA TFLOP/s` = 512 x (SQ_INSTS_VALU_MFMA_MOPS_BF16 + SQ_INSTS_VALU_MFMA_MOPS_F16) / launch duration "
+        "(executed 16-bit MFMA work: S and the backward on bf16, P V on fp16; the duration is the dispatch's own, "
+        "taken with the counters on);",
+        "* `MFMA util` = that rate / 2516.6 TFLOP/s (dense bf16/fp16 peak at 2.4 GHz);",
+        "* `clock` = GRBM_GUI_ACTIVE / 8 XCDs / duration (GHz): the engine clock the kernel actually ran at;",
+        "* `MFMA busy` = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 256 CUs x 4 SIMDs): the fraction of "
+        "SIMD cycles the matrix core was busy, at the actual clock (the counter sums over SIMDs);",
         "* `exec/alg` = executed MFMA flops / the kernel's algorithmic flops (fwd 4d, dK/dV 8d, dQ 2d per pair "
         "and head: the dQ kernel recomputes S and dP, 6d executed);",
         "* `LDS/MFMA` = SQ_INSTS_LDS / SQ_INSTS_MFMA; `exp/MFMA` = SQ_INSTS_VALU_TRANS_F32 / SQ_INSTS_MFMA;",
         "* `bank confl/LDS` = SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS (conflict cycles per LDS instruction).",
         "",
-        "| workload | kernel | ms | MFMA TFLOP/s | MFMA util | MFMA busy | exec/alg | SQ_INSTS_MFMA | LDS/MFMA | "
+        "| workload | kernel | ms | MFMA TFLOP/s | MFMA util | clock | MFMA busy | exec/alg | SQ_INSTS_MFMA | LDS/MFMA | "
         "exp/MFMA | bank confl/LDS |",
-        "|---|---|---|---|---|---|---|---|---|---|---|",
+        "|---|---|---|---|---|---|---|---|---|---|---|---|",
     ]
     rec = {}
     for (wl, slot), ds in sorted(groups.items()):
         m = {c: sum(val[d][c] for d in ds) / len(ds) for c in COUNTERS}
         ms = sum(dur[d] for d in ds) / len(ds) * 1e-6
-        flops = 512.0 * m["SQ_INSTS_VALU_MFMA_MOPS_BF16"]
+        flops = 512.0 * (m["SQ_INSTS_VALU_MFMA_MOPS_BF16"] + m["SQ_INSTS_VALU_MFMA_MOPS_F16"])
         rate = flops / (ms * 1e-3) if ms > 0 else 0.0
-        busy = m["SQ_VALU_MFMA_BUSY_CYCLES"] / max(1.0, m["GRBM_GUI_ACTIVE"] * 256 * 4)
+        cyc = m["GRBM_GUI_ACTIVE"] / XCDS
+        clock = cyc / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+        busy = m["SQ_VALU_MFMA_BUSY_CYCLES"] / max(1.0, cyc * CUS * SIMDS_PER_CU)
         a = alg.get(wl, {}).get(slot)
         mf = max(1.0, m["SQ_INSTS_MFMA"])
-        row = {"ms": ms, "mfma_tflops": rate / 1e12, "mfma_util": rate / peak, "mfma_busy": busy,
+        row = {"ms": ms, "mfma_tflops": rate / 1e12, "mfma_util": rate / peak, "clock_ghz": clock, "mfma_busy": busy,
                "exec_over_alg": flops / a if a else None, "lds_per_mfma": m["SQ_INSTS_LDS"] / mf,
                "exp_per_mfma": m["SQ_INSTS_VALU_TRANS_F32"] / mf,
                "bank_conflict_per_lds": m["SQ_LDS_BANK_CONFLICT"] / max(1.0, m["SQ_INSTS_LDS"]),
                "counters": m}
         rec.setdefault(wl, {})[slot] = row
         ea = f"{row['exec_over_alg']:.2f}" if a else "-"
-        lines.append(f"| {wl} | {slot} | {ms:.3f} | {rate / 1e12:.1f} | {rate / peak:.3f} | {busy:.3f} | {ea} | "
+        lines.append(f"| {wl} | {slot} | {ms:.3f} | {rate / 1e12:.1f} | {rate / peak:.3f} | {clock:.2f} | {busy:.3f} | {ea} | "
                      f"{m['SQ_INSTS_MFMA']:.4g} | {row['lds_per_mfma']:.2f} | {row['exp_per_mfma']:.2f} | "
                      f"{row['bank_conflict_per_lds']:.3f} |")
     lines += ["", "Raw counters per launch:", "", "| workload | kernel | " + " | ".join(COUNTERS) + " |",
@@ -470,7 +476,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--page-size", type=int, default=16)
     ap.add_argument("--extra-steps", type=int, default=10, help="timed calls of each extra workload (GEM, broadcast-Q)")
-    ap.add_argument("--cpu-sample", type=int, default=1, help="heads of sequence 0 in the oracle timing sample (0 = skip)")
+    ap.add_argument("--cpu-sample", type=int, default=16, help="heads of sequence 0 in the oracle timing sample (0 = skip)")
     ap.add_argument("--sweep", action="store_true", help="one JSON line per workload (GEM s, broadcast-Q, dense, decode)")
     ap.add_argument("--copy-calibration-mib", type=int, default=1024,
                     help="run one device copy of this size after timing (reference for HBM byte counters)")

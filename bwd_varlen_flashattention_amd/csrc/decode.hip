@@ -12,13 +12,18 @@
 // 16 keys of a tile:
 //   S^T[key][q]  = K Q^T      v_mfma_f32_16x16x32_bf16, A = K rows from LDS
 //   online softmax over the 16 keys x query column (per-lane + cross-lane)
-//   O^T[d][q]   += V^T P^T    v_mfma_f32_16x16x16_bf16, A = V through the
-//                             transposed LDS read, B = P^T straight from the
-//                             S^T accumulator
+//   O^T[d][q]   += V^T P^T    v_mfma_f32_16x16x16_f16, A = V (staged as fp16)
+//                             through the transposed LDS read, B = P^T rounded
+//                             to fp16 straight from the S^T accumulator (P keeps
+//                             11 significant bits; a unit whose V holds a value
+//                             beyond the fp16 range is computed again with P V
+//                             in bf16, as in the forward)
 // The four waves' (max, sum, accumulator) states are merged through LDS at the
 // end.  With one split the result is final (bf16 O, LSE); otherwise each split
 // leaves its normalised fp32 partial and its LSE, and decode_combine merges the
 // partials with weights exp(LSE_s - LSE).
+#include <type_traits>
+
 #include "jfa_internal.h"
 #include "device_common.h"
 
@@ -53,17 +58,20 @@ constexpr int kLptMaxBatch = 256;   // one rank per thread
 __device__ __forceinline__ f32x4 mfma16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ f32x4 mfma16x16x16(bf16x4 a, bf16x4 b, f32x4 c) {
+__device__ __forceinline__ f32x4 mfma16x16x16_f16(f16x4 a, f16x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x16_bf16(bf16x4 a, bf16x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a), __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
 }
 
 // NCG: 16-column query groups per workgroup (1 or 2).  A workgroup handles up to 16*NCG
 // query columns (token, query head of the GQA group) of one (sequence, KV head,
 // split); every K and V fragment it reads from LDS feeds all of its groups.
-// FP8: the KV cache holds OCP e4m3 bytes; rows are widened to bf16 (exactly:
-// every e4m3 value is a bf16 value) when they are written to LDS, and the
-// per-tensor scales are applied to the scores (K, folded into scale_log2 by the
-// host) and to the output (V).
+// FP8: the KV cache holds OCP e4m3 bytes; rows are widened exactly (every e4m3
+// value is a bf16 and an fp16 value; K to bf16, V to fp16) when they are written
+// to LDS, and the per-tensor scales are applied to the scores (K, folded into
+// scale_log2 by the host) and to the output (V).
 template <int D, int NCG, bool FP8>
 __global__ __launch_bounds__(256, (DecOcc<D, NCG>::WG_PER_CU)) void decode_kernel(DecodeArgs a) {
   using T = DecTile<D>;
@@ -99,20 +107,21 @@ __global__ __launch_bounds__(256, (DecOcc<D, NCG>::WG_PER_CU)) void decode_kerne
   // rank is computed from the KV lengths by every workgroup (batches up to
   // kLptMaxBatch; larger ones keep the given order).
   __shared__ int s_b;
+  // set when the fp16 accumulation was not finite (see the recomputation below)
+  __shared__ int s_big;
+  if (tid == 0) s_big = 0;
   int b = b_rank;
-  if (a.batch <= kLptMaxBatch) {
-    if (tid < a.batch) {
-      const int lt = a.seqlens[tid];
-      int rank = 0;
-      for (int j = 0; j < a.batch; ++j) {
-        const int lj = a.seqlens[j];
-        rank += (lj > lt || (lj == lt && j < tid)) ? 1 : 0;
-      }
-      if (rank == b_rank) s_b = tid;
+  if (a.batch <= kLptMaxBatch && tid < a.batch) {
+    const int lt = a.seqlens[tid];
+    int rank = 0;
+    for (int j = 0; j < a.batch; ++j) {
+      const int lj = a.seqlens[j];
+      rank += (lj > lt || (lj == lt && j < tid)) ? 1 : 0;
     }
-    __syncthreads();
-    b = s_b;
+    if (rank == b_rank) s_b = tid;
   }
+  __syncthreads();
+  if (a.batch <= kLptMaxBatch) b = s_b;
   const int L = a.seqlens[b];
   const int chunk = cdiv(cdiv(L, a.splits), BN) * BN;
   const int k_lo = s * chunk;
@@ -189,80 +198,127 @@ __global__ __launch_bounds__(256, (DecOcc<D, NCG>::WG_PER_CU)) void decode_kerne
       else { hi[2 * (w2 - 2)] = u.x; hi[2 * (w2 - 2) + 1] = u.y; }
     }
   };
-  auto store_lds = [&]() {
+  // F16 (a std::bool_constant): V is written as fp16 (e4m3 always is; a bf16
+  // value beyond the fp16 range becomes infinite), otherwise as bf16.
+  auto store_lds = [&](auto f16_tag) {
+    constexpr bool F16 = decltype(f16_tag)::value;
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
       const int id = tid + i * T::NT;
       if (BN * CHL % T::NT == 0 || id < BN * CHL) {
         const int r = id / CHL, c = id % CHL;
         if constexpr (FP8) {
-          u32x4 k0, k1, v0, v1;
+          u32x4 k0, k1;
           widen(kr[i], k0, k1);
-          widen(vr[i], v0, v1);
+          const u32x4 v0 = widen_e4m3x8_f16(uint2{vr[i][0], vr[i][1]});
+          const u32x4 v1 = widen_e4m3x8_f16(uint2{vr[i][2], vr[i][3]});
           *(u32x4*)&k_lds[r * KP + c * 16] = k0;
           *(u32x4*)&k_lds[r * KP + c * 16 + 8] = k1;
           *(u32x4*)&v_lds[r * VP + c * 16] = v0;
           *(u32x4*)&v_lds[r * VP + c * 16 + 8] = v1;
         } else {
+          u32x4 vh = vr[i];
+          if constexpr (F16) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) vh[x] = bf16x2_to_f16x2(vr[i][x]);
+          }
           *(u32x4*)&k_lds[r * KP + c * 8] = kr[i];
-          *(u32x4*)&v_lds[r * VP + c * 8] = vr[i];
+          *(u32x4*)&v_lds[r * VP + c * 8] = vh;
         }
       }
     }
   };
 
-  if (n_tiles > 0) load_regs(0);
-  for (int j = 0; j < n_tiles; ++j) {
-    store_lds();
-    __syncthreads();
-    if (j + 1 < n_tiles) load_regs(j + 1);
+  // The chunk's tiles; F16 selects the P V precision (fp16, or bf16 for the
+  // recomputation of a unit whose V does not fit fp16).
+  auto run_tiles = [&](auto f16_tag) {
+    constexpr bool F16 = decltype(f16_tag)::value;
+    if (n_tiles > 0) load_regs(0);
+    for (int j = 0; j < n_tiles; ++j) {
+      store_lds(f16_tag);
+      __syncthreads();
+      if (j + 1 < n_tiles) load_regs(j + 1);
 
-    // S^T[key][column] for this wave's 16 keys and every column group
-    f32x4 st[NCG];
+      // S^T[key][column] for this wave's 16 keys and every column group
+      f32x4 st[NCG];
 #pragma unroll
-    for (int cg = 0; cg < NCG; ++cg) st[cg] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const __bf16* kp = k_lds + (16 * w + l16) * KP + 8 * g16;
+      for (int cg = 0; cg < NCG; ++cg) st[cg] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const __bf16* kp = k_lds + (16 * w + l16) * KP + 8 * g16;
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const bf16x8 kfrag = *(const bf16x8*)(kp + 32 * kk);
+      for (int kk = 0; kk < KK; ++kk) {
+        const bf16x8 kfrag = *(const bf16x8*)(kp + 32 * kk);
 #pragma unroll
-      for (int cg = 0; cg < NCG; ++cg) st[cg] = mfma16x16x32(kfrag, qf[cg][kk], st[cg]);
+        for (int cg = 0; cg < NCG; ++cg) st[cg] = mfma16x16x32(kfrag, qf[cg][kk], st[cg]);
+      }
+
+      float pv[NCG][4];
+      float alpha[NCG];
+#pragma unroll
+      for (int cg = 0; cg < NCG; ++cg) {
+        float mx = NEG_INF;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = k_lo + j * BN + 16 * w + 4 * g16 + r;
+          st[cg][r] = key <= kmax[cg] ? st[cg][r] : NEG_INF;
+          mx = fmaxf(mx, st[cg][r]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = xhalf_max(mx);
+        const float m_new = fmaxf(m_run[cg], mx * a.scale_log2);
+        alpha[cg] = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run[cg] - m_new);
+        const float m_sub = (m_new == NEG_INF) ? 0.f : m_new;
+        float psum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pv[cg][r] = fast_exp2(fmaf(st[cg][r], a.scale_log2, -m_sub));
+          psum += pv[cg][r];
+        }
+        l_run[cg] = l_run[cg] * alpha[cg] + psum;
+        m_run[cg] = m_new;
+      }
+#pragma unroll
+      for (int db = 0; db < DB; ++db) {
+        const __bf16* vp = v_lds + (16 * w + 4 * g16 + (l16 >> 2)) * VP + 16 * db + 4 * (l16 & 3);
+#pragma unroll
+        for (int cg = 0; cg < NCG; ++cg) {
+          if constexpr (F16) {
+            const f16x4 pb = {(_Float16)pv[cg][0], (_Float16)pv[cg][1], (_Float16)pv[cg][2], (_Float16)pv[cg][3]};
+            acc[cg][db] = mfma16x16x16_f16(__builtin_bit_cast(f16x4, lds_read_tr4(vp)), pb, acc[cg][db] * alpha[cg]);
+          } else {
+            const bf16x4 pb = {(__bf16)pv[cg][0], (__bf16)pv[cg][1], (__bf16)pv[cg][2], (__bf16)pv[cg][3]};
+            acc[cg][db] = mfma16x16x16_bf16(lds_read_tr4(vp), pb, acc[cg][db] * alpha[cg]);
+          }
+        }
+      }
+      __syncthreads();   // the tile buffer is refilled at the top of the next iteration
     }
-
-    bf16x4 pb[NCG];
-    float alpha[NCG];
+  };
+  run_tiles(std::true_type{});   // e4m3 V is widened to fp16 as well
+  if constexpr (!FP8) {
+    // A bf16 V value beyond the fp16 range became infinite in the fp16 tile, so
+    // every accumulator it met is infinite or NaN; the flag is read after the
+    // barrier below.
+    float chk = 0.f;   // NaN iff some accumulator entry is not finite
+#pragma unroll
+    for (int cg = 0; cg < NCG; ++cg)
+#pragma unroll
+      for (int db = 0; db < DB; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) chk = fmaf(acc[cg][db][r], 0.f, chk);
+    if (__builtin_amdgcn_ballot_w64(chk != chk) != 0 && lane == 0) s_big = 1;
+  }
+  __syncthreads();
+  if (!FP8 && s_big) {
+    // Rare: the whole unit again with P V in bf16 (for V that is itself not
+    // finite this gives the result the first pass would have).
 #pragma unroll
     for (int cg = 0; cg < NCG; ++cg) {
-      float mx = NEG_INF;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = k_lo + j * BN + 16 * w + 4 * g16 + r;
-        st[cg][r] = key <= kmax[cg] ? st[cg][r] : NEG_INF;
-        mx = fmaxf(mx, st[cg][r]);
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 16));
-      mx = xhalf_max(mx);
-      const float m_new = fmaxf(m_run[cg], mx * a.scale_log2);
-      alpha[cg] = (m_new == NEG_INF) ? 1.f : fast_exp2(m_run[cg] - m_new);
-      const float m_sub = (m_new == NEG_INF) ? 0.f : m_new;
-      float psum = 0.f;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float p = fast_exp2(fmaf(st[cg][r], a.scale_log2, -m_sub));
-        psum += p;
-        pb[cg][r] = (__bf16)p;
-      }
-      l_run[cg] = l_run[cg] * alpha[cg] + psum;
-      m_run[cg] = m_new;
+      for (int db = 0; db < DB; ++db) acc[cg][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+      m_run[cg] = NEG_INF;
+      l_run[cg] = 0.f;
     }
-#pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const __bf16* vp = v_lds + (16 * w + 4 * g16 + (l16 >> 2)) * VP + 16 * db + 4 * (l16 & 3);
-      const bf16x4 vfrag = lds_read_tr4(vp);
-#pragma unroll
-      for (int cg = 0; cg < NCG; ++cg) acc[cg][db] = mfma16x16x16(vfrag, pb[cg], acc[cg][db] * alpha[cg]);
-    }
-    __syncthreads();   // the tile buffer is refilled at the top of the next iteration
+    run_tiles(std::false_type{});
   }
 
   // merge the four waves, one column group at a time: lanes of one column share
@@ -270,7 +326,8 @@ __global__ __launch_bounds__(256, (DecOcc<D, NCG>::WG_PER_CU)) void decode_kerne
   float* o_s = (float*)smem;                       // [4][16][OP]
   float* m_s = o_s + 4 * 16 * OP;                  // [4][16]
   float* l_s = m_s + 4 * 16;                       // [4][16]
-  if (n_tiles > 0) __syncthreads();
+  // (the tiles' LDS is free: the barrier after the check above, or the last one
+  // of the recomputation, follows every read of it)
 #pragma unroll
   for (int cg = 0; cg < NCG; ++cg) {
     float lr = l_run[cg];

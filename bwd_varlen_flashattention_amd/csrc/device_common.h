@@ -27,6 +27,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 #define JFA_LDS __attribute__((address_space(3)))
 
@@ -50,6 +54,42 @@ __device__ __forceinline__ u32x4 widen_e4m3x8(uint2 x) {
   return r;
 }
 
+// 8 e4m3 bytes -> 8 fp16 (exact: every e4m3 value is an fp16 value), packed two
+// per dword in column order.
+__device__ __forceinline__ u32x4 widen_e4m3x8_f16(uint2 x) {
+  u32x4 r;
+  const f32x2 p[4] = {__builtin_amdgcn_cvt_pk_f32_fp8(x.x, false), __builtin_amdgcn_cvt_pk_f32_fp8(x.x, true),
+                      __builtin_amdgcn_cvt_pk_f32_fp8(x.y, false), __builtin_amdgcn_cvt_pk_f32_fp8(x.y, true)};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) r[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(p[i], f16x2));
+  return r;
+}
+
+// P V runs on the fp16 matrix cores: P in [0, 2^8] (the lazy rescale bounds it)
+// keeps 11 significant bits instead of bf16's 8, and every bf16 V value of
+// magnitude below 65520 is exactly an fp16 value (below 2^-14 it becomes an fp16
+// subnormal, an absolute change under 2^-25).  Larger magnitudes become infinite:
+// the forward and the decode detect the non-finite accumulators that follows and
+// compute that work item again with P V in bf16.
+constexpr float kF16Overflow = 65520.f;   // smallest magnitude that fp16 rounds to infinity
+
+// Two bf16 values (one dword, low half first) -> two fp16 values.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t x) {
+  const float lo = __uint_as_float(x << 16), hi = __uint_as_float(x & 0xffff0000u);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, f16x2));
+}
+
+__device__ __forceinline__ f16x8 to_f16x8(const float* s) {
+  f16x8 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 h = __builtin_convertvector((f32x2){s[2 * i], s[2 * i + 1]}, f16x2);
+    r[2 * i] = h[0];
+    r[2 * i + 1] = h[1];
+  }
+  return r;
+}
+
 // Raw buffer resource for a wave-uniform base and byte range.  The base and range
 // are moved to scalar registers explicitly: when a 64-bit address product ends up
 // in vector registers, the compiler otherwise wraps every load through the
@@ -68,6 +108,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x16 mfma32x32x16_f16(f16x8 a, f16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
 // Transposed 4x16 read of a row-major bf16 tile in LDS (see the layout note above).

@@ -21,12 +21,18 @@
 //     j+1 are in flight while tile j is consumed;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 so each lane owns one query column:
 //     the row max/sum reductions are in-lane plus one permlane32 swap;
-//   * the S^T accumulator, rounded to bf16, is directly the B operand of
-//     O^T += V^T P^T.  V is staged into LDS already transposed (each thread
-//     transposes a 4-key x 8-column block in registers with v_perm_b32), with
-//     the keys of every 16-key group stored in the order the accumulator hands
-//     them out, so every MFMA operand is one 16-byte ds_read_b128 -- on gfx950
-//     the transposed LDS read delivers about a third of the b128 bandwidth;
+//   * the S^T accumulator, rounded to fp16, is directly the B operand of
+//     O^T += V^T P^T on v_mfma_f32_32x32x16_f16 (the fp16 rate equals the bf16
+//     one; P keeps 11 significant bits instead of 8, which keeps O within 1e-2
+//     of exact attention where bf16 rounding of P alone can exceed what the
+//     output's own bf16 rounding leaves of that budget).  V is converted to
+//     fp16 (exact below 65520 in magnitude; an item whose V holds a larger
+//     value is computed again with bf16 P V) and staged into LDS
+//     already transposed (each thread transposes a 4-key x 8-column block in
+//     registers with v_perm_b32), with the keys of every 16-key group stored in
+//     the order the accumulator hands them out, so every MFMA operand is one
+//     16-byte ds_read_b128 -- on gfx950 the transposed LDS read delivers about
+//     a third of the b128 bandwidth;
 //   * the key loop is split into a branch-free bulk and masked tail/diagonal tiles
 //     (loop peeling, TLX page fifth paragraph);
 //   * the running max is only moved (and the accumulator rescaled) when it grows
@@ -41,8 +47,8 @@ namespace jfa {
 
 // FP8: Q, K and V are OCP e4m3 bytes.  K stays e4m3 in LDS and S^T = K Q^T runs
 // on v_mfma_f32_32x32x64_f8f6f4 (64-deep k-steps, twice the bf16 rate); V is
-// widened to bf16 (exactly: every e4m3 value is a bf16 value) while it is staged
-// transposed, so P V is the bf16 contraction of the bf16 path.
+// widened to fp16 (exactly: every e4m3 value is an fp16 value) while it is
+// staged transposed, so P V is the fp16 contraction of the bf16 path.
 template <int D, bool FP8 = false>
 struct FwdTile {
   static constexpr int BN = D <= 192 ? 64 : 32;   // keys per KV tile (d = 256: 32, so nothing spills)
@@ -111,6 +117,9 @@ __global__ __launch_bounds__((FwdTile<D, FP8>::NT), (FwdTile<D, FP8>::WG_PER_CU)
   // claim k + 2, the next write to that entry, cannot overtake the read even when
   // item k + 1 has no tiles (and so no barrier of its own)
   __shared__ int s_queue[2 * kQueues];
+  // Number (counted from 1 over the workgroup's lifetime) of the last item whose
+  // fp16 accumulation was not finite; 0 = none
+  __shared__ int s_big_item;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, w = tid >> 6;
@@ -143,12 +152,15 @@ __global__ __launch_bounds__((FwdTile<D, FP8>::NT), (FwdTile<D, FP8>::WG_PER_CU)
 
   int home_q = blockIdx.x % kQueues, drained = 0;   // work-queue state (thread 0)
   load_queues(a.queues, s_queue);
+  if (tid == 0) s_big_item = 0;
   __syncthreads();
   if (tid == 0) s_item[0] = next_work_item(a.queues, s_queue, home_q, drained);
   __syncthreads();
   int slot = 0;   // s_item entry of the current claim (uniform)
+  int item_no = 0;   // items taken by this workgroup (uniform)
   int item = __builtin_amdgcn_readfirstlane(s_item[0]);   // uniform: the item loads are scalar
   while (item >= 0) {
+    ++item_no;
     const WorkItem e = a.items[item];
     const int h = e.h;
     const int g = h / a.group;
@@ -218,7 +230,11 @@ __global__ __launch_bounds__((FwdTile<D, FP8>::NT), (FwdTile<D, FP8>::WG_PER_CU)
           }
         }
     };
-    auto store_lds = [&](int buf) {
+    // F16 (a std::bool_constant): V is written as fp16 (e4m3 always is; a bf16
+    // value beyond the fp16 range becomes infinite, see the recomputation below),
+    // otherwise as bf16.
+    auto store_lds = [&](int buf, auto f16_tag) {
+      constexpr bool F16 = decltype(f16_tag)::value;
 #pragma unroll
       for (int i = 0; i < T::KLOADS; ++i) {
         const int id = tid + i * T::NT;
@@ -231,11 +247,16 @@ __global__ __launch_bounds__((FwdTile<D, FP8>::NT), (FwdTile<D, FP8>::WG_PER_CU)
         // 4 keys x 8 columns -> 8 rows of V^T holding 4 keys each
         const int col = 16 * (vkb[vi] >> 2) + 4 * vt_quarter_pos(vkb[vi] & 3);
         __bf16* dst = &vt_lds[buf][(8 * vdb[vi]) * VTP + col];
-        u32x4 r[4];
+        u32x4 r[4];   // 4 rows of 8 16-bit values
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          if constexpr (FP8) r[i] = widen_e4m3x8(vr[vi][i]);
-          else r[i] = vr[vi][i];
+          if constexpr (FP8) r[i] = widen_e4m3x8_f16(vr[vi][i]);
+          else if constexpr (F16) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) r[i][c] = bf16x2_to_f16x2(vr[vi][i][c]);
+          } else {
+            r[i] = vr[vi][i];
+          }
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -263,14 +284,16 @@ __global__ __launch_bounds__((FwdTile<D, FP8>::NT), (FwdTile<D, FP8>::WG_PER_CU)
 
     // Step s visits key tile j = tile_of(s).  MASK selects the tail / causal-diagonal
     // variant; the bulk variant has no per-element masking at all (loop peeling).
-    auto tile = [&](int step, auto mask_tag) {
+    // F16 selects the P V precision (fp16, or bf16 for the recomputation of an
+    // item whose V does not fit fp16).
+    auto tile = [&](int step, auto mask_tag, auto f16_tag) {
       constexpr bool MASK = decltype(mask_tag)::value;
+      constexpr bool F16 = decltype(f16_tag)::value;
       const int buf = step & 1;
       const int j = tile_of(step);
       if (step + 1 < n_tiles) load_regs(tile_of(step + 1));
       // a wave whose 32 rows all lie past the sequence end only stages and syncs
       if (wave_rows) {
-
       // S^T[key][query] for the tile's 32-key blocks
       f32x16 s[KB];
 #pragma unroll
@@ -319,7 +342,8 @@ __global__ __launch_bounds__((FwdTile<D, FP8>::NT), (FwdTile<D, FP8>::WG_PER_CU)
       const float m_sub = (m_run == NEG_INF) ? 0.f : m_run;
 
       float psum = 0.f;
-      bf16x8 pb[KB][2];
+      using PFrag = std::conditional_t<F16, f16x8, bf16x8>;
+      PFrag pb[KB][2];   // P^T: B operands of O^T += V^T P^T
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
         float pv[16];
@@ -328,8 +352,13 @@ __global__ __launch_bounds__((FwdTile<D, FP8>::NT), (FwdTile<D, FP8>::WG_PER_CU)
           pv[r] = fast_exp2(fmaf(s[kb][r], a.scale_log2, -m_sub));
           psum += pv[r];
         }
-        pb[kb][0] = to_bf16x8(pv);
-        pb[kb][1] = to_bf16x8(pv + 8);
+        if constexpr (F16) {
+          pb[kb][0] = to_f16x8(pv);
+          pb[kb][1] = to_f16x8(pv + 8);
+        } else {
+          pb[kb][0] = to_bf16x8(pv);
+          pb[kb][1] = to_bf16x8(pv + 8);
+        }
       }
       l_run += psum;
 
@@ -340,23 +369,50 @@ __global__ __launch_bounds__((FwdTile<D, FP8>::NT), (FwdTile<D, FP8>::WG_PER_CU)
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int t = 0; t < 2; ++t)
-            acc[db] = mfma32x32x16(*(const bf16x8*)(vp + 16 * (2 * kb + t)), pb[kb][t], acc[db]);
+          for (int t = 0; t < 2; ++t) {
+            if constexpr (F16)
+              acc[db] = mfma32x32x16_f16(*(const f16x8*)(vp + 16 * (2 * kb + t)), pb[kb][t], acc[db]);
+            else
+              acc[db] = mfma32x32x16(*(const bf16x8*)(vp + 16 * (2 * kb + t)), pb[kb][t], acc[db]);
+          }
       }
       }   // wave_rows
 
-      if (step + 1 < n_tiles) store_lds(buf ^ 1);
+      if (step + 1 < n_tiles) store_lds(buf ^ 1, f16_tag);
       __syncthreads();
     };
 
     // The loops are only reachable through the prologue, whose wait covers the
     // Q-fragment loads; otherwise every tile would wait on all outstanding loads.
-    if (n_tiles > 0) {
+    auto key_loop = [&](auto f16_tag) {
       load_regs(tile_of(0));
-      store_lds(0);
+      store_lds(0, f16_tag);
       __syncthreads();
-      for (int s = 0; s < n_bulk; ++s) tile(s, std::false_type{});
-      for (int s = n_bulk; s < n_tiles; ++s) tile(s, std::true_type{});
+      for (int s = 0; s < n_bulk; ++s) tile(s, std::false_type{}, f16_tag);
+      for (int s = n_bulk; s < n_tiles; ++s) tile(s, std::true_type{}, f16_tag);
+    };
+    if (n_tiles > 0) {
+      key_loop(std::true_type{});   // e4m3 V is widened to fp16 as well
+      if constexpr (!FP8) {
+        // A bf16 V value beyond the fp16 range became infinite in the fp16 tile,
+        // so every accumulator it met is infinite or NaN.  Rare: then the whole
+        // item again with P V in bf16 (for V that is itself non-finite this gives
+        // the same result as the first pass would have).
+        float chk = 0.f;   // NaN iff some accumulator entry is not finite
+#pragma unroll
+        for (int db = 0; db < DB; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) chk = fmaf(acc[db][r], 0.f, chk);
+        if (__builtin_amdgcn_ballot_w64(chk != chk) != 0 && lane == 0) s_big_item = item_no;
+        __syncthreads();
+      }
+      if (!FP8 && s_big_item == item_no) {
+#pragma unroll
+        for (int db = 0; db < DB; ++db) acc[db] = f32x16{};
+        m_run = NEG_INF;
+        l_run = 0.f;
+        key_loop(std::false_type{});
+      }
     }
 
     // epilogue: O = acc / l, LSE = (m + log2 l) * ln 2

@@ -1,4 +1,5 @@
 """GPU parity: jagged forward and backward through the C ABI against the fp64 oracle."""
+import dataclasses
 import math
 import sys
 
@@ -397,3 +398,47 @@ def test_one_long_causal_sequence(jfa):
     scale = np.abs(dk).sum(axis=0).max()
     assert np.abs(dk_sum).max() <= 2e-3 * scale, (np.abs(dk_sum).max(), scale)
     assert np.abs(dv_sum - do_sum).max() <= 2e-3 * np.abs(dv).sum(axis=0).max()
+
+
+# bf16 values beyond the fp16 range (|v| >= 65520), placed in a few V rows
+LARGE_V = [65536.0, -98304.0, 1048576.0, -16777216.0, 2.0 ** 27]
+
+
+def _plant_large_v(v, rng, n):
+    """Put LARGE_V values at n random (row, head, column) positions of v (float32 array, bf16 values)."""
+    v = v.copy()
+    for i in range(n):
+        r, h, c = rng.integers(0, v.shape[0]), rng.integers(0, v.shape[1]), rng.integers(0, v.shape[2])
+        v[r, h, c] = LARGE_V[i % len(LARGE_V)]
+    return v
+
+
+def _check_large(got, ref, mag, what):
+    """|error| <= 1e-2 + half a bf16 ulp of O + 2^-7 (P |V|): the output's own bf16
+    rounding, plus the rounding of P (bf16, 8 significant bits, in the recomputation such
+    inputs take: 2^-8 per term) and the normalisation by the unrounded sum (another
+    2^-8), relative to the magnitudes summed, P |V|, not to O."""
+    from parity import half_ulp_bf16
+    err = np.abs(got - ref)
+    bound = 1e-2 + half_ulp_bf16(ref) + 2.0 ** -7 * mag
+    assert np.isfinite(got).all(), f"{what}: non-finite values"
+    assert (err <= bound).all(), f"{what}: max excess {(err - bound).max():.3e}"
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128, 256])
+def test_forward_v_beyond_fp16_range(jfa, causal, d):
+    """V entries of magnitude 2^16 .. 2^27 (beyond fp16) in several items: in fp16 those V
+    values become infinite, so the items are computed again with P V in bf16."""
+    inp = workloads.jagged(77 + d, [5, 130, 64, 200, 1], None, 4, 2, d, causal)
+    rng = np.random.default_rng(5)
+    inp = dataclasses.replace(inp, v=_plant_large_v(inp.v, rng, 12))
+    q, k, v = (dev(x, torch) for x in (inp.q, inp.k, inp.v))
+    cq, ck = dev(inp.cu_q, torch), dev(inp.cu_k, torch)
+    o, lse = jfa.jfa_fwd(q, k, v, cq, ck, inp.max_len_q, inp.max_len_k, causal)
+    torch.cuda.synchronize()
+    f = lambda x: x.astype(np.float64)
+    ro, rl = oracle.attention_forward(f(inp.q), f(inp.k), f(inp.v), inp.cu_q, inp.cu_k, causal)
+    mag, _ = oracle.attention_forward(f(inp.q), f(inp.k), np.abs(f(inp.v)), inp.cu_q, inp.cu_k, causal)
+    _check_large(host(o), ro, mag, "O")
+    check_lse(host(lse), rl)

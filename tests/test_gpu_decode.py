@@ -6,7 +6,7 @@ import pytest
 
 import oracle
 import workloads
-from parity import check_lse, check_o, dev, host
+from parity import check_lse, check_o, dev, half_ulp_bf16, host
 
 pytestmark = pytest.mark.gpu
 
@@ -270,3 +270,28 @@ def test_decode_large_batch(jfa):
         o, lse = _run(jfa, d, splits)
         check_o(o, ro, f"O splits={splits}")
         check_lse(lse, rl, f"LSE splits={splits}")
+
+
+@pytest.mark.parametrize("dim", [64, 128, 256])
+def test_decode_v_beyond_fp16_range(jfa, dim):
+    """V entries of magnitude 2^16 .. 2^27 (beyond fp16) in some units: in fp16 those V values
+    become infinite, so the units are computed again with P V in bf16; |error| <= 1e-2 +
+    half a bf16 ulp of O + 2^-7 (P |V|) (the output's bf16 rounding, plus bf16 P (2^-8 per
+    term) and the normalisation by the unrounded sum (2^-8), relative to P |V|)."""
+    import dataclasses
+    base = workloads.decode(97, [5, 300, 1000, 64, 1], 8, 2, dim, 16)
+    rng = np.random.default_rng(9)
+    v = base.v.copy()
+    big = [65536.0, -98304.0, 1048576.0, -16777216.0, 2.0 ** 27]
+    for i in range(12):
+        v[rng.integers(0, v.shape[0]), rng.integers(0, v.shape[1]), rng.integers(0, v.shape[2])] = big[i % 5]
+    inp = workloads.repage(dataclasses.replace(base, v=v), 16, 3)
+    d = _Dev(inp)
+    f = lambda x: x.astype(np.float64)
+    ro, rl = oracle.decode_forward(f(inp.q), f(inp.k), f(inp.v), inp.cu_k)
+    mag, _ = oracle.decode_forward(f(inp.q), f(inp.k), np.abs(f(inp.v)), inp.cu_k)
+    for splits in (1, 3):
+        o, lse = _run(jfa, d, splits)
+        err, bound = np.abs(o - ro), 1e-2 + half_ulp_bf16(ro) + 2.0 ** -7 * mag
+        assert np.isfinite(o).all() and (err <= bound).all(), f"splits={splits}: excess {(err - bound).max():.3e}"
+        check_lse(lse, rl)
