@@ -16,7 +16,8 @@ from . import _lib
 from ._lib import AttnParams, DecodeParams, JfaError, KernelEventsStruct, load  # noqa: F401
 
 __all__ = ["jfa_fwd", "jfa_bwd", "jfa_decode_paged", "jfa_decode_num_splits", "jfa_fwd_workspace_size",
-           "jfa_bwd_workspace_size", "jfa_decode_workspace_size", "KernelEvents", "JfaError", "load"]
+           "jfa_bwd_workspace_size", "jfa_decode_workspace_size", "jfa_decode_paged_noalloc", "KernelEvents",
+           "JfaError", "load"]
 
 
 def _torch():
@@ -343,4 +344,30 @@ def jfa_decode_paged(q, k_cache, v_cache, page_table, seqlens_k, num_splits: int
     st = lib.jfa_decode_paged(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
                               _ptr(seqlens_k), _ptr(o), _ptr(l), ws.data_ptr(), ws.numel(), _stream())
     _lib.check(st, "jfa_decode_paged")
+    return o, l
+
+
+def jfa_decode_paged_noalloc(q, k_cache, v_cache, page_table, seqlens_k, num_splits: int = 0,
+                             softmax_scale: Optional[float] = None, out=None, lse=None, causal: bool = False,
+                             k_scale: Optional[float] = None, v_scale: Optional[float] = None,
+                             q_scale: Optional[float] = None, events: Optional[KernelEvents] = None):
+    """jfa_decode_paged with its split partials in the library's static device array
+    instead of a workspace (the library allocates nothing; pass out and lse to
+    allocate nothing here either).  Calls overlapping on one GPU race."""
+    torch = _torch()
+    _decode_shapes(q, k_cache, v_cache, page_table, seqlens_k)
+    if out is not None:
+        _check("out", out, _bf16(torch), tuple(q.shape))
+    if lse is not None:
+        _check("lse", lse, (torch.float32,), tuple(q.shape[:-1]))
+    _check_devices(q=q, k_cache=k_cache, v_cache=v_cache, page_table=page_table, seqlens_k=seqlens_k, out=out,
+                   lse=lse)
+    lib = load()
+    p = _decode_params(q, k_cache, page_table, num_splits, softmax_scale, causal, k_scale, v_scale, q_scale,
+                       events)
+    o = out if out is not None else torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
+    l = lse if lse is not None else torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
+    st = lib.jfa_decode_paged_noalloc(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
+                                      _ptr(seqlens_k), _ptr(o), _ptr(l), _stream())
+    _lib.check(st, "jfa_decode_paged_noalloc")
     return o, l

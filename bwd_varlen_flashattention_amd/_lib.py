@@ -21,10 +21,11 @@ JFA_ERR_HIP = 4
 # every symbol include/jfa.h declares
 EXPORTS = (
     "jfa_fwd_workspace_size", "jfa_fwd", "jfa_bwd_workspace_size", "jfa_bwd",
-    "jfa_decode_workspace_size", "jfa_decode_paged", "jfa_decode_num_splits",
+    "jfa_decode_workspace_size", "jfa_decode_paged", "jfa_decode_paged_noalloc", "jfa_decode_num_splits",
     "jfa_status_string", "jfa_abi_version",
 )
 ABI_VERSION = 4
+DECODE_SCRATCH_BYTES = 8 << 20   # JFA_DECODE_SCRATCH_BYTES
 
 
 class KernelEventsStruct(ctypes.Structure):
@@ -110,6 +111,8 @@ def load() -> ctypes.CDLL:
     lib.jfa_decode_num_splits.restype = ctypes.c_int32
     lib.jfa_decode_paged.argtypes = [dp, vp, vp, vp, i32p, i32p, vp, vp, vp, sz, vp]
     lib.jfa_decode_paged.restype = ctypes.c_int
+    lib.jfa_decode_paged_noalloc.argtypes = [dp, vp, vp, vp, i32p, i32p, vp, vp, vp]
+    lib.jfa_decode_paged_noalloc.restype = ctypes.c_int
     lib.jfa_status_string.argtypes = [ctypes.c_int]
     lib.jfa_status_string.restype = ctypes.c_char_p
     lib.jfa_abi_version.argtypes = []

@@ -201,6 +201,28 @@ size_t decode_ws(const jfa_decode_params_t* p, int splits) {
   return align_up(plane * splits * p->head_dim * sizeof(float)) + align_up(plane * splits * sizeof(float));
 }
 
+// ------------------------------------------------------------------ static scratch
+// jfa_decode_paged_noalloc keeps its split partials in this array instead of a
+// caller workspace.  Each GPU holds its own copy for the life of the process; host
+// code uses only the device address hipGetSymbolAddress reports for it (the
+// array's name on the host is a stand-in, not that address), looked up once per
+// device and cached.
+static __device__ __align__(256) unsigned char scratch[JFA_DECODE_SCRATCH_BYTES];
+void* g_scratch[kMaxDevices] = {nullptr};
+
+jfa_status_t scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return JFA_ERR_HIP;
+  void* ptr = __atomic_load_n(&g_scratch[dev], __ATOMIC_ACQUIRE);
+  if (!ptr) {
+    // two threads racing here store the same address
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return JFA_ERR_HIP;
+    __atomic_store_n(&g_scratch[dev], ptr, __ATOMIC_RELEASE);
+  }
+  *out = ptr;
+  return JFA_OK;
+}
+
 }  // namespace
 
 // ====================================================================== exported
@@ -459,6 +481,18 @@ int32_t jfa_decode_num_splits(const jfa_decode_params_t* p) {
 size_t jfa_decode_workspace_size(const jfa_decode_params_t* p) {
   if (check_decode(p) != JFA_OK) return 0;
   return decode_ws(p, resolve_splits(p));
+}
+
+jfa_status_t jfa_decode_paged_noalloc(const jfa_decode_params_t* p, const void* q, const void* k_cache,
+                                      const void* v_cache, const int32_t* page_table, const int32_t* seqlens_k,
+                                      void* o, float* lse, jfa_stream_t stream) {
+  const jfa_status_t st = check_decode(p);
+  if (st != JFA_OK) return st;
+  if (decode_ws(p, resolve_splits(p)) > JFA_DECODE_SCRATCH_BYTES) return JFA_ERR_WORKSPACE_TOO_SMALL;
+  void* ptr = nullptr;
+  if (scratch_address(&ptr) != JFA_OK) return JFA_ERR_HIP;
+  return jfa_decode_paged(p, q, k_cache, v_cache, page_table, seqlens_k, o, lse, ptr, JFA_DECODE_SCRATCH_BYTES,
+                          stream);
 }
 
 jfa_status_t jfa_decode_paged(const jfa_decode_params_t* p, const void* q, const void* k_cache,

@@ -237,6 +237,26 @@ jfa_status_t jfa_decode_paged(const jfa_decode_params_t* p,
                               void* o, float* lse,
                               void* workspace, size_t workspace_bytes, jfa_stream_t stream);
 
+/*
+ * jfa_decode_paged without a workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  The same computation and arguments as jfa_decode_paged;
+ * the split partials live in a static device array of
+ * JFA_DECODE_SCRATCH_BYTES that the library holds on every GPU it runs on (on
+ * the current device; `stream` must belong to it) until the process ends.  The
+ * call allocates nothing.  A problem whose partials (jfa_decode_workspace_size)
+ * exceed JFA_DECODE_SCRATCH_BYTES returns JFA_ERR_WORKSPACE_TOO_SMALL before
+ * any launch; failing to look up the array's address returns JFA_ERR_HIP.
+ * Every call on one GPU uses the same array: calls that overlap in time on one
+ * GPU (concurrent streams, or host threads) race and must be serialised by the
+ * caller.  Nothing in the array needs to start zeroed.
+ */
+#define JFA_DECODE_SCRATCH_BYTES ((size_t)8 << 20)
+jfa_status_t jfa_decode_paged_noalloc(const jfa_decode_params_t* p,
+                                      const void* q, const void* k_cache, const void* v_cache,
+                                      const int32_t* page_table, const int32_t* seqlens_k,
+                                      void* o, float* lse, jfa_stream_t stream);
+
 /* The split count jfa_decode_paged uses for p (resolves num_splits = 0). */
 int32_t jfa_decode_num_splits(const jfa_decode_params_t* p);
 

@@ -211,3 +211,18 @@ def test_struct_layouts_match_the_header(tmp_path):
         assert got[(cname, "size")] == ctypes.sizeof(cls), cname
         for f, _t in cls._fields_:
             assert got[(cname, f)] == getattr(cls, f).offset, (cname, f)
+
+
+def test_noalloc_decode_rejects_problems_beyond_its_scratch():
+    """jfa_decode_paged_noalloc: partials larger than its static array are refused before
+    any launch; invalid params keep their usual status."""
+    L, lib = _lib()
+    d = ctypes.c_void_p(256)
+    p = L.DecodeParams(batch=256, num_heads_q=64, num_heads_kv=8, head_dim=128, page_size=16, num_pages=10,
+                       max_pages_per_seq=1024, num_splits=16, softmax_scale=0.0, q_len=1, causal=0)
+    assert lib.jfa_decode_workspace_size(ctypes.byref(p)) > L.DECODE_SCRATCH_BYTES
+    assert lib.jfa_decode_paged_noalloc(ctypes.byref(p), d, d, d, d, d, d, d, None) == L.JFA_ERR_WORKSPACE_TOO_SMALL
+    p.page_size = 0
+    assert lib.jfa_decode_paged_noalloc(ctypes.byref(p), d, d, d, d, d, d, d, None) == L.JFA_ERR_INVALID_ARGUMENT
+    text = open(HEADER).read()
+    assert "#define JFA_DECODE_SCRATCH_BYTES ((size_t)8 << 20)" in text and L.DECODE_SCRATCH_BYTES == 8 << 20
