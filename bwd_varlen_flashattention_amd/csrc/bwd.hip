@@ -313,15 +313,11 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 #pragma unroll
     for (int db = 0; db < DB; ++db) { dkt[db] = f32x16{}; dvt[db] = f32x16{}; }
 
-    // step s -> unit u -> (query head, query tile); rows past Lq read as zero
-    // (buffer range).  The units start at a rotation that differs between the key
-    // tiles of one (sequence, KV head): those run at the same time on one XCD and
-    // would otherwise request the same Q/dO lines at the same moment.
-    const int rot = n_steps > 1 ? (int)(((int64_t)e.t * n_steps) / cdiv(lk, BN)) % n_steps : 0;
-    auto unit_of = [&](int s) {
-      const int u = s + rot;
-      return u >= n_steps ? u - n_steps : u;
-    };
+    // step s -> unit s -> (query head, query tile); rows past Lq read as zero
+    // (buffer range).  All key tiles of a (sequence, KV head) walk the query
+    // tiles in the same order, so the ones running together on an XCD find the
+    // same Q/dO tiles in its L2.
+    auto unit_of = [&](int s) { return s; };
     u32x4 sr[8];   // staged rows: 8 rows of one tile, or 4 rows of Q then 4 of dO
     // LSE and delta travel raw (range-checked buffer loads) and are only looked
     // at when they are written to LDS: consuming them right after the load would
@@ -709,16 +705,10 @@ __global__ __launch_bounds__((DqTile<D>::NT), (DqTile<D>::WG_PER_CU)) void bwd_d
         }
       };
 
-      // Key-tile order: bulk tiles rotated per (query tile, GQA head) so that the
-      // items sharing this K/V, which run together on one XCD, read different K/V
-      // lines at any moment; masked tiles last.
-      const int rot_cnt = cdiv(lq, BM) * a.group;
-      const int rot = n_bulk > 1 ? (int)(((int64_t)(qtile * a.group + h % a.group) * n_bulk) / rot_cnt) % n_bulk : 0;
-      auto tile_of = [&](int s) {
-        if (s >= n_bulk) return s;
-        const int j = s + rot;
-        return j >= n_bulk ? j - n_bulk : j;
-      };
+      // Key-tile order: bulk tiles first, masked tiles last, the same order for
+      // every item sharing this K/V (they run together on one XCD and find the
+      // same K/V tiles in its L2).
+      auto tile_of = [&](int s) { return s; };
       // the first K/V tile travels with the Q / dO / O fragments: one round trip
       if (n_tiles > 0) load_regs(tile_of(0));
 

@@ -270,17 +270,10 @@ __global__ __launch_bounds__((FwdTile<D, FP8>::NT), (FwdTile<D, FP8>::WG_PER_CU)
       }
     };
 
-    // Key-tile order: the bulk tiles start at a rotation that differs between the
-    // query tiles (and GQA heads) sharing this K/V, which run at the same time on
-    // one XCD and would otherwise request the same K/V lines at the same moment;
-    // the masked tiles come last.
-    const int rot_cnt = cdiv(lq, BM) * a.group;
-    const int rot = n_bulk > 1 ? (int)(((int64_t)(e.t * a.group + h % a.group) * n_bulk) / rot_cnt) % n_bulk : 0;
-    auto tile_of = [&](int s) {
-      if (s >= n_bulk) return s;
-      const int j = s + rot;
-      return j >= n_bulk ? j - n_bulk : j;
-    };
+    // Key-tile order: bulk tiles first, masked tiles last, the same order for every
+    // item sharing this K/V (they run together on one XCD and find the same K/V
+    // tiles in its L2).
+    auto tile_of = [&](int s) { return s; };
 
     // Step s visits key tile j = tile_of(s).  MASK selects the tail / causal-diagonal
     // variant; the bulk variant has no per-element masking at all (loop peeling).
