@@ -147,15 +147,17 @@ def _offsets(cu_seqlens_q, cu_seqlens_k, broadcast_q):
 
 
 def _attn_params(q, k, nb, max_q, max_k, causal, scale, broadcast_q, fp8=False,
-                 q_scale=None, k_scale=None, v_scale=None, events=None):
+                 q_scale=None, k_scale=None, v_scale=None, events=None, query_tile=0):
     sc = lambda x: float(x) if x is not None else 1.0
+    if query_tile not in (0, 128, 256):
+        raise ValueError(f"query_tile: {query_tile!r}, expected 0 (chosen from the lengths), 128 or 256")
     return AttnParams(
         batch=nb, num_heads_q=q.shape[1], num_heads_kv=k.shape[1], head_dim=q.shape[2],
         total_q=q.shape[0], total_k=k.shape[0], max_seqlen_q=int(max_q), max_seqlen_k=int(max_k),
         causal=int(bool(causal)), broadcast_q=int(bool(broadcast_q)),
         softmax_scale=float(scale) if scale is not None else 0.0,
         qkv_dtype=1 if fp8 else 0, q_scale=sc(q_scale), k_scale=sc(k_scale), v_scale=sc(v_scale),
-        events=events.pointer() if events is not None else None)
+        query_tile=int(query_tile), events=events.pointer() if events is not None else None)
 
 
 def _out_shapes(q, nb, broadcast_q):
@@ -169,17 +171,18 @@ def _out_shapes(q, nb, broadcast_q):
 # ----------------------------------------------------------------------------- entry points
 
 def jfa_fwd_workspace_size(q, k, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, causal: bool = False,
-                           broadcast_q: bool = False) -> int:
+                           broadcast_q: bool = False, query_tile: int = 0) -> int:
     """Workspace bytes jfa_fwd needs for these shapes (q may be bf16 or e4m3)."""
     p = _attn_params(q, k, cu_seqlens_k.numel() - 1, max_seqlen_q, max_seqlen_k, causal, None, broadcast_q,
-                     _is_fp8(q))
+                     _is_fp8(q), query_tile=query_tile)
     return int(load().jfa_fwd_workspace_size(ctypes.byref(p)))
 
 
 def jfa_bwd_workspace_size(q, k, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int, causal: bool = False,
-                           broadcast_q: bool = False) -> int:
+                           broadcast_q: bool = False, query_tile: int = 0) -> int:
     """Workspace bytes jfa_bwd needs for these shapes."""
-    p = _attn_params(q, k, cu_seqlens_k.numel() - 1, max_seqlen_q, max_seqlen_k, causal, None, broadcast_q)
+    p = _attn_params(q, k, cu_seqlens_k.numel() - 1, max_seqlen_q, max_seqlen_k, causal, None, broadcast_q,
+                     query_tile=query_tile)
     return int(load().jfa_bwd_workspace_size(ctypes.byref(p)))
 
 
@@ -187,11 +190,13 @@ def jfa_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k
             causal: bool = False, softmax_scale: Optional[float] = None, broadcast_q: bool = False,
             out=None, lse=None, workspace=None, q_scale: Optional[float] = None,
             k_scale: Optional[float] = None, v_scale: Optional[float] = None,
-            events: Optional[KernelEvents] = None):
+            events: Optional[KernelEvents] = None, query_tile: int = 0):
     """Jagged forward.  Self-attention: q [Tq,Hq,d], k/v [Tk,Hkv,d] -> o [Tq,Hq,d], lse [Hq,Tq].
     Broadcast-Q: q [Nq,Hq,d] shared by B items -> o [B,Nq,Hq,d], lse [B,Hq,Nq].
     q, k, v are all bfloat16, or all e4m3 (float8_e4m3fn or raw uint8 bytes) with
-    per-tensor scales q_scale, k_scale, v_scale (default 1); o is bfloat16 either way."""
+    per-tensor scales q_scale, k_scale, v_scale (default 1); o is bfloat16 either way.
+    query_tile: rows per work item (0: chosen from the lengths; 128 / 256 where the
+    kernel has both) -- a speed choice with the same result."""
     torch = _torch()
     fp8 = _is_fp8(q)
     _qkv_shapes(q, k, v, broadcast_q, fp8)
@@ -207,7 +212,7 @@ def jfa_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k
                    out=out, lse=lse, workspace=workspace)
     lib = load()
     p = _attn_params(q, k, nb, max_seqlen_q, max_seqlen_k, causal, softmax_scale, broadcast_q, fp8,
-                     q_scale, k_scale, v_scale, events)
+                     q_scale, k_scale, v_scale, events, query_tile)
     need = lib.jfa_fwd_workspace_size(ctypes.byref(p))
     if workspace is not None:
         _check_workspace(workspace, need)
@@ -223,8 +228,9 @@ def jfa_fwd(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k
 
 def jfa_bwd(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
             causal: bool = False, softmax_scale: Optional[float] = None, broadcast_q: bool = False,
-            dq=None, dk=None, dv=None, workspace=None, events: Optional[KernelEvents] = None):
-    """Jagged backward: returns (dq, dk, dv) in the layouts of q, k, v."""
+            dq=None, dk=None, dv=None, workspace=None, events: Optional[KernelEvents] = None,
+            query_tile: int = 0):
+    """Jagged backward: returns (dq, dk, dv) in the layouts of q, k, v (query_tile as in jfa_fwd)."""
     torch = _torch()
     _qkv_shapes(q, k, v, broadcast_q, False)
     dev = q.device
@@ -241,7 +247,8 @@ def jfa_bwd(q, k, v, o, lse, dout, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int
     _check_devices(q=q, k=k, v=v, o=o, lse=lse, dout=dout, cu_seqlens_q=None if broadcast_q else cu_seqlens_q,
                    cu_seqlens_k=cu_seqlens_k, dq=dq, dk=dk, dv=dv, workspace=workspace)
     lib = load()
-    p = _attn_params(q, k, nb, max_seqlen_q, max_seqlen_k, causal, softmax_scale, broadcast_q, events=events)
+    p = _attn_params(q, k, nb, max_seqlen_q, max_seqlen_k, causal, softmax_scale, broadcast_q, events=events,
+                     query_tile=query_tile)
     need = lib.jfa_bwd_workspace_size(ctypes.byref(p))
     if workspace is not None:
         _check_workspace(workspace, need)

@@ -24,7 +24,7 @@ EXPORTS = (
     "jfa_decode_workspace_size", "jfa_decode_paged", "jfa_decode_paged_noalloc", "jfa_decode_num_splits",
     "jfa_status_string", "jfa_abi_version",
 )
-ABI_VERSION = 4
+ABI_VERSION = 5
 DECODE_SCRATCH_BYTES = 8 << 20   # JFA_DECODE_SCRATCH_BYTES
 
 
@@ -52,6 +52,7 @@ class AttnParams(ctypes.Structure):
         ("q_scale", ctypes.c_float),
         ("k_scale", ctypes.c_float),
         ("v_scale", ctypes.c_float),
+        ("query_tile", ctypes.c_int32),
         ("events", ctypes.POINTER(KernelEventsStruct)),
     ]
 

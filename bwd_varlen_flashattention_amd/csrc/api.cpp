@@ -60,6 +60,7 @@ jfa_status_t check_attn(const jfa_attn_params_t* p) {
   if (!supported_dim(p->head_dim)) return JFA_ERR_UNSUPPORTED;
   if (p->qkv_dtype == JFA_DTYPE_FP8_E4M3 && p->head_dim % 64 != 0) return JFA_ERR_UNSUPPORTED;
   if (p->broadcast_q && p->causal) return JFA_ERR_UNSUPPORTED;
+  if (p->query_tile != 0 && p->query_tile != 128 && p->query_tile != 256) return JFA_ERR_INVALID_ARGUMENT;
   // 32-bit element offsets of packed rows stay within int64 math; row counts must fit int32 tiles
   if ((int64_t)p->total_q * p->num_heads_q * p->head_dim > (int64_t)1 << 40) return JFA_ERR_INVALID_ARGUMENT;
   return JFA_OK;
@@ -85,8 +86,26 @@ SchedLayout sched_layout(size_t base, int64_t max_items, int64_t groups) {
   return l;
 }
 
+// Tile shape per call.  When the sequences are short (mean query rows per
+// sequence at most JFA_NARROW_ROWS; broadcast-Q: the shared query rows), an
+// item of the 8-wave, 256-row forward / dQ workgroup is mostly empty rows and a
+// few tiles long, so its time is load latency: the 4-wave, 128-row shape, two
+// workgroups per CU, halves the idle rows and overlaps two items per CU.  Only
+// bf16 at d = 64 / 128 has both shapes; the choice is a function of the
+// parameters alone, so workspace sizing and launch agree.  A nonzero
+// query_tile in the params overrides it.
+#ifndef JFA_NARROW_ROWS
+#define JFA_NARROW_ROWS 160
+#endif
+bool narrow_tiles(const jfa_attn_params_t* p) {
+  if (p->qkv_dtype != JFA_DTYPE_BF16 || (p->head_dim != 64 && p->head_dim != 128)) return false;
+  if (p->query_tile != 0) return p->query_tile == 128;   // the caller's choice
+  if (p->broadcast_q) return p->total_q <= JFA_NARROW_ROWS;
+  return (int64_t)p->total_q <= (int64_t)JFA_NARROW_ROWS * p->batch;
+}
+
 int64_t fwd_max_entries(const jfa_attn_params_t* p) {
-  const int bm = fwd_block_rows(p->head_dim, p->qkv_dtype == JFA_DTYPE_FP8_E4M3);
+  const int bm = fwd_block_rows(p->head_dim, p->qkv_dtype == JFA_DTYPE_FP8_E4M3, narrow_tiles(p));
   if (p->broadcast_q) return (int64_t)p->batch * cdiv_i(p->total_q, bm);
   return cdiv_i(p->total_q, bm) + (int64_t)p->batch;
 }
@@ -97,7 +116,7 @@ int64_t dkdv_max_entries(const jfa_attn_params_t* p) {
 
 int64_t dq_max_entries(const jfa_attn_params_t* p) {
   if (p->broadcast_q) return 0;   // broadcast-Q dQ work is indexed directly
-  return cdiv_i(p->total_q, bwd_dq_rows(p->head_dim)) + (int64_t)p->batch;
+  return cdiv_i(p->total_q, bwd_dq_rows(p->head_dim, narrow_tiles(p))) + (int64_t)p->batch;
 }
 
 SchedLayout fwd_list(const jfa_attn_params_t* p) {
@@ -111,7 +130,7 @@ int64_t lse_elems(const jfa_attn_params_t* p) {
 // Broadcast-Q dQ: items split into chunks, enough (query tile, head, chunk) units
 // for two per CU; each chunk owns an fp32 partial of dQ.
 int bcast_dq_chunks(const jfa_attn_params_t* p) {
-  const int64_t tiles_heads = (int64_t)cdiv_i(p->total_q, bwd_dq_rows(p->head_dim)) * p->num_heads_q;
+  const int64_t tiles_heads = (int64_t)cdiv_i(p->total_q, bwd_dq_rows(p->head_dim, narrow_tiles(p))) * p->num_heads_q;
   if (tiles_heads == 0) return 0;   // no query rows: no dQ work
   const int64_t want = std::max<int64_t>(1, (2LL * cu_count() + tiles_heads - 1) / tiles_heads);
   const int per = cdiv_i(p->batch, std::min<int64_t>(p->batch, want));
@@ -265,7 +284,8 @@ jfa_status_t jfa_fwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   sa.cu_q = cu_seqlens_q;
   sa.cu_k = cu_seqlens_k;
   sa.batch = p->batch;
-  sa.stat_tile = fwd_block_rows(p->head_dim, p->qkv_dtype == JFA_DTYPE_FP8_E4M3);
+  const bool narrow = narrow_tiles(p);
+  sa.stat_tile = fwd_block_rows(p->head_dim, p->qkv_dtype == JFA_DTYPE_FP8_E4M3, narrow);
   sa.loop_tile = bn;
   sa.mode = 0;
   sa.causal = p->causal;
@@ -296,8 +316,9 @@ jfa_status_t jfa_fwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   fa.scale_log2 = eff_scale(p->softmax_scale, p->head_dim) * 1.4426950408889634f * (fp8 ? p->q_scale * p->k_scale : 1.f);
   fa.fp8 = fp8;
   fa.v_scale = fp8 ? p->v_scale : 1.f;
+  fa.narrow = narrow;
   const int64_t max_items = L.max_items;
-  const int grid = (int)std::min<int64_t>((int64_t)cu_count() * fwd_blocks_per_cu(p->head_dim, fp8), max_items);
+  const int grid = (int)std::min<int64_t>((int64_t)cu_count() * fwd_blocks_per_cu(p->head_dim, fp8, narrow), max_items);
   const jfa_kernel_events_t* ev = p->events;
   if (ev && record(ev->fwd_start, stream) != hipSuccess) return JFA_ERR_HIP;
   e = launch_fwd(fa, p->head_dim, std::max(grid, 1), stream);
@@ -345,7 +366,8 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   float* dq_part = p->broadcast_q ? at<float>(workspace, L.dq_part) : nullptr;
   const int64_t dq_elems = (int64_t)p->total_q * p->num_heads_q * p->head_dim;
   const int cus = cu_count();
-  const int dq_per_cu = bwd_dq_blocks_per_cu(p->head_dim);
+  const bool narrow = narrow_tiles(p);
+  const int dq_per_cu = bwd_dq_blocks_per_cu(p->head_dim, narrow);
 
   BwdArgs ba{};
   ba.q = (const __bf16*)q;
@@ -371,6 +393,7 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   ba.causal = p->causal;
   ba.scale = scale;
   ba.scale_log2 = scale * 1.4426950408889634f;
+  ba.narrow = narrow;
 
   // Both work lists (dQ: query-stationary, dK/dV: key-stationary) in one launch.
   const bool dq_list = p->total_q > 0 && !p->broadcast_q;
@@ -382,7 +405,7 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
     dq_sa.cu_q = cu_seqlens_q;
     dq_sa.cu_k = cu_seqlens_k;
     dq_sa.batch = p->batch;
-    dq_sa.stat_tile = bwd_dq_rows(p->head_dim);
+    dq_sa.stat_tile = bwd_dq_rows(p->head_dim, narrow);
     dq_sa.loop_tile = bwd_dq_tile(p->head_dim);
     dq_sa.mode = 0;
     dq_sa.causal = p->causal;
@@ -429,7 +452,7 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
 
     // dQ: query-stationary
     if (p->broadcast_q) {
-      const int qtiles = cdiv_i(p->total_q, bwd_dq_rows(p->head_dim));
+      const int qtiles = cdiv_i(p->total_q, bwd_dq_rows(p->head_dim, narrow));
       const int64_t tiles_heads = (int64_t)qtiles * p->num_heads_q;
       ba.bcast_chunks = L.chunks;
       ba.bcast_chunk = cdiv_i(p->batch, L.chunks);

@@ -545,7 +545,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ============================================================================= dQ
-template <int D>
+// NARROW (d = 128): the 4-wave, 128-row workgroup, two per CU, for problems of
+// short sequences, whose items are a few tiles long: two resident workgroups per
+// CU overlap one item's load latency with the other's work.
+template <int D, bool NARROW = false>
 struct DqTile {
   // keys per tile: 32, with the LDS stage double-buffered (one barrier per tile;
   // the next tile's stores leave the critical path); d = 96 splits evenly over
@@ -559,7 +562,7 @@ struct DqTile {
   // 96: two 4-wave workgroups of 128 rows (their tiles do not split over 512
   // threads); d = 192 / 256 keep Q, dO and dQ^T of the whole head in the
   // registers of one wave per SIMD
-  static constexpr int NT = (D <= 128 && (BN * CH) % 512 == 0) ? 512 : 256;
+  static constexpr int NT = (!NARROW && D <= 128 && (BN * CH) % 512 == 0) ? 512 : 256;
   static constexpr int BM = NT / 2;          // query rows per item (32 per wave)
   static constexpr int WG_PER_CU = (NT == 256 && D <= 128) ? 2 : 1;
   static constexpr int KP = D + 8;           // row pitch of K / V tiles
@@ -575,9 +578,9 @@ struct DqTile {
   static_assert(WG_PER_CU * (NSTAGE * (2 * BN * KP + D * KTP) + EP_EL) * 2 <= 160 * 1024, "LDS budget");
 };
 
-template <int D, bool CAUSAL, bool BCAST>
-__global__ __launch_bounds__((DqTile<D>::NT), (DqTile<D>::WG_PER_CU)) void bwd_dq_kernel(BwdArgs a) {
-  using T = DqTile<D>;
+template <int D, bool CAUSAL, bool BCAST, bool NARROW>
+__global__ __launch_bounds__((DqTile<D, NARROW>::NT), (DqTile<D, NARROW>::WG_PER_CU)) void bwd_dq_kernel(BwdArgs a) {
+  using T = DqTile<D, NARROW>;
   constexpr int BM = T::BM, BN = T::BN, KP = T::KP, KTP = T::KTP, KS = T::KS, DB = T::DB;
   constexpr int NSTAGE = T::NSTAGE;
   __shared__ __attribute__((aligned(16))) __bf16 k_lds[NSTAGE][BN * KP];
@@ -859,13 +862,15 @@ int bwd_dkdv_rows(int head_dim) { return head_dim <= 128 ? DkvTile<128>::BM : Dk
 int bwd_dkdv_slices(int head_dim) {
   return head_dim <= 128 ? DkvTile<128>::NC : head_dim <= 192 ? DkvTile<192>::NC : DkvTile<256>::NC;
 }
-int bwd_dq_rows(int head_dim) {
+int bwd_dq_rows(int head_dim, bool narrow) {
+  if (head_dim == 128 && narrow) return DqTile<128, true>::BM;
   return head_dim == 64 ? DqTile<64>::BM : head_dim == 96 ? DqTile<96>::BM : head_dim == 128 ? DqTile<128>::BM : DqTile<256>::BM;
 }
 int bwd_dq_tile(int head_dim) {
   return head_dim == 64 ? DqTile<64>::BN : head_dim == 96 ? DqTile<96>::BN : head_dim == 128 ? DqTile<128>::BN : DqTile<256>::BN;
 }
-int bwd_dq_blocks_per_cu(int head_dim) {
+int bwd_dq_blocks_per_cu(int head_dim, bool narrow) {
+  if (head_dim == 128 && narrow) return DqTile<128, true>::WG_PER_CU;
   return head_dim == 64 ? DqTile<64>::WG_PER_CU : head_dim == 96 ? DqTile<96>::WG_PER_CU
        : head_dim == 128 ? DqTile<128>::WG_PER_CU : DqTile<256>::WG_PER_CU;
 }
@@ -879,13 +884,21 @@ static hipError_t launch_dkdv_d(const BwdArgs& a, int grid, hipStream_t stream) 
   return hipGetLastError();
 }
 
+template <int D, bool NARROW>
+static hipError_t launch_dq_dn(const BwdArgs& a, int grid, hipStream_t stream) {
+  const dim3 g(grid), blk(DqTile<D, NARROW>::NT);
+  if (a.bcast) hipLaunchKernelGGL((bwd_dq_kernel<D, false, true, NARROW>), g, blk, 0, stream, a);
+  else if (a.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true, false, NARROW>), g, blk, 0, stream, a);
+  else hipLaunchKernelGGL((bwd_dq_kernel<D, false, false, NARROW>), g, blk, 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int D>
 static hipError_t launch_dq_d(const BwdArgs& a, int grid, hipStream_t stream) {
-  const dim3 g(grid), blk(DqTile<D>::NT);
-  if (a.bcast) hipLaunchKernelGGL((bwd_dq_kernel<D, false, true>), g, blk, 0, stream, a);
-  else if (a.causal) hipLaunchKernelGGL((bwd_dq_kernel<D, true, false>), g, blk, 0, stream, a);
-  else hipLaunchKernelGGL((bwd_dq_kernel<D, false, false>), g, blk, 0, stream, a);
-  return hipGetLastError();
+  if constexpr (D == 128) {
+    if (a.narrow) return launch_dq_dn<D, true>(a, grid, stream);
+  }
+  return launch_dq_dn<D, false>(a, grid, stream);
 }
 
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int grid, hipStream_t stream) {

@@ -49,7 +49,11 @@ namespace jfa {
 // on v_mfma_f32_32x32x64_f8f6f4 (64-deep k-steps, twice the bf16 rate); V is
 // widened to fp16 (exactly: every e4m3 value is an fp16 value) while it is
 // staged transposed, so P V is the fp16 contraction of the bf16 path.
-template <int D, bool FP8 = false>
+// NARROW: the 4-wave, 128-row workgroup (two per CU) at head dims that otherwise
+// take the 8-wave one; chosen per call for problems of short sequences, where an
+// item is a few tiles long and the latency of its loads, not its work, sets the
+// time: two resident workgroups per CU keep two items in flight.
+template <int D, bool FP8 = false, bool NARROW = false>
 struct FwdTile {
   static constexpr int BN = D <= 192 ? 64 : 32;   // keys per KV tile (d = 256: 32, so nothing spills)
   static constexpr int KB = BN / 32;        // 32-key blocks per tile
@@ -62,7 +66,7 @@ struct FwdTile {
   // CU path, not the HBM, limits the staging); otherwise 4 waves, 128 rows.
   // d = 96 and e4m3 at d = 64 keep 4 waves: their K tile does not split evenly
   // over 512 threads.
-  static constexpr int NT = (D <= 128 && (BN * CH) % 512 == 0) ? 512 : 256;
+  static constexpr int NT = (!NARROW && D <= 128 && (BN * CH) % 512 == 0) ? 512 : 256;
   static constexpr int BM = NT / 2;         // query rows per item (32 per wave)
   static constexpr int KLOADS = BN * CH / NT;
   static constexpr int VBLOCKS = (BN / 4) * (D / 8);   // 4-key x 8-column blocks of V
@@ -104,9 +108,9 @@ __device__ __forceinline__ int vt_quarter_pos(int q) { return ((q & 1) << 1) | (
 
 constexpr float kRescaleThreshold = 8.0f;   // log2 units
 
-template <int D, bool CAUSAL, bool BCAST, bool FP8>
-__global__ __launch_bounds__((FwdTile<D, FP8>::NT), (FwdTile<D, FP8>::WG_PER_CU)) void fwd_kernel(FwdArgs a) {
-  using T = FwdTile<D, FP8>;
+template <int D, bool CAUSAL, bool BCAST, bool FP8, bool NARROW>
+__global__ __launch_bounds__((FwdTile<D, FP8, NARROW>::NT), (FwdTile<D, FP8, NARROW>::WG_PER_CU)) void fwd_kernel(FwdArgs a) {
+  using T = FwdTile<D, FP8, NARROW>;
   constexpr int BM = T::BM, BN = T::BN, KB = T::KB, KP = T::KP, VTP = T::VTP, KS = T::KS, DB = T::DB;
   constexpr int EB = T::EB;
   __shared__ __attribute__((aligned(16))) unsigned char k_raw[2][T::K_LDS_BYTES];
@@ -483,42 +487,51 @@ __global__ __launch_bounds__((FwdTile<D, FP8>::NT), (FwdTile<D, FP8>::WG_PER_CU)
 // defined), the second only here, so no kernel is emitted by both units.
 constexpr bool fwd_in_ilp_unit(int d, bool causal) { return d >= 192 || (causal && d == 128); }
 
+// Head dims with an 8-wave forward, which may run NARROW instead.
+constexpr bool fwd_has_narrow(int d, bool fp8) { return !fp8 && (d == 64 || d == 128); }
+
 #ifndef JFA_FWD_ILP_UNIT
-template <bool FP8>
+template <bool FP8, bool NARROW>
 static int fwd_rows_t(int head_dim) {
   switch (head_dim) {
-    case 64: return FwdTile<64, FP8>::BM;
+    case 64: return FwdTile<64, FP8, NARROW>::BM;
     case 96: return FwdTile<96, false>::BM;
-    case 128: return FwdTile<128, FP8>::BM;
+    case 128: return FwdTile<128, FP8, NARROW>::BM;
     case 192: return FwdTile<192, FP8>::BM;
     default: return FwdTile<256, FP8>::BM;
   }
 }
-template <bool FP8>
+template <bool FP8, bool NARROW>
 static int fwd_wgs_t(int head_dim) {
   switch (head_dim) {
-    case 64: return FwdTile<64, FP8>::WG_PER_CU;
+    case 64: return FwdTile<64, FP8, NARROW>::WG_PER_CU;
     case 96: return FwdTile<96, false>::WG_PER_CU;
-    case 128: return FwdTile<128, FP8>::WG_PER_CU;
+    case 128: return FwdTile<128, FP8, NARROW>::WG_PER_CU;
     case 192: return FwdTile<192, FP8>::WG_PER_CU;
     default: return FwdTile<256, FP8>::WG_PER_CU;
   }
 }
-int fwd_block_rows(int head_dim, bool fp8) { return fp8 ? fwd_rows_t<true>(head_dim) : fwd_rows_t<false>(head_dim); }
+int fwd_block_rows(int head_dim, bool fp8, bool narrow) {
+  narrow = narrow && fwd_has_narrow(head_dim, fp8);
+  return fp8 ? fwd_rows_t<true, false>(head_dim) : narrow ? fwd_rows_t<false, true>(head_dim) : fwd_rows_t<false, false>(head_dim);
+}
 int fwd_kv_tile(int head_dim) { return head_dim <= 128 ? FwdTile<128>::BN : head_dim <= 192 ? FwdTile<192>::BN : FwdTile<256>::BN; }
-int fwd_blocks_per_cu(int head_dim, bool fp8) { return fp8 ? fwd_wgs_t<true>(head_dim) : fwd_wgs_t<false>(head_dim); }
+int fwd_blocks_per_cu(int head_dim, bool fp8, bool narrow) {
+  narrow = narrow && fwd_has_narrow(head_dim, fp8);
+  return fp8 ? fwd_wgs_t<true, false>(head_dim) : narrow ? fwd_wgs_t<false, true>(head_dim) : fwd_wgs_t<false, false>(head_dim);
+}
 
-template <int D, bool FP8>
+template <int D, bool FP8, bool NARROW>
 static hipError_t launch_fwd_dt(const FwdArgs& a, int grid, hipStream_t stream) {
   if (fwd_in_ilp_unit(D, a.causal && !a.bcast)) return launch_fwd_ilp(a, D, FP8, grid, stream);
-  const dim3 g(grid), blk(FwdTile<D, FP8>::NT);
+  const dim3 g(grid), blk(FwdTile<D, FP8, NARROW>::NT);
   if constexpr (!fwd_in_ilp_unit(D, false)) {
     if (a.bcast)
-      hipLaunchKernelGGL((fwd_kernel<D, false, true, FP8>), g, blk, 0, stream, a);
+      hipLaunchKernelGGL((fwd_kernel<D, false, true, FP8, NARROW>), g, blk, 0, stream, a);
     else if (a.causal) {
-      if constexpr (!fwd_in_ilp_unit(D, true)) hipLaunchKernelGGL((fwd_kernel<D, true, false, FP8>), g, blk, 0, stream, a);
+      if constexpr (!fwd_in_ilp_unit(D, true)) hipLaunchKernelGGL((fwd_kernel<D, true, false, FP8, NARROW>), g, blk, 0, stream, a);
     } else
-      hipLaunchKernelGGL((fwd_kernel<D, false, false, FP8>), g, blk, 0, stream, a);
+      hipLaunchKernelGGL((fwd_kernel<D, false, false, FP8, NARROW>), g, blk, 0, stream, a);
   }
   return hipGetLastError();
 }
@@ -526,11 +539,14 @@ static hipError_t launch_fwd_dt(const FwdArgs& a, int grid, hipStream_t stream) 
 template <int D>
 static hipError_t launch_fwd_d(const FwdArgs& a, int grid, hipStream_t stream) {
   if constexpr (D % 64 == 0) {
-    if (a.fp8) return launch_fwd_dt<D, true>(a, grid, stream);
+    if (a.fp8) return launch_fwd_dt<D, true, false>(a, grid, stream);
   } else {
     if (a.fp8) return hipErrorInvalidValue;   // e4m3 needs 64-deep k-steps
   }
-  return launch_fwd_dt<D, false>(a, grid, stream);
+  if constexpr (fwd_has_narrow(D, false)) {
+    if (a.narrow) return launch_fwd_dt<D, false, true>(a, grid, stream);
+  }
+  return launch_fwd_dt<D, false, false>(a, grid, stream);
 }
 
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t stream) {
@@ -545,28 +561,30 @@ hipError_t launch_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t stre
 }
 
 #else
-template <int D, bool FP8>
+template <int D, bool FP8, bool NARROW>
 static hipError_t launch_fwd_ilp_dt(const FwdArgs& a, int grid, hipStream_t stream) {
-  const dim3 g(grid), blk(FwdTile<D, FP8>::NT);
+  const dim3 g(grid), blk(FwdTile<D, FP8, NARROW>::NT);
   const bool causal = a.causal && !a.bcast;
   if (!fwd_in_ilp_unit(D, causal)) return hipErrorInvalidValue;
   if constexpr (fwd_in_ilp_unit(D, false)) {
     if (a.bcast)
-      hipLaunchKernelGGL((fwd_kernel<D, false, true, FP8>), g, blk, 0, stream, a);
+      hipLaunchKernelGGL((fwd_kernel<D, false, true, FP8, NARROW>), g, blk, 0, stream, a);
     else if (!causal)
-      hipLaunchKernelGGL((fwd_kernel<D, false, false, FP8>), g, blk, 0, stream, a);
+      hipLaunchKernelGGL((fwd_kernel<D, false, false, FP8, NARROW>), g, blk, 0, stream, a);
   }
   if constexpr (fwd_in_ilp_unit(D, true)) {
-    if (causal) hipLaunchKernelGGL((fwd_kernel<D, true, false, FP8>), g, blk, 0, stream, a);
+    if (causal) hipLaunchKernelGGL((fwd_kernel<D, true, false, FP8, NARROW>), g, blk, 0, stream, a);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_fwd_ilp(const FwdArgs& a, int head_dim, bool fp8, int grid, hipStream_t stream) {
   switch (head_dim) {
-    case 128: return fp8 ? launch_fwd_ilp_dt<128, true>(a, grid, stream) : launch_fwd_ilp_dt<128, false>(a, grid, stream);
-    case 192: return fp8 ? launch_fwd_ilp_dt<192, true>(a, grid, stream) : launch_fwd_ilp_dt<192, false>(a, grid, stream);
-    case 256: return fp8 ? launch_fwd_ilp_dt<256, true>(a, grid, stream) : launch_fwd_ilp_dt<256, false>(a, grid, stream);
+    case 128:
+      if (fp8) return launch_fwd_ilp_dt<128, true, false>(a, grid, stream);
+      return a.narrow ? launch_fwd_ilp_dt<128, false, true>(a, grid, stream) : launch_fwd_ilp_dt<128, false, false>(a, grid, stream);
+    case 192: return fp8 ? launch_fwd_ilp_dt<192, true, false>(a, grid, stream) : launch_fwd_ilp_dt<192, false, false>(a, grid, stream);
+    case 256: return fp8 ? launch_fwd_ilp_dt<256, true, false>(a, grid, stream) : launch_fwd_ilp_dt<256, false, false>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -87,14 +87,15 @@ struct FwdArgs {
   float scale_log2;         // softmax scale * log2(e) (e4m3: times the Q and K scales)
   int32_t fp8;              // Q, K, V are e4m3 bytes
   float v_scale;            // e4m3: V scale, applied to O
+  int32_t narrow;           // 1: the 4-wave, 128-row workgroups (short sequences; d = 64 / 128, bf16)
 };
 
 hipError_t launch_fwd(const FwdArgs& a, int head_dim, int grid, hipStream_t stream);
 // forward kernels of the iterative-ILP unit (causal d = 128, all d >= 192); called by launch_fwd
 hipError_t launch_fwd_ilp(const FwdArgs& a, int head_dim, bool fp8, int grid, hipStream_t stream);
-int fwd_block_rows(int head_dim, bool fp8);   // BM of the forward kernel
+int fwd_block_rows(int head_dim, bool fp8, bool narrow);   // BM of the forward kernel
 int fwd_kv_tile(int head_dim);   // BN of the forward kernel
-int fwd_blocks_per_cu(int head_dim, bool fp8);
+int fwd_blocks_per_cu(int head_dim, bool fp8, bool narrow);
 
 // Backward.
 struct BwdPreArgs {
@@ -136,15 +137,16 @@ struct BwdArgs {
   int32_t causal;
   float scale;
   float scale_log2;
+  int32_t narrow;           // dQ, d = 128: the 4-wave, 128-row workgroups (short sequences)
 };
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int grid, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int grid, hipStream_t stream);
 int bwd_dkdv_tile();                       // keys per dK/dV item
 int bwd_dkdv_rows(int head_dim);           // query rows per dK/dV step
 int bwd_dkdv_slices(int head_dim);         // head-dim slices (dK/dV items) per key tile
-int bwd_dq_rows(int head_dim);              // query rows per dQ item
+int bwd_dq_rows(int head_dim, bool narrow);            // query rows per dQ item
 int bwd_dq_tile(int head_dim);             // keys per dQ tile
-int bwd_dq_blocks_per_cu(int head_dim);    // resident dQ workgroups per CU
+int bwd_dq_blocks_per_cu(int head_dim, bool narrow);    // resident dQ workgroups per CU
 
 struct DqConvertArgs {
   const float* dq_part;     // [chunks, n] fp32 partials

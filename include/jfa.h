@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define JFA_ABI_VERSION 4
+#define JFA_ABI_VERSION 5
 
 /* Same type as hipStream_t, declared without including the HIP headers. */
 struct ihipStream_t;
@@ -124,6 +124,14 @@ typedef struct {
   float q_scale;          /* e4m3 only: per-tensor scales, each tensor's value = scale x its */
   float k_scale;          /* e4m3 value; finite and > 0.  Ignored for bf16 */
   float v_scale;
+  int32_t query_tile;     /* query rows per forward / dQ work item.  0: chosen from the
+                             lengths (128 when the mean query rows per sequence -- or
+                             broadcast-Q's Nq -- is at most 160, else 256).  128 or 256:
+                             that size wherever the kernel has both (bf16 forward at
+                             d = 64 / 128, dQ at d = 128), ignored elsewhere.  Any other
+                             value is JFA_ERR_INVALID_ARGUMENT.  The result does not
+                             depend on it; the workspace size does, so pass the same
+                             value to the size query and the call. */
   const jfa_kernel_events_t* events;   /* optional kernel timing (NULL: none) */
 } jfa_attn_params_t;
 

@@ -29,7 +29,7 @@ def test_header_declares_and_library_exports():
     for n in names:
         assert hasattr(lib, n), f"missing export {n}"
     assert set(names) == set(L.EXPORTS)
-    assert lib.jfa_abi_version() == L.ABI_VERSION == 4
+    assert lib.jfa_abi_version() == L.ABI_VERSION == 5
 
 
 def test_header_compiles_as_c(tmp_path):
@@ -54,6 +54,7 @@ BAD = [
     (dict(qkv_dtype=1, q_scale=1.0, k_scale=float("inf"), v_scale=1.0), 1),
     (dict(qkv_dtype=1, q_scale=1.0, k_scale=1.0, v_scale=float("nan")), 1),
     (dict(qkv_dtype=1, q_scale=1.0, k_scale=1.0, v_scale=1.0, head_dim=96), 2),
+    (dict(query_tile=64), 1), (dict(query_tile=-1), 1), (dict(query_tile=512), 1),
 ]
 
 
@@ -98,6 +99,24 @@ def test_misaligned_workspace_is_rejected():
                         max_pages_per_seq=5, num_splits=4, softmax_scale=0.0, q_len=1, causal=0)
     nd = lib.jfa_decode_workspace_size(ctypes.byref(pd))
     assert lib.jfa_decode_paged(ctypes.byref(pd), d, d, d, d, d, d, d, mis, nd, None) == L.JFA_ERR_INVALID_ARGUMENT
+
+
+def test_query_tile_sizes_the_work_lists():
+    """query_tile picks the forward / dQ item size where the kernel has two (bf16, d = 64 / 128):
+    128-row items need longer work lists than 256-row ones; elsewhere it changes nothing."""
+    L, lib = _lib()
+    size = lambda f, **kw: f(ctypes.byref(_params(L, batch=4, total_q=4000, total_k=4000, **kw)))
+    for f in (lib.jfa_fwd_workspace_size, lib.jfa_bwd_workspace_size):
+        wide, narrow = size(f, query_tile=256), size(f, query_tile=128)
+        assert narrow > wide > 0
+        # mean 1000 query rows per sequence: the automatic choice is the 256-row item
+        assert size(f, query_tile=0) == wide
+    # mean 100 rows: the automatic choice is the 128-row item
+    p = lambda qt: _params(L, batch=40, total_q=4000, total_k=4000, query_tile=qt)
+    assert lib.jfa_fwd_workspace_size(ctypes.byref(p(0))) == lib.jfa_fwd_workspace_size(ctypes.byref(p(128)))
+    # d = 96 has one shape
+    assert size(lib.jfa_fwd_workspace_size, head_dim=96, query_tile=128) == \
+        size(lib.jfa_fwd_workspace_size, head_dim=96, query_tile=256)
 
 
 def test_empty_problem_is_a_no_op():

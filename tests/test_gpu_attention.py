@@ -28,12 +28,12 @@ def jfa():
     return m
 
 
-def _run_self(jfa, inp, scale=None):
+def _run_self(jfa, inp, scale=None, query_tile=0):
     q, k, v, do = (dev(x, torch) for x in (inp.q, inp.k, inp.v, inp.do))
     cq, ck = dev(inp.cu_q, torch), dev(inp.cu_k, torch)
     mq, mk = inp.max_len_q, inp.max_len_k
-    o, lse = jfa.jfa_fwd(q, k, v, cq, ck, mq, mk, inp.causal, scale)
-    dq, dk, dv = jfa.jfa_bwd(q, k, v, o, lse, do, cq, ck, mq, mk, inp.causal, scale)
+    o, lse = jfa.jfa_fwd(q, k, v, cq, ck, mq, mk, inp.causal, scale, query_tile=query_tile)
+    dq, dk, dv = jfa.jfa_bwd(q, k, v, o, lse, do, cq, ck, mq, mk, inp.causal, scale, query_tile=query_tile)
     torch.cuda.synchronize()
     return host(o), host(lse), host(dq), host(dk), host(dv)
 
@@ -107,6 +107,17 @@ def test_wide_query_tiles(jfa, d, causal):
     inp = workloads.jagged(300 + d, WIDE_TILE, None, 4, 2, d, causal)
     _say(f"wide tiles d={d} causal={causal}")
     _compare_full(_run_self(jfa, inp), _oracle_self(inp))
+
+
+@pytest.mark.parametrize("qt", [128, 256])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+def test_both_query_tiles(jfa, qt, d, causal):
+    """Both item shapes of the forward / dQ (128 and 256 query rows; the automatic
+    choice takes 128 for short sequences) on lengths around either tile size."""
+    inp = workloads.jagged(500 + d + qt, RAGGED + WIDE_TILE, None, 4, 2, d, causal)
+    _say(f"query tile {qt} d={d} causal={causal}")
+    _compare_full(_run_self(jfa, inp, query_tile=qt), _oracle_self(inp))
 
 
 def test_cross_lengths_bottom_right_causal(jfa):
@@ -240,12 +251,13 @@ def test_dense_causal_full_size_sampled(jfa, d):
         _say(f"  seq {b} head {h} ok")
 
 
-def _run_bcast(jfa, inp):
+def _run_bcast(jfa, inp, query_tile=0):
     q, k, v, do = (dev(x, torch) for x in (inp.q, inp.k, inp.v, inp.do))
     ck = dev(inp.cu_k, torch)
     nq = inp.q.shape[0]
-    o, lse = jfa.jfa_fwd(q, k, v, None, ck, nq, inp.max_len_k, False, None, broadcast_q=True)
-    dq, dk, dv = jfa.jfa_bwd(q, k, v, o, lse, do, None, ck, nq, inp.max_len_k, False, None, broadcast_q=True)
+    o, lse = jfa.jfa_fwd(q, k, v, None, ck, nq, inp.max_len_k, False, None, broadcast_q=True, query_tile=query_tile)
+    dq, dk, dv = jfa.jfa_bwd(q, k, v, o, lse, do, None, ck, nq, inp.max_len_k, False, None, broadcast_q=True,
+                             query_tile=query_tile)
     torch.cuda.synchronize()
     return host(o), host(lse), host(dq), host(dk), host(dv)
 
@@ -267,6 +279,15 @@ def test_broadcast_q(jfa, nq, lengths, hq, hkv):
     inp = workloads.broadcast(3, nq, lengths, hq, hkv, 128)
     _say(f"broadcast nq={nq} lengths={lengths}")
     _compare_full(_run_bcast(jfa, inp), _oracle_bcast(inp))
+
+
+@pytest.mark.parametrize("qt", [128, 256])
+@pytest.mark.parametrize("d", [64, 128])
+def test_broadcast_q_both_query_tiles(jfa, qt, d):
+    """Broadcast-Q with either item shape: Nq = 300 is two 256-row tiles or three 128-row ones."""
+    inp = workloads.broadcast(9 + d, 300, [33, 0, 257, 512, 129, 1], 4, 2, d)
+    _say(f"broadcast query tile {qt} d={d}")
+    _compare_full(_run_bcast(jfa, inp, query_tile=qt), _oracle_bcast(inp))
 
 
 @pytest.mark.parametrize("s", [0.9, 0.5, 0.1])
