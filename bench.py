@@ -113,9 +113,10 @@ class JaggedCase:
 
 
 class DecodeCase:
-    def __init__(self, torch, jfa, inp, splits=0, causal=False):
+    def __init__(self, torch, jfa, inp, splits=0, causal=False, single_launch=False):
         self.torch, self.jfa, self.inp = torch, jfa, inp
         self.causal = causal
+        self.single_launch = single_launch
         self.q = dev(inp.q, torch)
         if inp.k_cache.dtype == np.uint8:       # e4m3 bytes
             self.kc = torch.from_numpy(inp.k_cache).to("cuda").view(torch.float8_e4m3fn)
@@ -127,13 +128,14 @@ class DecodeCase:
         self.nsplits = jfa.jfa_decode_num_splits(self.q, self.kc, self.pt, splits)
         self.bytes = decode_bytes(inp)
         n = jfa.jfa_decode_workspace_size(self.q, self.kc, self.pt, splits)
-        self.ws = torch.empty(max(1, n), dtype=torch.uint8, device="cuda")
+        self.ws = torch.zeros(max(1, n), dtype=torch.uint8, device="cuda")   # arrival counters start at zero
         self.o, self.lse = jfa.jfa_decode_paged(self.q, self.kc, self.vc, self.pt, self.sl, splits, causal=causal,
-                                                workspace=self.ws)
+                                                workspace=self.ws, single_launch=single_launch)
 
     def step(self, events=None):
         self.jfa.jfa_decode_paged(self.q, self.kc, self.vc, self.pt, self.sl, self.splits, out=self.o, lse=self.lse,
-                                  workspace=self.ws, causal=self.causal, events=events)
+                                  workspace=self.ws, causal=self.causal, events=events,
+                                  single_launch=self.single_launch)
 
 
 # ----------------------------------------------------------------------------- stored counter data
@@ -519,7 +521,6 @@ def main():
     log(f"inputs generated in {time.time() - t0:.1f}s")
     jc = JaggedCase(torch, jfa, dense_inp)
     dc = DecodeCase(torch, jfa, dec_inp)
-    del dec_inp
 
     for _ in range(args.warmup):
         jc.step()
@@ -569,6 +570,21 @@ def main():
                         "kernels_ms": {k: round(v, 4) for k, v in ek.items()}}
         del case
         torch.cuda.empty_cache()
+
+    # the same decode with the split merge inside the decode launch (single_launch)
+    dc1 = DecodeCase(torch, jfa, dc.inp, single_launch=True)
+    for _ in range(3):
+        dc1.step()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        dc1.step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms1 = e0.elapsed_time(e1) / args.steps
+    extras["decode_single_launch"] = {"value": round(dc.bytes / (ms1 * 1e-3) / 1e12, 3), "unit": "TB/s",
+                                      "ms": round(ms1, 4)}
+    del dc1
 
     # plain device copy of known size: reference for FETCH_SIZE / WRITE_SIZE scaling
     if args.copy_calibration_mib > 0:

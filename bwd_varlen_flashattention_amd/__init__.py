@@ -290,7 +290,7 @@ def _decode_shapes(q, k_cache, v_cache, page_table, seqlens_k):
 
 
 def _decode_params(q, k_cache, page_table, num_splits, scale, causal=False, k_scale=None, v_scale=None,
-                   q_scale=None, events=None):
+                   q_scale=None, events=None, single_launch=False):
     """q is [B, Hq, d] (one token per sequence) or [B, q_len, Hq, d]; an fp8 cache
     or query (float8_e4m3fn, or its raw bytes as uint8) selects the e4m3 path."""
     q_len = 1 if q.dim() == 3 else q.shape[1]
@@ -303,7 +303,7 @@ def _decode_params(q, k_cache, page_table, num_splits, scale, causal=False, k_sc
         q_len=int(q_len), causal=int(bool(causal)), kv_dtype=1 if fp8 else 0,
         k_scale=float(k_scale) if k_scale is not None else 0.0, v_scale=float(v_scale) if v_scale is not None else 0.0,
         q_dtype=1 if q8 else 0, q_scale=float(q_scale) if q_scale is not None else 0.0,
-        events=events.pointer() if events is not None else None)
+        single_launch=int(bool(single_launch)), events=events.pointer() if events is not None else None)
 
 
 def jfa_decode_workspace_size(q, k_cache, page_table, num_splits: int = 0) -> int:
@@ -320,7 +320,8 @@ def jfa_decode_num_splits(q, k_cache, page_table, num_splits: int = 0) -> int:
 def jfa_decode_paged(q, k_cache, v_cache, page_table, seqlens_k, num_splits: int = 0,
                      softmax_scale: Optional[float] = None, out=None, lse=None, workspace=None,
                      causal: bool = False, k_scale: Optional[float] = None, v_scale: Optional[float] = None,
-                     q_scale: Optional[float] = None, events: Optional[KernelEvents] = None):
+                     q_scale: Optional[float] = None, events: Optional[KernelEvents] = None,
+                     single_launch: bool = False):
     """Paged decode of q_len new tokens per sequence against a paged KV cache.
 
     q [B, Hq, d] (one token) or [B, q_len, Hq, d] (q_len <= 16); caches
@@ -328,6 +329,9 @@ def jfa_decode_paged(q, k_cache, v_cache, page_table, seqlens_k, num_splits: int
     causal: the q_len tokens are the last ones of each sequence (bottom-right mask).
     FP8 caches (torch.float8_e4m3fn or raw uint8 bytes): K = k_scale * cache value,
     V = v_scale * cache value.  An FP8 q: Q = q_scale * q value.
+    single_launch: the split partials are merged by the last split of each unit inside
+    the decode launch instead of a second launch; a caller's workspace must then have
+    been zero-filled once when it was allocated (its arrival counters, see jfa.h).
     """
     torch = _torch()
     _decode_shapes(q, k_cache, v_cache, page_table, seqlens_k)
@@ -341,13 +345,15 @@ def jfa_decode_paged(q, k_cache, v_cache, page_table, seqlens_k, num_splits: int
                    lse=lse, workspace=workspace)
     lib = load()
     p = _decode_params(q, k_cache, page_table, num_splits, softmax_scale, causal, k_scale, v_scale, q_scale,
-                       events)
+                       events, single_launch)
     need = lib.jfa_decode_workspace_size(ctypes.byref(p))
     if workspace is not None:
         _check_workspace(workspace, need)
     o = out if out is not None else torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     l = lse if lse is not None else torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
-    ws = workspace if workspace is not None else torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    # a fresh workspace starts with its arrival counters zero (see jfa.h); a
+    # caller's workspace must have been zero-filled once when it was allocated
+    ws = workspace if workspace is not None else torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
     st = lib.jfa_decode_paged(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),
                               _ptr(seqlens_k), _ptr(o), _ptr(l), ws.data_ptr(), ws.numel(), _stream())
     _lib.check(st, "jfa_decode_paged")
@@ -357,7 +363,8 @@ def jfa_decode_paged(q, k_cache, v_cache, page_table, seqlens_k, num_splits: int
 def jfa_decode_paged_noalloc(q, k_cache, v_cache, page_table, seqlens_k, num_splits: int = 0,
                              softmax_scale: Optional[float] = None, out=None, lse=None, causal: bool = False,
                              k_scale: Optional[float] = None, v_scale: Optional[float] = None,
-                             q_scale: Optional[float] = None, events: Optional[KernelEvents] = None):
+                             q_scale: Optional[float] = None, events: Optional[KernelEvents] = None,
+                             single_launch: bool = False):
     """jfa_decode_paged with its split partials in the library's static device array
     instead of a workspace (the library allocates nothing; pass out and lse to
     allocate nothing here either).  Calls overlapping on one GPU race."""
@@ -371,7 +378,7 @@ def jfa_decode_paged_noalloc(q, k_cache, v_cache, page_table, seqlens_k, num_spl
                    lse=lse)
     lib = load()
     p = _decode_params(q, k_cache, page_table, num_splits, softmax_scale, causal, k_scale, v_scale, q_scale,
-                       events)
+                       events, single_launch)
     o = out if out is not None else torch.empty(q.shape, dtype=torch.bfloat16, device=q.device)
     l = lse if lse is not None else torch.empty(q.shape[:-1], dtype=torch.float32, device=q.device)
     st = lib.jfa_decode_paged_noalloc(ctypes.byref(p), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(page_table),

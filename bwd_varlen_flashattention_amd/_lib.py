@@ -24,8 +24,9 @@ EXPORTS = (
     "jfa_decode_workspace_size", "jfa_decode_paged", "jfa_decode_paged_noalloc", "jfa_decode_num_splits",
     "jfa_status_string", "jfa_abi_version",
 )
-ABI_VERSION = 5
+ABI_VERSION = 6
 DECODE_SCRATCH_BYTES = 8 << 20   # JFA_DECODE_SCRATCH_BYTES
+DECODE_COUNTER_BYTES = 256 << 10   # JFA_DECODE_COUNTER_BYTES
 
 
 class KernelEventsStruct(ctypes.Structure):
@@ -75,6 +76,7 @@ class DecodeParams(ctypes.Structure):
         ("v_scale", ctypes.c_float),
         ("q_dtype", ctypes.c_int32),
         ("q_scale", ctypes.c_float),
+        ("single_launch", ctypes.c_int32),
         ("events", ctypes.POINTER(KernelEventsStruct)),
     ]
 

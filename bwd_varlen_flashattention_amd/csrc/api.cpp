@@ -188,6 +188,7 @@ jfa_status_t check_decode(const jfa_decode_params_t* p) {
   if (!(p->softmax_scale == p->softmax_scale) || isinf(p->softmax_scale)) return JFA_ERR_INVALID_ARGUMENT;
   if (!supported_dim(p->head_dim)) return JFA_ERR_UNSUPPORTED;
   if (p->q_len < 1 || p->q_len > 16 || (p->causal != 0 && p->causal != 1)) return JFA_ERR_INVALID_ARGUMENT;
+  if (p->single_launch != 0 && p->single_launch != 1) return JFA_ERR_INVALID_ARGUMENT;
   if (p->kv_dtype != JFA_KV_BF16 && p->kv_dtype != JFA_KV_FP8_E4M3) return JFA_ERR_INVALID_ARGUMENT;
   if (p->q_dtype != JFA_DTYPE_BF16 && p->q_dtype != JFA_DTYPE_FP8_E4M3) return JFA_ERR_INVALID_ARGUMENT;
   if (!(p->q_scale == p->q_scale) || isinf(p->q_scale)) return JFA_ERR_INVALID_ARGUMENT;
@@ -198,13 +199,20 @@ jfa_status_t check_decode(const jfa_decode_params_t* p) {
   return JFA_OK;
 }
 
+// Units (sequence, 16-column query unit, KV head) of one decode split: one arrival
+// counter each.
+int64_t decode_units(const jfa_decode_params_t* p) {
+  const int cols = p->num_heads_q / p->num_heads_kv * p->q_len;
+  const int64_t col_units = cdiv_i(cdiv_i(cols, 16), decode_col_groups(cols, p->head_dim));
+  return (int64_t)p->batch * p->num_heads_kv * col_units;
+}
+
 int resolve_splits(const jfa_decode_params_t* p) {
   if (p->num_splits > 0) return p->num_splits;
   // about two workgroups per resident slot: the later ones fill in behind units
   // of short sequences, which balances mixed lengths
   const int cols = p->num_heads_q / p->num_heads_kv * p->q_len;
-  const int64_t col_units = cdiv_i(cdiv_i(cols, 16), decode_col_groups(cols, p->head_dim));
-  const int64_t units = (int64_t)p->batch * p->num_heads_kv * col_units;
+  const int64_t units = decode_units(p);
   int s = cdiv_i(2 * (int64_t)cu_count() * decode_blocks_per_cu(cols, p->head_dim), units);
   const int64_t max_len = (int64_t)p->max_pages_per_seq * p->page_size;
   const int cap = (int)std::max<int64_t>(1, (max_len + 1023) / 1024);   // at least ~1k keys per split
@@ -214,11 +222,17 @@ int resolve_splits(const jfa_decode_params_t* p) {
   return s;
 }
 
+// Split partials: [arrival counters, JFA_DECODE_COUNTER_BYTES][O_s fp32][LSE_s fp32].
+// The counters sit at a fixed offset with a fixed size, so a workspace reused by
+// decode calls of any shape keeps them zero between calls.
 size_t decode_ws(const jfa_decode_params_t* p, int splits) {
   if (splits <= 1) return 0;
   const size_t plane = (size_t)p->batch * p->q_len * p->num_heads_q;
-  return align_up(plane * splits * p->head_dim * sizeof(float)) + align_up(plane * splits * sizeof(float));
+  return JFA_DECODE_COUNTER_BYTES + align_up(plane * splits * p->head_dim * sizeof(float)) +
+         align_up(plane * splits * sizeof(float));
 }
+static_assert(JFA_DECODE_COUNTER_BYTES == kDecodeCounterSlots * sizeof(uint32_t), "counter region");
+static_assert(JFA_DECODE_COUNTER_BYTES % kAlign == 0, "partials stay aligned");
 
 // ------------------------------------------------------------------ static scratch
 // jfa_decode_paged_noalloc keeps its split partials in this array instead of a
@@ -540,8 +554,14 @@ jfa_status_t jfa_decode_paged(const jfa_decode_params_t* p, const void* q, const
   a.o = (__bf16*)o;
   a.lse = lse;
   const size_t plane = (size_t)p->batch * p->q_len * p->num_heads_q;
-  a.o_part = splits > 1 ? (float*)workspace : nullptr;
-  a.lse_part = splits > 1 ? (float*)((char*)workspace + align_up(plane * splits * p->head_dim * sizeof(float))) : nullptr;
+  char* parts = splits > 1 ? (char*)workspace + JFA_DECODE_COUNTER_BYTES : nullptr;
+  a.o_part = (float*)parts;
+  a.lse_part = splits > 1 ? (float*)(parts + align_up(plane * splits * p->head_dim * sizeof(float))) : nullptr;
+  // single-launch mode: the last split of each unit merges inside the decode
+  // launch, unless there are more units than counters (then, as by default,
+  // decode_combine_kernel runs after the decode kernel)
+  const bool fused = p->single_launch == 1 && splits > 1 && decode_units(p) <= kDecodeCounterSlots;
+  a.counters = fused ? (uint32_t*)workspace : nullptr;
   a.batch = p->batch;
   a.hq = p->num_heads_q;
   a.hkv = p->num_heads_kv;
@@ -562,7 +582,7 @@ jfa_status_t jfa_decode_paged(const jfa_decode_params_t* p, const void* q, const
   hipError_t e = launch_decode(a, p->head_dim, stream);
   if (e != hipSuccess) return JFA_ERR_HIP;
   if (ev && record(ev->decode_stop, stream) != hipSuccess) return JFA_ERR_HIP;
-  if (splits > 1) {
+  if (splits > 1 && !fused) {
     e = launch_decode_combine(a, p->head_dim, stream);
     if (e != hipSuccess) return JFA_ERR_HIP;
   }

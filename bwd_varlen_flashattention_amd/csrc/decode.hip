@@ -20,8 +20,14 @@
 //                             in bf16, as in the forward)
 // The four waves' (max, sum, accumulator) states are merged through LDS at the
 // end.  With one split the result is final (bf16 O, LSE); otherwise each split
-// leaves its normalised fp32 partial and its LSE, and decode_combine merges the
-// partials with weights exp(LSE_s - LSE).
+// leaves its normalised fp32 partial and its LSE, and the partials are merged
+// with weights exp(LSE_s - LSE) (the LSE-weighted combine the split-KV scheme of
+// PR 1940 implies): by decode_combine_kernel in a second launch, or (single-
+// launch mode) by the unit's last split to finish, in the decode launch itself,
+// which learns that it is last from a per-unit arrival counter.  The second
+// launch is the default: on the MI355X the single-launch merge measured 1-2 %
+// slower on 32 sequences of 4k-16k tokens and 5-17 % on batches of 1-8, as every
+// workgroup then waits for its partial stores and the counter before it exits.
 #include <type_traits>
 
 #include "jfa_internal.h"
@@ -90,18 +96,17 @@ __global__ __launch_bounds__(256, (DecOcc<D, NCG>::WG_PER_CU)) void decode_kerne
   const int l16 = lane & 15, g16 = lane >> 4;
   const float NEG_INF = -__builtin_inff();
 
-  // unit = (b, s, column unit, g) with g fastest: the KV heads of one chunk are
-  // neighbouring workgroups, dispatched together, so the token rows they share
-  // are read from DRAM at about the same time
+  // Workgroup -> (chunk, KV head g) with g fastest; chunk = (b rank, split s,
+  // column unit cu) with cu fastest.  The KV heads of one chunk share its token
+  // rows (one row of the cache holds all Hkv heads) and are neighbouring
+  // workgroups, dispatched together.  (Grouping them on one XCD instead --
+  // workgroups go to the XCDs round robin -- was 1.5 % slower.)
   const int cols = a.group * a.q_len;               // query columns of one (sequence, KV head)
   const int n_cu = cdiv(cdiv(cols, 16), NCG);
-  int unit = blockIdx.x;
-  const int g = unit % a.hkv;
-  unit /= a.hkv;
-  const int cu = unit % n_cu;
-  unit /= n_cu;
-  const int s = unit % a.splits;
-  const int b_rank = unit / a.splits;
+  const int ci = blockIdx.x / a.hkv, g = blockIdx.x % a.hkv;
+  const int cu = ci % n_cu;
+  const int s = (ci / n_cu) % a.splits;
+  const int b_rank = ci / n_cu / a.splits;
   // Longest sequences first: the workgroups are dispatched in index order, so the
   // units of long sequences start early and short ones fill in at the end.  The
   // rank is computed from the KV lengths by every workgroup (batches up to
@@ -109,6 +114,7 @@ __global__ __launch_bounds__(256, (DecOcc<D, NCG>::WG_PER_CU)) void decode_kerne
   __shared__ int s_b;
   // set when the fp16 accumulation was not finite (see the recomputation below)
   __shared__ int s_big;
+  __shared__ int s_last;   // this workgroup is the last split of its unit to finish
   if (tid == 0) s_big = 0;
   int b = b_rank;
   if (a.batch <= kLptMaxBatch && tid < a.batch) {
@@ -366,12 +372,88 @@ __global__ __launch_bounds__(256, (DecOcc<D, NCG>::WG_PER_CU)) void decode_kerne
         a.o[row * D + d] = (__bf16)(O * inv);
         if (d == 0) a.lse[row] = lse;
       } else {
+        // device-scope stores: written through to memory, so that another XCD's
+        // device-scope loads see them without an L2 write-back of this XCD
         const int64_t pi = (int64_t)s * a.batch * a.q_len * a.hq + row;
-        a.o_part[pi * D + d] = O * inv;
-        if (d == 0) a.lse_part[pi] = lse;
+        __hip_atomic_store(a.o_part + pi * D + d, O * inv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (d == 0) __hip_atomic_store(a.lse_part + pi, lse, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
     }
     if (cg + 1 < NCG) __syncthreads();   // the merge buffers are rewritten by the next group
+  }
+  if (a.splits == 1 || a.counters == nullptr) return;
+
+  // Arrival.  The XCDs' L2 caches are not coherent with one another, so the
+  // partials were stored at device scope (through to memory) and are read back
+  // at device scope below; every wave waits for its stores to complete before
+  // the workgroup is counted.  (A device-scope fence would do the same by writing
+  // back the whole L2 of the XCD, which cost 3x the decode's time.)  The counter
+  // wraps to zero at the last arrival, so every call leaves it zero.
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);   // vmcnt = expcnt = lgkmcnt = 0: this wave's stores are done
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (tid == 0) {
+    const int idx = (b * n_cu + cu) * a.hkv + g;
+    const unsigned last = (unsigned)(a.splits - 1);
+    s_last = atomicInc(a.counters + idx, last) == last;   // relaxed, device scope
+  }
+  __syncthreads();
+  if (!s_last) return;
+
+  // The unit's columns: weights exp(LSE_s - M) per (column, split) in LDS, then
+  // O = sum_s w_s O_s / sum_s w_s, summed in split order as decode_combine does.
+  const int c_beg = cu * NCG * 16;
+  const int ncol = min(16 * NCG, cols - c_beg);
+  const int64_t plane = (int64_t)a.batch * a.q_len * a.hq;
+  float* w_s = (float*)smem;                               // [16 * NCG][kMaxDecodeSplits]
+  float* mw_s = w_s + 16 * NCG * kMaxDecodeSplits;         // [16 * NCG]: M, then sum of weights
+  float* sw_s = mw_s + 16 * NCG;
+  static_assert((16 * NCG * kMaxDecodeSplits + 2 * 16 * NCG) * 4 <= SMEM, "combine weights fit");
+  auto row_of = [&](int c) {
+    const int t = c / a.group, h = g * a.group + c % a.group;
+    return ((int64_t)b * a.q_len + t) * a.hq + h;
+  };
+  for (int i = tid; i < ncol * a.splits; i += T::NT) {
+    const int c = i / a.splits, sp = i % a.splits;
+    w_s[c * kMaxDecodeSplits + sp] =
+        __hip_atomic_load(a.lse_part + sp * plane + row_of(c_beg + c), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (tid < ncol) {
+    float* wc = w_s + tid * kMaxDecodeSplits;
+    float M = NEG_INF;
+    for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, wc[sp]);
+    float wsum = 0.f;
+    for (int sp = 0; sp < a.splits; ++sp) {
+      const float wt = (M == NEG_INF || wc[sp] == NEG_INF) ? 0.f : __expf(wc[sp] - M);
+      wc[sp] = wt;
+      wsum += wt;
+    }
+    mw_s[tid] = M;
+    sw_s[tid] = wsum;
+  }
+  __syncthreads();
+  const int64_t stride = plane * D;
+  for (int e = tid; e < ncol * D; e += T::NT) {
+    const int c = e / D, d = e % D;
+    const int64_t row = row_of(c_beg + c);
+    const float* op = a.o_part + row * D + d;
+    const float* wc = w_s + c * kMaxDecodeSplits;
+    float O = 0.f;
+    int sp = 0;
+    for (; sp + 8 <= a.splits; sp += 8) {   // eight loads in flight, then the sums in split order
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = __hip_atomic_load(op + (sp + u) * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) O = fmaf(wc[sp + u], x[u], O);
+    }
+    for (; sp < a.splits; ++sp)
+      O = fmaf(wc[sp], __hip_atomic_load(op + sp * stride, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), O);
+    const float wsum = sw_s[c];
+    a.o[row * D + d] = (__bf16)(wsum > 0.f ? O / wsum : 0.f);
+    if (d == 0) a.lse[row] = wsum > 0.f ? mw_s[c] + __logf(wsum) : NEG_INF;
   }
 }
 

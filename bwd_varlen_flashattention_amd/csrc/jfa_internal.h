@@ -6,14 +6,14 @@
 
 namespace jfa {
 
-// Work queues: one per XCD.  Workgroups are dispatched to the XCDs round robin
-// by block index, so block i serves queue i % kQueues first and steals from the
-// others when its own queue runs dry.
-constexpr int kQueues = 8;
+// Workgroups are dispatched to the MI355X's 8 XCDs (each with its own L2) round
+// robin by block index.
+constexpr int kXcds = 8;
 
-// One work item: sequence (or broadcast item) b, tile t along the stationary
-// axis, head h (a query head for query-stationary kernels, a KV head for the
-// key-stationary one).
+// Work queues: one per XCD.  Block i serves queue i % kQueues first and steals
+// from the others when its own queue runs dry.
+constexpr int kQueues = kXcds;
+
 // One work item: sequence b, tile t, head (or head/slice) h, and the sequence's
 // packed offsets and lengths, so a consumer needs one 32-byte load per item.
 struct WorkItem {
@@ -170,6 +170,8 @@ struct DecodeArgs {
   float* lse;
   float* o_part;            // [splits, B, Hq, d] when splits > 1
   float* lse_part;          // [splits, B, Hq]
+  uint32_t* counters;       // per (b, column unit, KV head) arrival counters, zero at the
+                            // start (then the last split merges), or null (decode_combine)
   int32_t batch, hq, hkv, group;
   int32_t page_size;
   int32_t max_pages;
@@ -184,6 +186,7 @@ struct DecodeArgs {
 hipError_t launch_decode(const DecodeArgs& a, int head_dim, hipStream_t stream);
 hipError_t launch_decode_combine(const DecodeArgs& a, int head_dim, hipStream_t stream);
 constexpr int kMaxDecodeSplits = 128;   // largest num_splits the decode accepts
+constexpr int64_t kDecodeCounterSlots = 65536;   // arrival counters at the workspace start
 int decode_chunk_align();
 int decode_col_groups(int columns, int head_dim);      // 16-column query groups per decode workgroup
 int decode_blocks_per_cu(int columns, int head_dim);   // decode workgroups resident per CU

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define JFA_ABI_VERSION 5
+#define JFA_ABI_VERSION 6
 
 /* Same type as hipStream_t, declared without including the HIP headers. */
 struct ihipStream_t;
@@ -209,9 +209,22 @@ enum { JFA_KV_BF16 = JFA_DTYPE_BF16, JFA_KV_FP8_E4M3 = JFA_DTYPE_FP8_E4M3 };
  * columns of one query tile (only real rows: no padding to a fixed tile height),
  * so every KV byte is read once per 64 such columns.  Each sequence's tokens are
  * cut into num_splits contiguous chunks processed in parallel; every chunk
- * leaves a normalised partial output and its LSE, and a final pass merges them
- * with weights exp(LSE_s - LSE).  num_splits = 0 picks a count from the problem
- * size; 1 writes o/lse directly.
+ * leaves a normalised partial output and its LSE in the workspace, and they are
+ * merged with weights exp(LSE_s - LSE): by a second kernel launch (default), or
+ * with single_launch = 1 by the last chunk of each (sequence, KV head) to
+ * finish, inside the decode launch.  num_splits = 0 picks a count from the
+ * problem size; 1 writes o/lse directly and needs no workspace.
+ * Workspace (num_splits > 1): JFA_DECODE_COUNTER_BYTES of per-unit arrival
+ * counters, then the fp32 partials.  Only single_launch = 1 uses the counters,
+ * which must then be zero when the call starts; a call that runs to completion
+ * leaves them zero, so zero-filling a workspace once when it is allocated
+ * (hipMemset, torch.zeros) suffices for every later decode call on it, of any
+ * shape and either mode; anything else written into that region (another entry
+ * point's use of the same buffer) must be cleared again before the next
+ * single-launch call.  The rest of the workspace needs no initialisation.
+ * Problems with more than JFA_DECODE_COUNTER_BYTES / 4 units
+ * (B * Hkv * ceil(ceil(Hq / Hkv * q_len / 16) / 2) at d <= 128) merge in a
+ * second launch in either mode and do not touch the counters.
  * FP8 caches ("Optimizing FlashAttention-4 for Efficient Inference", PR 2109:
  * FP8 inputs): k_cache / v_cache hold OCP e4m3 bytes (same shapes, one byte per
  * element) with per-tensor scales; the result is that of bf16 attention on the
@@ -234,9 +247,17 @@ typedef struct {
   float v_scale;              /* fp8 caches: V = v_scale * e4m3 value (<= 0 means 1) */
   int32_t q_dtype;            /* JFA_DTYPE_BF16 or JFA_DTYPE_FP8_E4M3 (q element type) */
   float q_scale;              /* e4m3 q: Q = q_scale * e4m3 value (<= 0 means 1) */
+  int32_t single_launch;      /* 0: split partials merged by a second launch; 1: by the
+                                 last split of each unit inside the decode launch (needs
+                                 the workspace's counters zero, see above) */
   const jfa_kernel_events_t* events;   /* optional kernel timing (NULL: none) */
 } jfa_decode_params_t;
 
+/* Bytes at the start of a decode workspace that hold arrival counters. */
+#define JFA_DECODE_COUNTER_BYTES ((size_t)256 << 10)
+
+/* Bytes of workspace jfa_decode_paged needs: 0 without splits, else
+ * JFA_DECODE_COUNTER_BYTES + the fp32 partials (0 if the params are invalid). */
 size_t jfa_decode_workspace_size(const jfa_decode_params_t* p);
 
 jfa_status_t jfa_decode_paged(const jfa_decode_params_t* p,
@@ -257,7 +278,8 @@ jfa_status_t jfa_decode_paged(const jfa_decode_params_t* p,
  * any launch; failing to look up the array's address returns JFA_ERR_HIP.
  * Every call on one GPU uses the same array: calls that overlap in time on one
  * GPU (concurrent streams, or host threads) race and must be serialised by the
- * caller.  Nothing in the array needs to start zeroed.
+ * caller.  The array's counter region (its first JFA_DECODE_COUNTER_BYTES) is
+ * zero when the library is loaded and every completed call leaves it zero.
  */
 #define JFA_DECODE_SCRATCH_BYTES ((size_t)8 << 20)
 jfa_status_t jfa_decode_paged_noalloc(const jfa_decode_params_t* p,

@@ -29,7 +29,7 @@ def test_header_declares_and_library_exports():
     for n in names:
         assert hasattr(lib, n), f"missing export {n}"
     assert set(names) == set(L.EXPORTS)
-    assert lib.jfa_abi_version() == L.ABI_VERSION == 5
+    assert lib.jfa_abi_version() == L.ABI_VERSION == 6
 
 
 def test_header_compiles_as_c(tmp_path):
@@ -131,6 +131,7 @@ DEC_BAD = [
     (dict(num_heads_q=30), 1), (dict(num_pages=0), 1),
     (dict(q_len=0), 1), (dict(q_len=17), 1), (dict(causal=2), 1),
     (dict(q_dtype=2), 1), (dict(q_dtype=1, q_scale=float("nan")), 1), (dict(kv_dtype=3), 1),
+    (dict(single_launch=2), 1), (dict(single_launch=-1), 1),
 ]
 
 
@@ -153,6 +154,9 @@ def test_decode_workspace_query():
     p.q_len = 4
     assert lib.jfa_decode_workspace_size(ctypes.byref(p)) >= 4 * 32 * 4 * 32 * 129 * 4   # partials per token
     p.q_len = 1
+    # the arrival counters, then the fp32 partials O_s and LSE_s (each 256-byte aligned)
+    assert lib.jfa_decode_workspace_size(ctypes.byref(p)) == L.DECODE_COUNTER_BYTES + 4 * 32 * 32 * 128 * 4 + 4 * 32 * 32 * 4
+    assert "#define JFA_DECODE_COUNTER_BYTES ((size_t)256 << 10)" in open(HEADER).read()
     p.num_splits = 1
     assert lib.jfa_decode_workspace_size(ctypes.byref(p)) == 0
     d = ctypes.c_void_p(256)

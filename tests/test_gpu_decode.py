@@ -295,3 +295,64 @@ def test_decode_v_beyond_fp16_range(jfa, dim):
         err, bound = np.abs(o - ro), 1e-2 + half_ulp_bf16(ro) + 2.0 ** -7 * mag
         assert np.isfinite(o).all() and (err <= bound).all(), f"splits={splits}: excess {(err - bound).max():.3e}"
         check_lse(lse, rl)
+
+
+def test_decode_single_launch_workspace_reuse(jfa):
+    """single_launch: the last split of each (sequence, KV head) to finish merges the
+    partials inside the decode launch, found through arrival counters at the workspace
+    start that must be zero when a call begins.  One workspace, zeroed once, serves
+    calls of different shapes, split counts and both modes back to back; after every
+    call its counter region is zero again, and each single-launch result equals the
+    two-launch one bit for bit (same sums in the same order) and matches the oracle."""
+    import bwd_varlen_flashattention_amd._lib as L
+    probs = [(workloads.decode(93, [700, 5, 0, 2000, 64], 32, 8, 128, 16), 7, 1),
+             (workloads.decode(94, [3000, 1], 8, 2, 64, 3), 16, 1),
+             (workloads.decode(95, [33, 900, 4000], 16, 4, 128, 16, q_len=3), 5, 3),
+             (workloads.decode(96, [1500] * 40, 32, 8, 256, 128), 3, 1),
+             (workloads.decode(97, [100, 20000], 32, 8, 128, 1), 128, 1)]
+    need = 0
+    for inp, splits, _ in probs:
+        d = _Dev(inp)
+        need = max(need, jfa.jfa_decode_workspace_size(d.q, d.kc, d.pt, splits))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    f = lambda x: x.astype(np.float64)
+    for rep in range(2):
+        for i, (inp, splits, q_len) in enumerate(probs):
+            _say(f"workspace reuse: problem {i} splits={splits} rep={rep}")
+            d = _Dev(inp)
+            o1, l1 = jfa.jfa_decode_paged(d.q, d.kc, d.vc, d.pt, d.sl, splits, workspace=ws, single_launch=True)
+            torch.cuda.synchronize()
+            assert int(ws[:L.DECODE_COUNTER_BYTES].count_nonzero()) == 0, f"problem {i}: counters left non-zero"
+            o2, l2 = jfa.jfa_decode_paged(d.q, d.kc, d.vc, d.pt, d.sl, splits, workspace=ws)
+            torch.cuda.synchronize()
+            assert int(ws[:L.DECODE_COUNTER_BYTES].count_nonzero()) == 0, f"problem {i}: two-launch call wrote counters"
+            np.testing.assert_array_equal(host(o1), host(o2))
+            np.testing.assert_array_equal(host(l1), host(l2))
+            if q_len == 1:
+                ro, rl = oracle.decode_forward(f(inp.q), f(inp.k), f(inp.v), inp.cu_k)
+            else:
+                ro, rl = oracle.decode_forward_multi(f(inp.q), f(inp.k), f(inp.v), inp.cu_k, False)
+            check_o(host(o1), ro, f"O problem {i}")
+            check_lse(host(l1), rl, f"LSE problem {i}")
+
+
+def test_decode_more_units_than_counters(jfa):
+    """8200 sequences x 8 KV heads (one query head each): 65600 units, more than the
+    65536 arrival counters, so a single-launch call merges in a second launch after all.
+    Against the oracle, and bit for bit against the single-launch merge of the first
+    8000 sequences (the same tensors, sliced)."""
+    rng = np.random.default_rng(98)
+    lens = rng.integers(0, 41, 8200).tolist()
+    inp = workloads.decode(99, lens, 8, 8, 64, 16)
+    d = _Dev(inp)
+    ro, rl = _ref(inp)
+    o, lse = jfa.jfa_decode_paged(d.q, d.kc, d.vc, d.pt, d.sl, 2, single_launch=True)
+    torch.cuda.synchronize()
+    o, lse = host(o), host(lse)
+    check_o(o, ro, "O (two launches)")
+    check_lse(lse, rl, "LSE (two launches)")
+    o2, l2 = jfa.jfa_decode_paged(d.q[:8000].contiguous(), d.kc, d.vc, d.pt[:8000].contiguous(),
+                                  d.sl[:8000].contiguous(), 2, single_launch=True)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(host(o2), o[:8000])
+    np.testing.assert_array_equal(host(l2), lse[:8000])
