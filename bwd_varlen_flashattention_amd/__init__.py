@@ -17,7 +17,7 @@ from ._lib import AttnParams, DecodeParams, JfaError, KernelEventsStruct, load  
 
 __all__ = ["jfa_fwd", "jfa_bwd", "jfa_decode_paged", "jfa_decode_num_splits", "jfa_fwd_workspace_size",
            "jfa_bwd_workspace_size", "jfa_decode_workspace_size", "jfa_decode_paged_noalloc", "KernelEvents",
-           "JfaError", "load"]
+           "JfaError", "load", "jfa_check_offsets", "jfa_check_paged_cache"]
 
 
 def _torch():
@@ -310,6 +310,35 @@ def jfa_decode_workspace_size(q, k_cache, page_table, num_splits: int = 0) -> in
     """Workspace bytes jfa_decode_paged needs for these shapes and split count."""
     p = _decode_params(q, k_cache, page_table, num_splits, None)
     return int(load().jfa_decode_workspace_size(ctypes.byref(p)))
+
+
+def jfa_check_offsets(offsets, total: int) -> int:
+    """Device-side check of packed offsets [B + 1] (int32, on the GPU): the OR of the
+    violated JFA_CHECK_* bits (start at 0, non-decreasing, end at `total`), 0 if valid.
+    Waits for the check kernel."""
+    torch = _torch()
+    _check("offsets", offsets, (torch.int32,), (None,))
+    _check_devices(offsets=offsets)
+    if offsets.numel() < 1:
+        raise ValueError("offsets: needs at least one entry")
+    res = torch.empty(1, dtype=torch.int32, device=offsets.device)
+    st = load().jfa_check_offsets(_ptr(offsets), offsets.numel() - 1, int(total), res.data_ptr(), _stream())
+    _lib.check(st, "jfa_check_offsets")
+    return int(res.item())
+
+
+def jfa_check_paged_cache(q, k_cache, page_table, seqlens_k) -> int:
+    """Device-side check of a paged cache's lengths and page table against the cache
+    shape (as jfa_decode_paged would see them): the OR of the violated JFA_CHECK_* bits,
+    0 if valid.  Waits for the check kernel."""
+    torch = _torch()
+    _decode_shapes(q, k_cache, k_cache, page_table, seqlens_k)
+    _check_devices(q=q, k_cache=k_cache, page_table=page_table, seqlens_k=seqlens_k)
+    p = _decode_params(q, k_cache, page_table, 0, None)
+    res = torch.empty(1, dtype=torch.int32, device=q.device)
+    st = load().jfa_check_paged_cache(ctypes.byref(p), _ptr(page_table), _ptr(seqlens_k), res.data_ptr(), _stream())
+    _lib.check(st, "jfa_check_paged_cache")
+    return int(res.item())
 
 
 def jfa_decode_num_splits(q, k_cache, page_table, num_splits: int = 0) -> int:

@@ -22,8 +22,10 @@ JFA_ERR_HIP = 4
 EXPORTS = (
     "jfa_fwd_workspace_size", "jfa_fwd", "jfa_bwd_workspace_size", "jfa_bwd",
     "jfa_decode_workspace_size", "jfa_decode_paged", "jfa_decode_paged_noalloc", "jfa_decode_num_splits",
-    "jfa_status_string", "jfa_abi_version",
+    "jfa_status_string", "jfa_abi_version", "jfa_check_offsets", "jfa_check_paged_cache",
 )
+CHECK_OFFSETS_START, CHECK_OFFSETS_ORDER, CHECK_OFFSETS_END = 1, 2, 4
+CHECK_SEQLEN_RANGE, CHECK_PAGE_RANGE = 8, 16
 ABI_VERSION = 6
 DECODE_SCRATCH_BYTES = 8 << 20   # JFA_DECODE_SCRATCH_BYTES
 DECODE_COUNTER_BYTES = 256 << 10   # JFA_DECODE_COUNTER_BYTES
@@ -116,6 +118,10 @@ def load() -> ctypes.CDLL:
     lib.jfa_decode_paged.restype = ctypes.c_int
     lib.jfa_decode_paged_noalloc.argtypes = [dp, vp, vp, vp, i32p, i32p, vp, vp, vp]
     lib.jfa_decode_paged_noalloc.restype = ctypes.c_int
+    lib.jfa_check_offsets.argtypes = [i32p, ctypes.c_int32, ctypes.c_int32, i32p, vp]
+    lib.jfa_check_offsets.restype = ctypes.c_int
+    lib.jfa_check_paged_cache.argtypes = [dp, i32p, i32p, i32p, vp]
+    lib.jfa_check_paged_cache.restype = ctypes.c_int
     lib.jfa_status_string.argtypes = [ctypes.c_int]
     lib.jfa_status_string.restype = ctypes.c_char_p
     lib.jfa_abi_version.argtypes = []

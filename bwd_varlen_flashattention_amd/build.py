@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libjfa.so")
-SOURCES = ["api.cpp", "sched.hip", "fwd.hip", "fwd_ilp.hip", "bwd.hip", "decode.hip"]
+SOURCES = ["api.cpp", "sched.hip", "fwd.hip", "fwd_ilp.hip", "bwd.hip", "decode.hip", "check.hip"]
 ARCH = "gfx950"
 # Per-source code-generation options.  The backward's key-stationary kernel runs
 # one wave per SIMD, so its LDS reads must be issued well ahead of the MFMAs that

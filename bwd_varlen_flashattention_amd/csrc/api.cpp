@@ -510,6 +510,20 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
   return JFA_OK;
 }
 
+jfa_status_t jfa_check_offsets(const int32_t* offsets, int32_t batch, int32_t total, int32_t* result,
+                               jfa_stream_t stream) {
+  if (!offsets || !result || batch < 0 || total < 0) return JFA_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_check_offsets(offsets, batch, total, result, (hipStream_t)stream));
+}
+
+jfa_status_t jfa_check_paged_cache(const jfa_decode_params_t* p, const int32_t* page_table,
+                                   const int32_t* seqlens_k, int32_t* result, jfa_stream_t stream) {
+  if (!p || !page_table || !seqlens_k || !result) return JFA_ERR_INVALID_ARGUMENT;
+  if (p->batch < 1 || p->page_size < 1 || p->num_pages < 1 || p->max_pages_per_seq < 1) return JFA_ERR_INVALID_ARGUMENT;
+  return hip_status(launch_check_paged(page_table, seqlens_k, p->batch, p->max_pages_per_seq, p->page_size,
+                                       p->num_pages, result, (hipStream_t)stream));
+}
+
 int32_t jfa_decode_num_splits(const jfa_decode_params_t* p) {
   if (check_decode(p) != JFA_OK) return 0;
   return resolve_splits(p);

@@ -188,6 +188,9 @@ hipError_t launch_decode_combine(const DecodeArgs& a, int head_dim, hipStream_t 
 constexpr int kMaxDecodeSplits = 128;   // largest num_splits the decode accepts
 constexpr int64_t kDecodeCounterSlots = 65536;   // arrival counters at the workspace start
 int decode_chunk_align();
+hipError_t launch_check_offsets(const int32_t* cu, int32_t batch, int32_t total, int32_t* result, hipStream_t stream);
+hipError_t launch_check_paged(const int32_t* page_table, const int32_t* seqlens, int32_t batch, int32_t max_pages,
+                              int32_t page_size, int32_t num_pages, int32_t* result, hipStream_t stream);
 int decode_col_groups(int columns, int head_dim);      // 16-column query groups per decode workgroup
 int decode_blocks_per_cu(int columns, int head_dim);   // decode workgroups resident per CU
 

@@ -35,9 +35,11 @@
  *   - Host-checkable errors are returned before anything is launched.  The
  *     library never aborts, throws or prints.  A failed launch returns
  *     JFA_ERR_HIP.
- *   - Device contents are the caller's contract and are not checked: offsets
- *     start at 0, do not decrease and end at the packed total; page ids are
- *     < num_pages; seqlens_k[b] <= max_pages_per_seq * page_size.
+ *   - Device contents are the caller's contract and are not checked by the
+ *     compute entry points: offsets start at 0, do not decrease and end at the
+ *     packed total; page ids are < num_pages; seqlens_k[b] <= max_pages_per_seq *
+ *     page_size.  jfa_check_offsets and jfa_check_paged_cache check them on the
+ *     device on request.
  *   - Sequences (or items) of length 0 are legal.  A query row that sees no key
  *     gets O = 0 and LSE = -inf, and contributes no gradient.
  */
@@ -286,6 +288,33 @@ jfa_status_t jfa_decode_paged_noalloc(const jfa_decode_params_t* p,
                                       const void* q, const void* k_cache, const void* v_cache,
                                       const int32_t* page_table, const int32_t* seqlens_k,
                                       void* o, float* lse, jfa_stream_t stream);
+
+/*
+ * Device-side checks of the input contents the entry points take on trust (the
+ * "device contents" convention above), for debugging a caller: each enqueues one
+ * small kernel on `stream` that reads only the array it checks, within the sizes
+ * passed, and writes to *result (a device int32) the OR of the JFA_CHECK_* bits
+ * of every violation found, 0 if there is none.  Nothing else is written, and
+ * bad contents are reported, never dereferenced.  Host-checkable errors (null
+ * pointers, negative sizes) return JFA_ERR_INVALID_ARGUMENT before any launch.
+ *
+ * jfa_check_offsets: offsets [batch + 1] of a packed layout (cu_seqlens_q or
+ *   cu_seqlens_k of jfa_fwd / jfa_bwd) must start at 0, not decrease and end at
+ *   total (T_q or T_k).
+ * jfa_check_paged_cache: with p's batch, page_size, num_pages and
+ *   max_pages_per_seq, every seqlens_k[b] must lie in
+ *   [0, max_pages_per_seq * page_size] and every page id a sequence uses
+ *   (page_table[b][0 .. ceil(seqlens_k[b] / page_size) - 1]) in [0, num_pages).
+ */
+#define JFA_CHECK_OFFSETS_START 1    /* offsets[0] != 0 */
+#define JFA_CHECK_OFFSETS_ORDER 2    /* some offsets[b + 1] < offsets[b] */
+#define JFA_CHECK_OFFSETS_END 4      /* offsets[batch] != total */
+#define JFA_CHECK_SEQLEN_RANGE 8     /* some seqlens_k[b] < 0 or > max_pages_per_seq * page_size */
+#define JFA_CHECK_PAGE_RANGE 16      /* some used page id < 0 or >= num_pages */
+jfa_status_t jfa_check_offsets(const int32_t* offsets, int32_t batch, int32_t total, int32_t* result,
+                               jfa_stream_t stream);
+jfa_status_t jfa_check_paged_cache(const jfa_decode_params_t* p, const int32_t* page_table,
+                                   const int32_t* seqlens_k, int32_t* result, jfa_stream_t stream);
 
 /* The split count jfa_decode_paged uses for p (resolves num_splits = 0). */
 int32_t jfa_decode_num_splits(const jfa_decode_params_t* p);

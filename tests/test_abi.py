@@ -249,3 +249,25 @@ def test_noalloc_decode_rejects_problems_beyond_its_scratch():
     assert lib.jfa_decode_paged_noalloc(ctypes.byref(p), d, d, d, d, d, d, d, None) == L.JFA_ERR_INVALID_ARGUMENT
     text = open(HEADER).read()
     assert "#define JFA_DECODE_SCRATCH_BYTES ((size_t)8 << 20)" in text and L.DECODE_SCRATCH_BYTES == 8 << 20
+
+
+def test_input_checks_reject_host_errors_before_launch():
+    """jfa_check_offsets / jfa_check_paged_cache: null pointers and bad sizes are
+    refused on the host; the JFA_CHECK_* bits match the binding's constants."""
+    L, lib = _lib()
+    d = ctypes.c_void_p(256)
+    assert lib.jfa_check_offsets(None, 4, 10, d, None) == L.JFA_ERR_INVALID_ARGUMENT
+    assert lib.jfa_check_offsets(d, 4, 10, None, None) == L.JFA_ERR_INVALID_ARGUMENT
+    assert lib.jfa_check_offsets(d, -1, 10, d, None) == L.JFA_ERR_INVALID_ARGUMENT
+    assert lib.jfa_check_offsets(d, 4, -10, d, None) == L.JFA_ERR_INVALID_ARGUMENT
+    p = L.DecodeParams(batch=2, num_heads_q=32, num_heads_kv=8, head_dim=128, page_size=16, num_pages=10,
+                       max_pages_per_seq=5, num_splits=0, softmax_scale=0.0, q_len=1, causal=0)
+    assert lib.jfa_check_paged_cache(None, d, d, d, None) == L.JFA_ERR_INVALID_ARGUMENT
+    assert lib.jfa_check_paged_cache(ctypes.byref(p), None, d, d, None) == L.JFA_ERR_INVALID_ARGUMENT
+    assert lib.jfa_check_paged_cache(ctypes.byref(p), d, d, None, None) == L.JFA_ERR_INVALID_ARGUMENT
+    p.page_size = 0
+    assert lib.jfa_check_paged_cache(ctypes.byref(p), d, d, d, None) == L.JFA_ERR_INVALID_ARGUMENT
+    text = open(HEADER).read()
+    for name in ("OFFSETS_START", "OFFSETS_ORDER", "OFFSETS_END", "SEQLEN_RANGE", "PAGE_RANGE"):
+        m = re.search(rf"#define JFA_CHECK_{name} (\d+)", text)
+        assert m and int(m.group(1)) == getattr(L, f"CHECK_{name}"), name
