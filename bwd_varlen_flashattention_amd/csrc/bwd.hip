@@ -317,7 +317,24 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     // (buffer range).  All key tiles of a (sequence, KV head) walk the query
     // tiles in the same order, so the ones running together on an XCD find the
     // same Q/dO tiles in its L2.
-    auto unit_of = [&](int s) { return s; };
+    // Causal: only the first n_diag query tiles of each head reach past this key
+    // tile's diagonal and need the mask.  Those steps run first, for every head,
+    // then the unmasked ones (one head at a time, tiles in increasing order).
+    // (d = 192 keeps one masked step body: the second one makes it spill.)
+    constexpr bool SPLIT_MASK = CAUSAL && D != 192;
+    int n_diag = 0;
+    if constexpr (SPLIT_MASK) {
+      const int last_key = kt0 + BN - 1 - off;   // the tile's last key, in query-row units
+      n_diag = last_key < 0 ? 0 : max(0, min(n_qt, last_key / BM - i_first + 1));
+    }
+    const int n_mask = n_diag * a.group;
+    const int n_rest = n_qt - n_diag;
+    auto unit_of = [&](int s) {
+      if (!SPLIT_MASK) return s;
+      if (s < n_mask) return (s / n_diag) * n_qt + s % n_diag;
+      const int r = s - n_mask;
+      return (r / n_rest) * n_qt + n_diag + r % n_rest;
+    };
     u32x4 sr[8];   // staged rows: 8 rows of one tile, or 4 rows of Q then 4 of dO
     // LSE and delta travel raw (range-checked buffer loads) and are only looked
     // at when they are written to LDS: consuming them right after the load would
@@ -400,7 +417,9 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       }
     };
 
-    auto step = [&](int s) {
+    // MASK (a std::bool_constant): the step applies the causal mask
+    auto step = [&](int s, auto mask_tag) {
+      constexpr bool MASK = decltype(mask_tag)::value;
       const int buf = s & 1;
       const int qt = i_first + unit_of(s) % n_qt;
       if (s + 1 < n_steps) load_regs(s + 1);
@@ -429,7 +448,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
           for (int x = 0; x < 4; ++x) {
             const int r = 4 * r4 + x;
             float p = fast_exp2(fmaf(sacc[r], a.scale_log2, -l4[x]));
-            if constexpr (CAUSAL) p = (my_key <= qt * BM + q0 + x + off) ? p : 0.f;
+            if constexpr (MASK) p = (my_key <= qt * BM + q0 + x + off) ? p : 0.f;
             pv[r] = p;
             dsv[r] = p * (pacc[r] - d4[x]);
           }
@@ -492,9 +511,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         store_lds(0);
         __syncthreads();
       }
-      // causal masking is one compare per element in every step: a single step
-      // body keeps the register allocation of the causal kernel free of spills
-      for (int s = 0; s < n_steps; ++s) step(s);
+      // Causal: only the query tiles of a head that reach past this key tile's
+      // diagonal (the first n_diag of each head's n_qt) need the mask; the
+      // others run the step without it.
+      if constexpr (SPLIT_MASK) {
+        int s = 0;
+        for (; s < n_mask; ++s) step(s, std::true_type{});
+        for (; s < n_steps; ++s) step(s, std::false_type{});
+      } else {
+        for (int s = 0; s < n_steps; ++s) step(s, std::bool_constant<CAUSAL>{});
+      }
     }
 
     // epilogue: dK = scale * dK^T, dV = dV^T of the owned slice.  A lane holds 4
