@@ -788,9 +788,14 @@ __global__ __launch_bounds__((DqTile<D, NARROW>::NT), (DqTile<D, NARROW>::WG_PER
         }
         if (s + 1 < n_tiles) load_regs(tile_of(s + 1));
         const int kmax_ok = CAUSAL ? min(lk - 1, my_row + off) : lk - 1;
-        // a wave whose 32 rows all lie past the sequence end only stages and syncs
+        // a wave whose 32 rows all lie past the sequence end only stages and syncs;
+        // in a causal diagonal tile, so does a wave for the 32-key blocks past its
+        // last row's diagonal (the blocks are in key order: the live ones come first)
+        int live_kb = wave_rows ? BN / 32 : 0;
+        if (CAUSAL && MASK && wave_rows)
+          live_kb = max(0, min(BN / 32, cdiv(row0 + 32 * w + 31 + off + 1 - j * BN, 32)));
 #pragma unroll
-        for (int kb = 0; kb < (wave_rows ? BN / 32 : 0); ++kb) {
+        for (int kb = 0; kb < live_kb; ++kb) {
           // S^T[key][q] = K Q^T and dP^T[key][q] = V dO^T for 32 keys
           f32x16 st = f32x16{}, pt = f32x16{};
           const __bf16* kp = &k_lds[stg][(32 * kb + l32) * KP + 8 * hh];

@@ -289,8 +289,9 @@ __global__ __launch_bounds__((FwdTile<D, FP8, NARROW>::NT), (FwdTile<D, FP8, NAR
       const int buf = step & 1;
       const int j = tile_of(step);
       if (step + 1 < n_tiles) load_regs(tile_of(step + 1));
-      // a wave whose 32 rows all lie past the sequence end only stages and syncs
-      if (wave_rows) {
+      // a wave whose 32 rows all lie past the sequence end only stages and syncs,
+      // and so does one whose rows all lie before a causal diagonal tile's first key
+      if (wave_rows && !(CAUSAL && MASK && j * BN > row0 + 32 * w + 31 + off)) {
       // S^T[key][query] for the tile's 32-key blocks
       f32x16 s[KB];
 #pragma unroll
