@@ -143,18 +143,21 @@ KERNEL_SLOTS = ("fwd", "bwd_dq", "bwd_dkdv", "decode")
 # kernel name prefixes of the slots
 SLOT_KERNEL = {"fwd": "fwd_kernel", "bwd_dq": "bwd_dq_kernel", "bwd_dkdv": "bwd_dkdv_kernel", "decode": "decode_kernel"}
 # template arguments that tell the bench step's workloads apart (head dim, causal, broadcast[, fp8])
+# (fwd_kernel<d, causal, broadcast, fp8, narrow>, bwd_dq_kernel<d, causal, broadcast, narrow>,
+#  bwd_dkdv_kernel<d, causal, broadcast>; the bench workloads take the 256-row shapes)
 WORKLOAD_KERNELS = {
-    "dense_causal_d128": {"fwd": "fwd_kernel<128, true, false, false>", "bwd_dq": "bwd_dq_kernel<128, true, false>",
+    "dense_causal_d128": {"fwd": "fwd_kernel<128, true, false, false, false>",
+                          "bwd_dq": "bwd_dq_kernel<128, true, false, false>",
                           "bwd_dkdv": "bwd_dkdv_kernel<128, true, false>"},
-    "gem_s0.5": {"fwd": "fwd_kernel<128, false, false, false>", "bwd_dq": "bwd_dq_kernel<128, false, false>",
+    "gem_s0.5": {"fwd": "fwd_kernel<128, false, false, false, false>", "bwd_dq": "bwd_dq_kernel<128, false, false, false>",
                  "bwd_dkdv": "bwd_dkdv_kernel<128, false, false>"},
-    "bcast_s0.5": {"fwd": "fwd_kernel<128, false, true, false>", "bwd_dq": "bwd_dq_kernel<128, false, true>",
+    "bcast_s0.5": {"fwd": "fwd_kernel<128, false, true, false, false>", "bwd_dq": "bwd_dq_kernel<128, false, true, false>",
                    "bwd_dkdv": "bwd_dkdv_kernel<128, false, true>"},
     "decode_ps16": {"decode": "decode_kernel<128, 1, false>"},
 }
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_bench_step.txt")
 COUNTER_PROFILE = os.path.join(ROOT, "profiles", "mfma_lds_counters_bench_step.md")
-BENCH_CMD = "python3 $REPO/bench.py --steps 2 --warmup 1 --cpu-sample 0"
+BENCH_CMD = "python3 $REPO/bench.py --steps 2 --warmup 1 --cpu-sample 0 --single-launch-steps 0"
 
 
 def source_digest() -> str:
@@ -375,7 +378,7 @@ def trace_summary(db: str, timed: str, out: str):
         "```",
         "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --kernel-trace --stats -d "
         "$REPO/gpurun_out/prof_bench -o bench -- python3 $REPO/bench.py --steps 10 --warmup 3 --cpu-sample 0 "
-        "> $REPO/gpurun_out/prof_bench.json",
+        "--single-launch-steps 0 > $REPO/gpurun_out/prof_bench.json",
         "python3 bench.py --trace-summary gpurun_out/prof_bench/bench_results.db gpurun_out/prof_bench.json",
         "```",
         "",
@@ -478,6 +481,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--page-size", type=int, default=16)
     ap.add_argument("--extra-steps", type=int, default=10, help="timed calls of each extra workload (GEM, broadcast-Q)")
+    ap.add_argument("--single-launch-steps", type=int, default=20,
+                    help="timed calls of the decode in single-launch mode, after the steps (0 = skip)")
     ap.add_argument("--cpu-sample", type=int, default=16, help="heads of sequence 0 in the oracle timing sample (0 = skip)")
     ap.add_argument("--sweep", action="store_true", help="one JSON line per workload (GEM s, broadcast-Q, dense, decode)")
     ap.add_argument("--copy-calibration-mib", type=int, default=1024,
@@ -571,20 +576,22 @@ def main():
         del case
         torch.cuda.empty_cache()
 
-    # the same decode with the split merge inside the decode launch (single_launch)
-    dc1 = DecodeCase(torch, jfa, dc.inp, single_launch=True)
-    for _ in range(3):
-        dc1.step()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        dc1.step()
-    e1.record()
-    torch.cuda.synchronize()
-    ms1 = e0.elapsed_time(e1) / args.steps
-    extras["decode_single_launch"] = {"value": round(dc.bytes / (ms1 * 1e-3) / 1e12, 3), "unit": "TB/s",
-                                      "ms": round(ms1, 4)}
-    del dc1
+    # the same decode, back to back in both modes: split merge in a second launch
+    # (the default, as in the steps) and inside the decode launch (single_launch)
+    if args.single_launch_steps > 0:
+        dc1 = DecodeCase(torch, jfa, dc.inp, single_launch=True)
+        for mode, case in (("decode_two_launches", dc), ("decode_single_launch", dc1)):
+            for _ in range(3):
+                case.step()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.single_launch_steps):
+                case.step()
+            e1.record()
+            torch.cuda.synchronize()
+            ms1 = e0.elapsed_time(e1) / args.single_launch_steps
+            extras[mode] = {"value": round(dc.bytes / (ms1 * 1e-3) / 1e12, 3), "unit": "TB/s", "ms": round(ms1, 4)}
+        del dc1
 
     # plain device copy of known size: reference for FETCH_SIZE / WRITE_SIZE scaling
     if args.copy_calibration_mib > 0:
