@@ -571,6 +571,35 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
 }
 
 // ============================================================================= dQ
+// Broadcast-Q dQ splits the items into chunks of about equal cost (key tiles,
+// plus one for an item's own loads): the cost prefix over the items lives in LDS
+// for up to kBcastPrefixItems items, beyond which chunks hold equal item counts.
+constexpr int kBcastPrefixItems = 2048;
+
+// Exclusive prefix sum of one value per thread over the workgroup (blockDim a
+// multiple of 64, at most 16 waves); *total receives the sum.  wave_tot: 16 ints
+// of LDS.  Two barriers.
+__device__ int block_exclusive_scan(int x, int* wave_tot, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int incl = x;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += y;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int before = 0, sum = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int t = wave_tot[w];
+    before += w < wave ? t : 0;
+    sum += t;
+  }
+  *total = sum;
+  __syncthreads();
+  return before + incl - x;
+}
+
 // NARROW (d = 128): the 4-wave, 128-row workgroup, two per CU, for problems of
 // short sequences, whose items are a few tiles long: two resident workgroups per
 // CU overlap one item's load latency with the other's work.
@@ -639,6 +668,44 @@ __global__ __launch_bounds__((DqTile<D, NARROW>::NT), (DqTile<D, NARROW>::WG_PER
     voff[i] = (uint32_t)(((id / T::CH) * rs + (id % T::CH) * 8) * 2);
   }
 
+  // Broadcast-Q chunks: cost prefix of the items (s_pre[b] = cost of items < b),
+  // chunk c = the items whose prefix lies in [c, c + 1) * total / chunks.  Every
+  // workgroup derives the same boundaries from the offsets, so the chunking (and
+  // the chunk-ordered dQ sum) depends on the lengths alone.
+  __shared__ int s_pre[BCAST ? kBcastPrefixItems + 1 : 1];
+  __shared__ int s_wave_tot[16];
+  const bool by_cost = BCAST && a.batch <= kBcastPrefixItems;
+  if (BCAST && by_cost) {
+    const int per = cdiv(a.batch, T::NT);
+    const int lo = min(tid * per, a.batch), hi = min(lo + per, a.batch);
+    auto cost = [&](int b) {
+      const int lk = a.cu_k[b + 1] - a.cu_k[b];
+      return lk > 0 ? cdiv(lk, BN) + 1 : 0;
+    };
+    int run = 0;
+    for (int b = lo; b < hi; ++b) run += cost(b);
+    int total;
+    int base = block_exclusive_scan(run, s_wave_tot, &total);
+    for (int b = lo; b < hi; ++b) {
+      s_pre[b] = base;
+      base += cost(b);
+    }
+    if (tid == 0) s_pre[a.batch] = total;
+    __syncthreads();
+  }
+  // first item of chunk c: the smallest b with s_pre[b] * chunks >= c * total
+  auto chunk_start = [&](int c) {
+    if (!by_cost) return min(a.batch, c * a.bcast_chunk);
+    const int64_t want = (int64_t)c * s_pre[a.batch];
+    int lo = 0, hi = a.batch;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if ((int64_t)s_pre[mid] * a.bcast_chunks >= want) hi = mid;
+      else lo = mid + 1;
+    }
+    return lo;
+  };
+
   // Work: self-attention pulls (sequence, query tile, head) items from the per-XCD
   // work queues; broadcast-Q owns (query tile, head, chunk of items) by block index.
   int bcast_item = blockIdx.x;
@@ -661,8 +728,8 @@ __global__ __launch_bounds__((DqTile<D, NARROW>::NT), (DqTile<D, NARROW>::WG_PER
       const int rem = bcast_item % per_tile;
       h = rem / a.bcast_chunks;
       chunk = rem % a.bcast_chunks;
-      b_lo = chunk * a.bcast_chunk;
-      b_hi = min(a.batch, b_lo + a.bcast_chunk);
+      b_lo = chunk_start(chunk);
+      b_hi = chunk_start(chunk + 1);
       bcast_item += gridDim.x;
     } else {
       if (item < 0) break;
@@ -683,6 +750,16 @@ __global__ __launch_bounds__((DqTile<D, NARROW>::NT), (DqTile<D, NARROW>::WG_PER
     f32x16 dqt[DB];
 #pragma unroll
     for (int db = 0; db < DB; ++db) dqt[db] = f32x16{};
+
+    // Q fragment: B operand of S^T = K Q^T.  Broadcast-Q shares one Q among all
+    // items, so it is loaded once per unit; self-attention loads it per item below.
+    bf16x8 qf[KS];
+    if constexpr (BCAST) {
+      const bool q_ok = my_row < a.bcast_nq;
+      const __bf16* qp = a.q + ((int64_t)my_row * a.hq + h) * D + 8 * hh;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qf[ks] = q_ok ? *(const bf16x8*)(qp + 16 * ks) : zero_bf16x8();
+    }
 
     for (int b = b_lo; b < b_hi; ++b) {
       int lq, q_base, k_base, lk;
@@ -742,7 +819,7 @@ __global__ __launch_bounds__((DqTile<D, NARROW>::NT), (DqTile<D, NARROW>::WG_PER
       if (n_tiles > 0) load_regs(tile_of(0));
 
       // per-row state: Q and dO fragments (B operands of S^T = K Q^T, dP^T = V dO^T), LSE, delta
-      bf16x8 qf[KS], df[KS];
+      bf16x8 df[KS];
       float lse2 = INF, dlt = 0.f;
       {
         const __bf16* qp = a.q + ((int64_t)(q_base + my_row) * a.hq + h) * D + 8 * hh;
@@ -750,7 +827,7 @@ __global__ __launch_bounds__((DqTile<D, NARROW>::NT), (DqTile<D, NARROW>::WG_PER
         const __bf16* op = a.dout + (orow * a.hq + h) * D + 8 * hh;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-          qf[ks] = row_ok ? *(const bf16x8*)(qp + 16 * ks) : zero_bf16x8();
+          if constexpr (!BCAST) qf[ks] = row_ok ? *(const bf16x8*)(qp + 16 * ks) : zero_bf16x8();
           df[ks] = row_ok ? *(const bf16x8*)(op + 16 * ks) : zero_bf16x8();
         }
         const int64_t li = BCAST ? ((int64_t)b * a.hq + h) * lq + my_row : (int64_t)h * a.total_q + q_base + my_row;
