@@ -668,10 +668,11 @@ __global__ __launch_bounds__((DqTile<D, NARROW>::NT), (DqTile<D, NARROW>::WG_PER
     voff[i] = (uint32_t)(((id / T::CH) * rs + (id % T::CH) * 8) * 2);
   }
 
-  // Broadcast-Q chunks: cost prefix of the items (s_pre[b] = cost of items < b),
-  // chunk c = the items whose prefix lies in [c, c + 1) * total / chunks.  Every
-  // workgroup derives the same boundaries from the offsets, so the chunking (and
-  // the chunk-ordered dQ sum) depends on the lengths alone.
+  // Broadcast-Q chunks: item b owns the cost positions [s_pre[b], s_pre[b + 1]):
+  // one for its own loads, then one per key tile.  Chunk c takes the positions
+  // [c, c + 1) * total / chunks, so an item's key tiles may be split between two
+  // chunks.  Every workgroup derives the same cuts from the offsets, so the
+  // chunking (and the chunk-ordered dQ sum) depends on the lengths alone.
   __shared__ int s_pre[BCAST ? kBcastPrefixItems + 1 : 1];
   __shared__ int s_wave_tot[16];
   const bool by_cost = BCAST && a.batch <= kBcastPrefixItems;
@@ -693,14 +694,16 @@ __global__ __launch_bounds__((DqTile<D, NARROW>::NT), (DqTile<D, NARROW>::WG_PER
     if (tid == 0) s_pre[a.batch] = total;
     __syncthreads();
   }
-  // first item of chunk c: the smallest b with s_pre[b] * chunks >= c * total
-  auto chunk_start = [&](int c) {
-    if (!by_cost) return min(a.batch, c * a.bcast_chunk);
-    const int64_t want = (int64_t)c * s_pre[a.batch];
-    int lo = 0, hi = a.batch;
+  // first cost position of chunk c, and the smallest b in [lo, batch] with
+  // s_pre[b] > pos (strict) or >= pos
+  auto chunk_pos = [&](int c) {
+    return (int)(((int64_t)c * s_pre[a.batch] + a.bcast_chunks - 1) / a.bcast_chunks);
+  };
+  auto first_item = [&](int lo, int pos, bool strict) {
+    int hi = a.batch;
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if ((int64_t)s_pre[mid] * a.bcast_chunks >= want) hi = mid;
+      if (strict ? s_pre[mid] > pos : s_pre[mid] >= pos) hi = mid;
       else lo = mid + 1;
     }
     return lo;
@@ -720,6 +723,7 @@ __global__ __launch_bounds__((DqTile<D, NARROW>::NT), (DqTile<D, NARROW>::WG_PER
   }
   for (;;) {
     int b_lo, b_hi, h, qtile, chunk = 0;
+    int pos_lo = 0, pos_hi = 0;   // broadcast-Q, by cost: the chunk's cost positions
     int e_qbase = 0, e_lq = 0, e_kbase = 0, e_lk = 0;   // self-attention: the item's sequence
     if (BCAST) {
       if (bcast_item >= a.bcast_units) break;
@@ -728,8 +732,15 @@ __global__ __launch_bounds__((DqTile<D, NARROW>::NT), (DqTile<D, NARROW>::WG_PER
       const int rem = bcast_item % per_tile;
       h = rem / a.bcast_chunks;
       chunk = rem % a.bcast_chunks;
-      b_lo = chunk_start(chunk);
-      b_hi = chunk_start(chunk + 1);
+      if (by_cost) {
+        pos_lo = chunk_pos(chunk);
+        pos_hi = chunk_pos(chunk + 1);
+        b_lo = max(0, first_item(1, pos_lo, true) - 1);   // the item holding position pos_lo
+        b_hi = first_item(0, pos_hi, false);               // the first item starting at or past pos_hi
+      } else {
+        b_lo = min(a.batch, chunk * a.bcast_chunk);
+        b_hi = min(a.batch, b_lo + a.bcast_chunk);
+      }
       bcast_item += gridDim.x;
     } else {
       if (item < 0) break;
@@ -779,6 +790,16 @@ __global__ __launch_bounds__((DqTile<D, NARROW>::NT), (DqTile<D, NARROW>::WG_PER
         n_tiles = cdiv(lk, BN);
         n_bulk = lk / BN;
       }
+      // broadcast-Q by cost: the item's key tiles [t0, t0 + n_tiles) that fall
+      // into this chunk's positions (the item's first position is its own loads)
+      int t0 = 0;
+      if (BCAST && by_cost) {
+        const int pb = s_pre[b] + 1;
+        t0 = max(0, pos_lo - pb);
+        const int t1 = min(n_tiles, pos_hi - pb);
+        n_bulk = max(0, min(n_bulk, t1) - t0);
+        n_tiles = max(0, t1 - t0);
+      }
       if (BCAST && n_tiles == 0) continue;   // uniform
 
       const __bf16* kbase = a.k + ((int64_t)k_base * a.hkv + g) * D;
@@ -814,7 +835,7 @@ __global__ __launch_bounds__((DqTile<D, NARROW>::NT), (DqTile<D, NARROW>::WG_PER
       // Key-tile order: bulk tiles first, masked tiles last, the same order for
       // every item sharing this K/V (they run together on one XCD and find the
       // same K/V tiles in its L2).
-      auto tile_of = [&](int s) { return s; };
+      auto tile_of = [&](int s) { return t0 + s; };
       // the first K/V tile travels with the Q / dO / O fragments: one round trip
       if (n_tiles > 0) load_regs(tile_of(0));
 
