@@ -290,6 +290,20 @@ def test_broadcast_q_both_query_tiles(jfa, qt, d):
     _compare_full(_run_bcast(jfa, inp, query_tile=qt), _oracle_bcast(inp))
 
 
+@pytest.mark.parametrize("d", [64, 96, 128])
+def test_broadcast_q_chunks_split_items(jfa, d):
+    """Broadcast-Q dQ cuts its item chunks at equal cost, at key-tile granularity, so a
+    long item's tiles are shared by two chunks: 40 items of 0-900 keys (ragged tails,
+    empty items), Nq = 100, at each dQ tile shape (d = 96: one 64-key stage)."""
+    rng = np.random.default_rng(40 + d)
+    lengths = rng.integers(0, 901, 40).tolist()
+    lengths[3] = 0
+    lengths[17] = 900
+    inp = workloads.broadcast(50 + d, 100, lengths, 4, 2, d)
+    _say(f"broadcast split chunks d={d}")
+    _compare_full(_run_bcast(jfa, inp), _oracle_bcast(inp))
+
+
 @pytest.mark.parametrize("s", [0.9, 0.5, 0.1])
 def test_broadcast_q_config(jfa, s):
     """Broadcast-Q config (Nq = 256, 512 items, 4 heads, d = 128) at full size, whole
