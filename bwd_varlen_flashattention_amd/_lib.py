@@ -10,7 +10,9 @@ import ctypes
 import os
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libjfa.so")
+# JFA_LIBRARY selects another in-tree build of the same sources (the race-hunting
+# libjfa_debug_sync.so); by default the library is libjfa.so next to this file.
+LIB_PATH = os.environ.get("JFA_LIBRARY") or os.path.join(_PKG, "libjfa.so")
 
 JFA_OK = 0
 JFA_ERR_INVALID_ARGUMENT = 1

@@ -17,6 +17,10 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libjfa.so")
+# Race-hunting variant: the same sources with JFA_DEBUG_SYNC (extra workgroup
+# barriers before every LDS stage refill and epilogue); selected at run time with
+# the JFA_LIBRARY environment variable.
+DEBUG_SYNC_LIB = os.path.join(PKG, "libjfa_debug_sync.so")
 SOURCES = ["api.cpp", "sched.hip", "fwd.hip", "fwd_ilp.hip", "bwd.hip", "decode.hip", "check.hip"]
 ARCH = "gfx950"
 # Per-source code-generation options.  The backward's key-stationary kernel runs
@@ -47,30 +51,35 @@ def common_flags() -> list[str]:
     ]
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *common_flags(), *EXTRA_FLAGS.get(src, []), "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str = BUILD, defines: tuple = ()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [_hipcc(), *common_flags(), *EXTRA_FLAGS.get(src, []), *[f"-D{d}" for d in defines],
+           "-x", "hip", "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, debug_sync: bool = False) -> str:
+    lib = DEBUG_SYNC_LIB if debug_sync else LIB
+    build_dir = os.path.join(BUILD, "debug_sync") if debug_sync else BUILD
+    defines = ("JFA_DEBUG_SYNC",) if debug_sync else ()
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(len(SOURCES), os.cpu_count() or 4)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, build_dir, defines), SOURCES))
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":
     build(verbose=True)
+    build(verbose=True, debug_sync=True)
     sys.exit(0)

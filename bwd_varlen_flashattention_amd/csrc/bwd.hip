@@ -481,6 +481,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
           grads(qb, sacc, pacc);
         }
       }
+      debug_barrier();
       if (s + 1 < n_steps) store_lds(buf ^ 1);
       __syncthreads();
     };
@@ -528,6 +529,7 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
     // write 32 rows in 8-byte pieces per instruction; the wave's 32 x DC block is
     // transposed through LDS instead (free after the last step's barrier) and
     // written back 16 bytes per lane, DC / 8 lanes covering one row.
+    debug_barrier();
     {
       constexpr int EP = DC + 8;                 // row pitch of the epilogue blocks
       static_assert(2 * 32 * EP <= 2 * BM * QP && 2 * 32 * EP <= 2 * DC * QTP, "epilogue blocks fit");
@@ -924,6 +926,7 @@ __global__ __launch_bounds__((DqTile<D, NARROW>::NT), (DqTile<D, NARROW>::WG_PER
         }
         // two stages: the next tile goes into the other stage, whose readers
         // finished before the previous barrier; one stage: refilled next tile
+        debug_barrier();
         if (NSTAGE == 2 && s + 1 < n_tiles) store_lds(stg ^ 1);
         __syncthreads();
       };
@@ -947,6 +950,7 @@ __global__ __launch_bounds__((DqTile<D, NARROW>::NT), (DqTile<D, NARROW>::WG_PER
           *(f32x4*)(dst + 32 * db + 8 * r4 + 4 * hh) =
               f32x4{dqt[db][4 * r4], dqt[db][4 * r4 + 1], dqt[db][4 * r4 + 2], dqt[db][4 * r4 + 3]};
     }
+    debug_barrier();
     if (!BCAST) {
       // A lane holds 4 consecutive columns of its row per register quad; the
       // wave's 32 x D block goes through LDS (4 waves: the stages, free after the

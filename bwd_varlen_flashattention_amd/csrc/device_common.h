@@ -157,6 +157,17 @@ __device__ __forceinline__ int cdiv(int a, int b) { return (a + b - 1) / b; }
 // inside the loop.  (gfx9 encoding: vmcnt 0, expcnt 7, lgkmcnt 15.)
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Race-hunting build: with JFA_DEBUG_SYNC defined every kernel adds a workgroup
+// barrier before it refills an LDS stage and before it reuses the stages for its
+// epilogue.  Only called where the whole workgroup arrives (outside per-wave
+// branches).  Outputs must match the normal build bit for bit; a difference
+// points at a missing barrier in the normal one.
+__device__ __forceinline__ void debug_barrier() {
+#ifdef JFA_DEBUG_SYNC
+  __syncthreads();
+#endif
+}
+
 // Work-queue hand-out for persistent workgroups.  The queue starts and sizes
 // are copied into LDS once (load_queues, by all threads, followed by a barrier);
 // next_work_item is then called by one thread.  `q` starts at the block's home

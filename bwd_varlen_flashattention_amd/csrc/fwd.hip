@@ -376,6 +376,7 @@ __global__ __launch_bounds__((FwdTile<D, FP8, NARROW>::NT), (FwdTile<D, FP8, NAR
       }
       }   // wave_rows
 
+      debug_barrier();
       if (step + 1 < n_tiles) store_lds(buf ^ 1, f16_tag);
       __syncthreads();
     };
@@ -429,6 +430,7 @@ __global__ __launch_bounds__((FwdTile<D, FP8, NARROW>::NT), (FwdTile<D, FP8, NAR
     constexpr int EP = T::EP, NW = T::NW;
     constexpr bool ALL_VT = T::EP_ALL_VT, OWN = T::EP_OWN > 1;
     constexpr bool VIA_LDS = ALL_VT || T::EP_SPLIT || OWN;
+    debug_barrier();
     if constexpr (VIA_LDS) {
       __bf16* blk = OWN ? &ep_lds[0] + w * 32 * EP
                   : (ALL_VT || w < NW / 2) ? &vt_lds[0][0] + (ALL_VT ? w : w % (NW / 2)) * 32 * EP
