@@ -85,6 +85,15 @@ class JaggedCase:
         self.pairs = pairs_of(None if self.bcast else x.cu_q, x.cu_k, self.causal, x.q.shape[0] if self.bcast else None)
         self.fwd_flops = 4.0 * self.d * self.hq * self.pairs
         self.bwd_flops = 10.0 * self.d * self.hq * self.pairs
+        # Algorithmic HBM bytes (each tensor read or written once): forward reads Q, K, V
+        # and writes O, LSE; backward reads Q, K, V, O, dO, LSE, delta and writes dQ, dK, dV.
+        # Broadcast-Q: Q and dQ are [Nq, Hq, d], O, dO, LSE and delta per item.
+        hkv, tk = x.k.shape[1], x.k.shape[0]
+        nq = x.q.shape[0]
+        rows_o = (len(x.cu_k) - 1) * nq if self.bcast else nq     # rows of O / dO / LSE
+        q_el, o_el, k_el = nq * self.hq * self.d, rows_o * self.hq * self.d, tk * hkv * self.d
+        self.fwd_bytes = 2.0 * (q_el + 2 * k_el + o_el) + 4.0 * rows_o * self.hq
+        self.bwd_bytes = 2.0 * (2 * q_el + 4 * k_el + 2 * o_el) + 8.0 * rows_o * self.hq
         # Algorithmic flops per launch of each main kernel (per visible query-key pair, times Hq):
         #   fwd       4d  (S = Q K^T, O = P V)
         #   bwd_dkdv  8d  (S recomputed, dP, dV, dK: the backward's contractions except dQ)
@@ -664,6 +673,34 @@ def sweep(torch, jfa, workloads, args, log):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / n
 
+    scrub = None
+
+    def per_call(fn, n=20, w=5, cold=False):
+        """Each call timed on its own (HIP events on the launch stream): (median, min) ms.
+        cold: a 512 MB buffer is written before every call (outside the events), so the
+        call finds none of its inputs in the 256 MB MALL."""
+        nonlocal scrub
+        if cold and scrub is None:
+            scrub = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        for _ in range(w):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        for e0, e1 in ev:
+            if cold:
+                scrub.fill_(1)
+            e0.record()
+            fn()
+            e1.record()
+        torch.cuda.synchronize()
+        t = sorted(e0.elapsed_time(e1) for e0, e1 in ev)
+        return t[len(t) // 2], t[0]
+
+    def roof(flops, nbytes, ms):
+        """Roofline time of the work (MFMA or HBM bound) and the fraction of it reached."""
+        t = max(flops / (MFMA_BF16_PEAK_TFLOPS * 1e9), nbytes / (HBM_PEAK_GBS * 1e6))
+        return {"roofline_ms": round(t, 4), "bound": "hbm" if nbytes / HBM_PEAK_GBS * 1e3 > flops / MFMA_BF16_PEAK_TFLOPS
+                else "mfma", "frac_of_roofline": round(t / ms, 3)}
+
     cases = [("gem_s0.1", lambda: workloads.gem(0, 0.1)), ("gem_s0.5", lambda: workloads.gem(0, 0.5)),
              ("gem_s0.9", lambda: workloads.gem(0, 0.9)),
              ("bcast_s0.1", lambda: workloads.broadcast_q(0, 0.1)), ("bcast_s0.5", lambda: workloads.broadcast_q(0, 0.5)),
@@ -676,14 +713,31 @@ def sweep(torch, jfa, workloads, args, log):
         inp = make()
         jc = JaggedCase(torch, jfa, bcast=inp) if name.startswith("bcast") else JaggedCase(torch, jfa, inp)
         del inp
-        f_ms = timeit(lambda: jfa.jfa_fwd(jc.q, jc.k, jc.v, jc.cq, jc.ck, jc.mq, jc.mk, jc.causal, broadcast_q=jc.bcast,
-                                          out=jc.o, lse=jc.lse, workspace=jc.ws_f))
-        b_ms = timeit(lambda: jfa.jfa_bwd(jc.q, jc.k, jc.v, jc.o, jc.lse, jc.do, jc.cq, jc.ck, jc.mq, jc.mk, jc.causal,
-                                          broadcast_q=jc.bcast, dq=jc.dq, dk=jc.dk, dv=jc.dv, workspace=jc.ws_b))
+        fwd_call = lambda: jfa.jfa_fwd(jc.q, jc.k, jc.v, jc.cq, jc.ck, jc.mq, jc.mk, jc.causal, broadcast_q=jc.bcast,
+                                       out=jc.o, lse=jc.lse, workspace=jc.ws_f)
+        bwd_call = lambda: jfa.jfa_bwd(jc.q, jc.k, jc.v, jc.o, jc.lse, jc.do, jc.cq, jc.ck, jc.mq, jc.mk, jc.causal,
+                                       broadcast_q=jc.bcast, dq=jc.dq, dk=jc.dk, dv=jc.dv, workspace=jc.ws_b)
+        # back to back (mean) first, which also warms the GPU up after the inputs were
+        # written; then each call timed on its own: median (the reported time) and
+        # min; the working sets near or within the MALL also cold
+        f_b2b, b_b2b = timeit(fwd_call, w=5), timeit(bwd_call, w=5)
+        f_ms, fmin = per_call(fwd_call)
+        b_ms, bmin = per_call(bwd_call)
         line = {"workload": name, "fwd_ms": round(f_ms, 4), "bwd_ms": round(b_ms, 4),
                 "fwd_tflops": round(jc.fwd_flops / f_ms / 1e9, 1), "bwd_tflops": round(jc.bwd_flops / b_ms / 1e9, 1),
                 "fwd_pct_peak": round(100 * jc.fwd_flops / f_ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2),
-                "bwd_pct_peak": round(100 * jc.bwd_flops / b_ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2)}
+                "bwd_pct_peak": round(100 * jc.bwd_flops / b_ms / 1e9 / MFMA_BF16_PEAK_TFLOPS, 2),
+                "fwd_ms_min": round(fmin, 4), "bwd_ms_min": round(bmin, 4),
+                "fwd_ms_back_to_back": round(f_b2b, 4), "bwd_ms_back_to_back": round(b_b2b, 4),
+                "fwd_gb": round(jc.fwd_bytes / 1e9, 3), "bwd_gb": round(jc.bwd_bytes / 1e9, 3),
+                "fwd_roofline": roof(jc.fwd_flops, jc.fwd_bytes, f_ms),
+                "bwd_roofline": roof(jc.bwd_flops, jc.bwd_bytes, b_ms)}
+        if jc.fwd_bytes < 0.4e9:   # GEM and broadcast-Q at sparsity 0.9: near or within the 256 MB MALL
+            fc, _ = per_call(fwd_call, cold=True)
+            bc, _ = per_call(bwd_call, cold=True)
+            line.update({"fwd_ms_cold": round(fc, 4), "bwd_ms_cold": round(bc, 4),
+                         "fwd_roofline_cold": roof(jc.fwd_flops, jc.fwd_bytes, fc),
+                         "bwd_roofline_cold": roof(jc.bwd_flops, jc.bwd_bytes, bc)})
         print(json.dumps(line), flush=True)
         del jc
         torch.cuda.empty_cache()
