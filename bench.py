@@ -602,13 +602,22 @@ def main():
             extras[mode] = {"value": round(dc.bytes / (ms1 * 1e-3) / 1e12, 3), "unit": "TB/s", "ms": round(ms1, 4)}
         del dc1
 
-    # plain device copy of known size: reference for FETCH_SIZE / WRITE_SIZE scaling
+    # plain device copy of known size: reference for FETCH_SIZE / WRITE_SIZE scaling,
+    # and a measured HBM ceiling reported beside the published peak (never instead of it)
+    copy_tbs = None
     if args.copy_calibration_mib > 0:
         n = args.copy_calibration_mib * (1 << 20) // 4
         src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(5):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_tbs = round(2 * 4 * n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e12, 3)   # read + write bytes
         del src, dst
 
     stored = stored_traffic("dense_causal_d128")
@@ -647,6 +656,7 @@ def main():
         "bwd_pct_peak": _pct(jc.bwd_flops, b_ms),
         "decode": {"value": round(dec_tbs, 3), "unit": "TB/s", "pct_hbm_peak": round(100 * dec_tbs * 1e3 / HBM_PEAK_GBS, 2),
                    "ms": round(dec_ms, 4)},
+        "measured_hbm_copy_tbs": copy_tbs,
         "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
         "extra_steps": args.extra_steps,
         **extras,
