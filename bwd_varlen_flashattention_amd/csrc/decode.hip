@@ -371,12 +371,16 @@ __global__ __launch_bounds__(256, (DecOcc<D, NCG>::WG_PER_CU)) void decode_kerne
       if (a.splits == 1) {
         a.o[row * D + d] = (__bf16)(O * inv);
         if (d == 0) a.lse[row] = lse;
-      } else {
-        // device-scope stores: written through to memory, so that another XCD's
-        // device-scope loads see them without an L2 write-back of this XCD
+      } else if (a.counters) {
+        // single launch: device-scope stores, written through to memory, so that
+        // another XCD's device-scope loads see them without an L2 write-back here
         const int64_t pi = (int64_t)s * a.batch * a.q_len * a.hq + row;
         __hip_atomic_store(a.o_part + pi * D + d, O * inv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (d == 0) __hip_atomic_store(a.lse_part + pi, lse, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {   // merged by decode_combine_kernel after this launch
+        const int64_t pi = (int64_t)s * a.batch * a.q_len * a.hq + row;
+        a.o_part[pi * D + d] = O * inv;
+        if (d == 0) a.lse_part[pi] = lse;
       }
     }
     if (cg + 1 < NCG) __syncthreads();   // the merge buffers are rewritten by the next group
