@@ -166,6 +166,7 @@ WORKLOAD_KERNELS = {
 }
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_bench_step.txt")
 COUNTER_PROFILE = os.path.join(ROOT, "profiles", "mfma_lds_counters_bench_step.md")
+STALL_PROFILE = os.path.join(ROOT, "profiles", "wave_state_counters_bench_step.md")
 BENCH_CMD = "python3 $REPO/bench.py --steps 2 --warmup 1 --cpu-sample 0 --single-launch-steps 0"
 
 
@@ -365,6 +366,71 @@ def counter_summary(db: str, out: str):
     print("\n".join(lines))
 
 
+STALL_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU", "SQ_ACTIVE_INST_LDS",
+                  "SQ_ACTIVE_INST_VMEM", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_WAIT_INST_LDS", "GRBM_GUI_ACTIVE")
+
+
+def stall_summary(db: str, out: str):
+    """Summarise one rocprofv3 --pmc run of the wave-state counters (STALL_COUNTERS) of this
+    benchmark: per main kernel, where its waves spend their resident cycles."""
+    val, name, dur = _per_dispatch(db, set(STALL_COUNTERS))
+    groups = _workload_dispatches(name)
+    lines = [
+        "# Wave-state counters: where the bench step kernels' waves spend their cycles",
+        "",
+        "Command (repository root on the MI355X box = $REPO):",
+        "",
+        "```",
+        "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc " + " ".join(STALL_COUNTERS)
+        + f" --kernel-trace -d $REPO/gpurun_out/pmc_stall -o stall -- {BENCH_CMD}",
+        "python3 bench.py --stall-summary gpurun_out/pmc_stall/stall_results.db",
+        "```",
+        "",
+        "The SQ counters are wave-cycles summed over all resident waves (quad-cycle units), so every column but the "
+        "first two is a fraction of SQ_WAVE_CYCLES, the cycles the waves were resident:",
+        "",
+        "* `waves/SIMD` = 4 x SQ_WAVE_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs): mean resident waves per SIMD;",
+        "* `issuing` = SQ_ACTIVE_INST_ANY (cycles a wave was executing some instruction); `valu`, `lds`, `vmem` = "
+        "SQ_ACTIVE_INST_VALU (MFMA included), _LDS, _VMEM;",
+        "* `wait dep` = SQ_WAIT_ANY (waiting at s_waitcnt or a barrier for memory, LDS or other waves); "
+        "`wait issue` = SQ_WAIT_INST_ANY (ready but not issued: its unit busy, or a dependency on an unfinished "
+        "instruction such as an MFMA in flight); `wait LDS issue` = SQ_WAIT_INST_LDS.",
+        "",
+        "The categories overlap (an issuing wave can also be waiting on another counter) and the hardware "
+        "documents them as nondeterministic: read them as proportions, not as a partition.",
+        "",
+        "| workload | kernel | ms | waves/SIMD | issuing | valu | lds | vmem | wait dep | wait issue | wait LDS issue |",
+        "|---|---|---|---|---|---|---|---|---|---|---|",
+    ]
+    rec = {}
+    for (wl, slot), ds in sorted(groups.items()):
+        m = {c: sum(val[d][c] for d in ds) / len(ds) for c in STALL_COUNTERS}
+        ms = sum(dur[d] for d in ds) / len(ds) * 1e-6
+        wc = max(1.0, m["SQ_WAVE_CYCLES"])
+        cyc = m["GRBM_GUI_ACTIVE"] / XCDS
+        row = {"ms": ms, "waves_per_simd": 4.0 * wc / max(1.0, cyc * CUS * SIMDS_PER_CU),
+               "issuing": m["SQ_ACTIVE_INST_ANY"] / wc, "valu": m["SQ_ACTIVE_INST_VALU"] / wc,
+               "lds": m["SQ_ACTIVE_INST_LDS"] / wc, "vmem": m["SQ_ACTIVE_INST_VMEM"] / wc,
+               "wait_dep": m["SQ_WAIT_ANY"] / wc, "wait_issue": m["SQ_WAIT_INST_ANY"] / wc,
+               "wait_lds_issue": m["SQ_WAIT_INST_LDS"] / wc, "counters": m}
+        rec.setdefault(wl, {})[slot] = row
+        lines.append(f"| {wl} | {slot} | {ms:.3f} | {row['waves_per_simd']:.2f} | " + " | ".join(
+            f"{row[k]:.3f}" for k in ("issuing", "valu", "lds", "vmem", "wait_dep", "wait_issue", "wait_lds_issue"))
+            + " |")
+    lines += ["", "Raw counters per launch:", "", "| workload | kernel | " + " | ".join(STALL_COUNTERS) + " |",
+              "|---|---|" + "---|" * len(STALL_COUNTERS)]
+    for wl in sorted(rec):
+        for slot, row in sorted(rec[wl].items()):
+            lines.append(f"| {wl} | {slot} | " + " | ".join(f"{row['counters'][c]:.4g}" for c in STALL_COUNTERS) + " |")
+    lines += ["", "Machine-readable line (the digest covers the kernel sources and build options):", ""]
+    lines.append(json.dumps({"source_digest": source_digest(),
+                             "per_launch": {wl: {s: {k: v for k, v in r.items() if k != "counters"}
+                                                 for s, r in d.items()} for wl, d in rec.items()}}))
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def trace_summary(db: str, timed: str, out: str):
     """Summarise a rocprofv3 --kernel-trace --stats run of this benchmark: per kernel the
     calls and durations, plus the mean of the timed launches of the bench step's main
@@ -500,6 +566,8 @@ def main():
                     help="summarise two rocprofv3 --pmc runs of this benchmark into the traffic profile and exit")
     ap.add_argument("--counter-summary", metavar="DB",
                     help="summarise a rocprofv3 --pmc run of the MFMA/LDS counters into the counter profile and exit")
+    ap.add_argument("--stall-summary", metavar="DB",
+                    help="summarise a rocprofv3 --pmc run of the wave-state counters into the stall profile and exit")
     ap.add_argument("--trace-summary", nargs=2, metavar=("DB", "BENCH_JSON"),
                     help="summarise a rocprofv3 --kernel-trace run of this benchmark and exit")
     args = ap.parse_args()
@@ -507,6 +575,8 @@ def main():
         return pmc_summary(*args.pmc_summary, args.copy_calibration_mib, TRAFFIC_PROFILE)
     if args.counter_summary:
         return counter_summary(args.counter_summary, COUNTER_PROFILE)
+    if args.stall_summary:
+        return stall_summary(args.stall_summary, STALL_PROFILE)
     if args.trace_summary:
         return trace_summary(*args.trace_summary,
                              os.path.join(ROOT, "profiles", "kernel_trace_bench_step_dense_causal_d128.md"))
