@@ -226,6 +226,13 @@ def _workload_dispatches(name):
     return out
 
 
+def _reference_dispatches(name):
+    """{("library_gemm_bf16_8192", "gemm"): [dispatch ids]}: the library GEMM of --gemm-probe,
+    summarised beside the attention kernels as a reference for clock and MFMA busy."""
+    ds = [d for d, k in name.items() if k.startswith("Cijk_")]
+    return {("library_gemm_bf16_8192", "gemm"): ds} if ds else {}
+
+
 def pmc_summary(fetch_db: str, write_db: str, copy_mib: int, out: str):
     """Turn two rocprofv3 --pmc databases of this benchmark (FETCH_SIZE, then WRITE_SIZE)
     into per-launch byte counts, scaled by what the same counters read for the plain
@@ -290,7 +297,7 @@ def counter_summary(db: str, out: str):
     kernel of each workload, the counters per launch and what follows from them."""
     import workloads
     val, name, dur = _per_dispatch(db, set(COUNTERS))
-    groups = _workload_dispatches(name)
+    groups = {**_workload_dispatches(name), **_reference_dispatches(name)}
     # algorithmic flops per launch, from the same seeded workloads the benchmark runs
     alg = {}
     for wl, make in (("dense_causal_d128", lambda: workloads.dense_causal(0, head_dim=128)),
@@ -301,6 +308,7 @@ def counter_summary(db: str, out: str):
         u = x.q.shape[2] * x.q.shape[1] * pairs
         alg[wl] = {"fwd": 4.0 * u, "bwd_dkdv": 8.0 * u, "bwd_dq": 2.0 * u}
         del x
+    alg["library_gemm_bf16_8192"] = {"gemm": 2.0 * 8192 ** 3}
     peak = MFMA_BF16_PEAK_TFLOPS * 1e12
     lines = [
         "# MFMA, LDS and transcendental counters: bench step kernels",
@@ -326,6 +334,10 @@ def counter_summary(db: str, out: str):
         "and head: the dQ kernel recomputes S and dP, 6d executed);",
         "* `LDS/MFMA` = SQ_INSTS_LDS / SQ_INSTS_MFMA; `exp/MFMA` = SQ_INSTS_VALU_TRANS_F32 / SQ_INSTS_MFMA;",
         "* `bank confl/LDS` = SQ_LDS_BANK_CONFLICT / SQ_INSTS_LDS (conflict cycles per LDS instruction).",
+        "",
+        "`library_gemm_bf16_8192` is the reference GEMM the benchmark times after its steps (torch.matmul, "
+        "bf16, 8192 x 8192 x 8192, contiguous operands): the clock and MFMA busy a tuned library kernel "
+        "sustains on this GPU.",
         "",
         "| workload | kernel | ms | MFMA TFLOP/s | MFMA util | clock | MFMA busy | exec/alg | SQ_INSTS_MFMA | LDS/MFMA | "
         "exp/MFMA | bank confl/LDS |",
@@ -374,7 +386,7 @@ def stall_summary(db: str, out: str):
     """Summarise one rocprofv3 --pmc run of the wave-state counters (STALL_COUNTERS) of this
     benchmark: per main kernel, where its waves spend their resident cycles."""
     val, name, dur = _per_dispatch(db, set(STALL_COUNTERS))
-    groups = _workload_dispatches(name)
+    groups = {**_workload_dispatches(name), **_reference_dispatches(name)}
     lines = [
         "# Wave-state counters: where the bench step kernels' waves spend their cycles",
         "",
@@ -562,6 +574,8 @@ def main():
     ap.add_argument("--sweep", action="store_true", help="one JSON line per workload (GEM s, broadcast-Q, dense, decode)")
     ap.add_argument("--copy-calibration-mib", type=int, default=1024,
                     help="run one device copy of this size after timing (reference for HBM byte counters)")
+    ap.add_argument("--gemm-probe", type=int, default=1,
+                    help="time a library bf16 GEMM (8192^3) after the steps: the sustained MFMA rate (0 = skip)")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DB", "WRITE_DB"),
                     help="summarise two rocprofv3 --pmc runs of this benchmark into the traffic profile and exit")
     ap.add_argument("--counter-summary", metavar="DB",
@@ -690,6 +704,25 @@ def main():
         copy_tbs = round(2 * 4 * n * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e12, 3)   # read + write bytes
         del src, dst
 
+    # a library bf16 GEMM (8192^3, contiguous operands): the dense MFMA rate this GPU
+    # sustains under its power limit, reported beside the published peak (never instead of it)
+    gemm_tflops = None
+    if args.gemm_probe:
+        ga = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+        gb = torch.randn(8192, 8192, device="cuda").to(torch.bfloat16)
+        gc = torch.empty(8192, 8192, device="cuda", dtype=torch.bfloat16)
+        for _ in range(5):
+            torch.matmul(ga, gb, out=gc)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            torch.matmul(ga, gb, out=gc)
+        e1.record()
+        torch.cuda.synchronize()
+        gemm_tflops = round(2 * 8192 ** 3 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e12, 1)
+        del ga, gb, gc
+
     stored = stored_traffic("dense_causal_d128")
     traffic = round(stored[dominant]) if stored and dominant in stored else None
 
@@ -727,6 +760,7 @@ def main():
         "decode": {"value": round(dec_tbs, 3), "unit": "TB/s", "pct_hbm_peak": round(100 * dec_tbs * 1e3 / HBM_PEAK_GBS, 2),
                    "ms": round(dec_ms, 4)},
         "measured_hbm_copy_tbs": copy_tbs,
+        "measured_bf16_gemm_tflops": gemm_tflops,
         "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
         "extra_steps": args.extra_steps,
         **extras,
