@@ -475,7 +475,8 @@ def trace_summary(db: str, timed: str, out: str):
         "|---|---|---|---|---|",
     ]
     for name, calls, tot, avg, pct in rows:
-        lines.append(f"| `{name}` | {calls} | {tot:.1f} | {avg:.1f} | {pct:.2f} |")
+        short = name if len(name) <= 120 else name[:117] + "..."   # library kernels' template names run to pages
+        lines.append(f"| `{short}` | {calls} | {tot:.1f} | {avg:.1f} | {pct:.2f} |")
     lines += ["", f"Timed launches of the step's main kernels (the first {steps} launches after the "
               f"warmup of each; bench.py's own HIP-event means from the same run beside them):", "",
               "| workload | kernel | trace mean (ms) | bench.py events (ms) |", "|---|---|---|---|"]
