@@ -96,6 +96,17 @@ def test_ragged(jfa, d, causal, hq, hkv):
     _compare_full(_run_self(jfa, inp), _oracle_self(inp))
 
 
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("hq,hkv", [(16, 2), (16, 1)])
+def test_wide_gqa_groups(jfa, d, causal, hq, hkv):
+    """GQA ratios 8 and 16: every dK/dV item sums its gradients over that many query heads,
+    and the forward / dQ items of one KV head run together."""
+    inp = workloads.jagged(300 + d + hq // hkv, [1, 77, 300, 129, 0, 513], None, hq, hkv, d, causal)
+    _say(f"wide GQA d={d} causal={causal} hq={hq} hkv={hkv}")
+    _compare_full(_run_self(jfa, inp), _oracle_self(inp))
+
+
 # Lengths around the 256-row query tiles of the 8-wave forward / dQ workgroups (d = 64, 128):
 # every count of waves past the sequence end (0..7) occurs in some tile.
 WIDE_TILE = [255, 256, 257, 288, 289, 320, 352, 384, 416, 448, 480, 511, 512, 513, 40]
