@@ -157,6 +157,16 @@ def test_explicit_scale(jfa):
     _compare_full(_run_self(jfa, inp, 0.3), _oracle_self(inp, 0.3))
 
 
+@pytest.mark.parametrize("scale", [4.0, 1e-3])
+@pytest.mark.parametrize("causal", [False, True])
+def test_extreme_scales(jfa, scale, causal):
+    """Scale 4 at d = 128: scores spread over hundreds of log2 units, so rows are nearly one-hot
+    and the forward's running max moves many times; scale 1e-3: nearly flat rows."""
+    inp = workloads.jagged(60, [700, 33, 257, 1], None, 4, 2, 128, causal)
+    _say(f"extreme scale {scale} causal={causal}")
+    _compare_full(_run_self(jfa, inp, scale), _oracle_self(inp, scale))
+
+
 def test_outputs_overwritten(jfa):
     """Outputs pre-filled with NaN must be fully overwritten (catches unwritten rows)."""
     inp = workloads.jagged(9, [3, 130, 64, 0, 1], None, 4, 2, 64, True)

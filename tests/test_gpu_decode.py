@@ -60,6 +60,19 @@ def test_decode_small(jfa, page_size, hq, hkv):
         check_lse(lse, rl, f"LSE splits={splits}")
 
 
+@pytest.mark.parametrize("scale", [4.0, 1e-3])
+def test_decode_extreme_scales(jfa, scale):
+    """Nearly one-hot (scale 4) and nearly flat (1e-3) rows, across split counts."""
+    inp = workloads.decode(61, [1, 900, 64, 2500, 17], 8, 2, 128, 16)
+    _say(f"decode extreme scale {scale}")
+    d = _Dev(inp)
+    ro, rl = _ref(inp, scale)
+    for splits in (1, 3, 0):
+        o, lse = _run(jfa, d, splits, scale)
+        check_o(o, ro, f"O splits={splits}")
+        check_lse(lse, rl, f"LSE splits={splits}")
+
+
 @pytest.mark.parametrize("dim", [64, 96, 192, 256])
 def test_decode_head_dims(jfa, dim):
     inp = workloads.decode(31, [5, 200, 129], 8, 2, dim, 16)
