@@ -27,8 +27,10 @@
  *     JFA_ERR_INVALID_ARGUMENT.
  *   - The caller owns all memory (inputs, outputs, workspace) and the optional
  *     timing events.  The library allocates no device memory and keeps no state
- *     beyond a per-device cache of the compute-unit count.  Calls with distinct workspaces may run
- *     concurrently on different streams.
+ *     beyond a per-device cache of the compute-unit count; the one exception is
+ *     jfa_decode_paged_noalloc, whose static device array (and its cached
+ *     per-device address) is described with it.  Calls with distinct workspaces
+ *     may run concurrently on different streams.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and
  *     runs asynchronously: no call synchronises with the host.
  *   - Outputs are fully overwritten, never accumulated into.
