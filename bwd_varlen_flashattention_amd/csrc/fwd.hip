@@ -251,25 +251,44 @@ __global__ __launch_bounds__((FwdTile<D, FP8, NARROW>::NT), (FwdTile<D, FP8, NAR
         // 4 keys x 8 columns -> 8 rows of V^T holding 4 keys each
         const int col = 16 * (vkb[vi] >> 2) + 4 * vt_quarter_pos(vkb[vi] & 3);
         __bf16* dst = &vt_lds[buf][(8 * vdb[vi]) * VTP + col];
-        u32x4 r[4];   // 4 rows of 8 16-bit values
+        // Per column pair (2c, 2c + 1): rows 0-1 and 2-3 of column 2c (lo01, lo23) and of
+        // column 2c + 1 (hi01, hi23), two 16-bit values per register
+        uint32_t lo01[4], lo23[4], hi01[4], hi23[4];
+        if constexpr (!FP8 && F16) {
+          // bf16 -> fp16 with each packed conversion taking two rows of one column,
+          // so its result is already the transposed pair (no permutes)
+          auto lo = [](uint32_t x) { return __uint_as_float(x << 16); };
+          auto hi = [](uint32_t x) { return __uint_as_float(x & 0xffff0000u); };
+          auto pk = [](float a, float b) {   // a in the low half
+            return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, f16x2));
+          };
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          if constexpr (FP8) r[i] = widen_e4m3x8_f16(vr[vi][i]);
-          else if constexpr (F16) {
+          for (int c = 0; c < 4; ++c) {
+            const uint32_t x0 = vr[vi][0][c], x1 = vr[vi][1][c], x2 = vr[vi][2][c], x3 = vr[vi][3][c];
+            lo01[c] = pk(lo(x0), lo(x1));
+            lo23[c] = pk(lo(x2), lo(x3));
+            hi01[c] = pk(hi(x0), hi(x1));
+            hi23[c] = pk(hi(x2), hi(x3));
+          }
+        } else {
+          u32x4 r[4];   // 4 rows of 8 16-bit values
 #pragma unroll
-            for (int c = 0; c < 4; ++c) r[i][c] = bf16x2_to_f16x2(vr[vi][i][c]);
-          } else {
-            r[i] = vr[vi][i];
+          for (int i = 0; i < 4; ++i) {
+            if constexpr (FP8) r[i] = widen_e4m3x8_f16(vr[vi][i]);
+            else r[i] = vr[vi][i];
+          }
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            lo01[c] = __builtin_amdgcn_perm(r[1][c], r[0][c], 0x05040100u);
+            lo23[c] = __builtin_amdgcn_perm(r[3][c], r[2][c], 0x05040100u);
+            hi01[c] = __builtin_amdgcn_perm(r[1][c], r[0][c], 0x07060302u);
+            hi23[c] = __builtin_amdgcn_perm(r[3][c], r[2][c], 0x07060302u);
           }
         }
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const uint32_t lo01 = __builtin_amdgcn_perm(r[1][c], r[0][c], 0x05040100u);
-          const uint32_t lo23 = __builtin_amdgcn_perm(r[3][c], r[2][c], 0x05040100u);
-          const uint32_t hi01 = __builtin_amdgcn_perm(r[1][c], r[0][c], 0x07060302u);
-          const uint32_t hi23 = __builtin_amdgcn_perm(r[3][c], r[2][c], 0x07060302u);
-          *(uint2*)(dst + (2 * c) * VTP) = make_uint2(lo01, lo23);
-          *(uint2*)(dst + (2 * c + 1) * VTP) = make_uint2(hi01, hi23);
+          *(uint2*)(dst + (2 * c) * VTP) = make_uint2(lo01[c], lo23[c]);
+          *(uint2*)(dst + (2 * c + 1) * VTP) = make_uint2(hi01[c], hi23[c]);
         }
       }
     };
