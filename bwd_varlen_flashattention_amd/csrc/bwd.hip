@@ -482,7 +482,17 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         }
       }
       debug_barrier();
-      if (s + 1 < n_steps) store_lds(buf ^ 1);
+      // Self-attention: unconditional, so the staging shares the step's basic block
+      // and the scheduler can interleave it with the gradient MFMAs (dense causal
+      // and GEM s = 0.1 dK/dV -1.3 %); the last step writes stale registers into
+      // the stage nobody reads again before the barrier.  Broadcast-Q items are
+      // Nq / 64 steps long (4 at Nq = 256), where that wasted last staging costs
+      // more than the interleaving saves (+1 %), so they skip it.
+      if constexpr (BCAST) {
+        if (s + 1 < n_steps) store_lds(buf ^ 1);
+      } else {
+        store_lds(buf ^ 1);
+      }
       __syncthreads();
     };
 
