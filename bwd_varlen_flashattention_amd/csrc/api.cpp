@@ -451,17 +451,17 @@ jfa_status_t jfa_bwd(const jfa_attn_params_t* p, const void* q, const void* k, c
     // Broadcast-Q: delta = rowsum(dO * O) for every item.  Self-attention
     // computes delta inside the dQ kernel.
     if (p->broadcast_q) {
-    BwdPreArgs pa{};
-    pa.o = (const __bf16*)o;
-    pa.dout = (const __bf16*)dout;
-    pa.delta = delta;
-    pa.rows = p->broadcast_q ? (int64_t)p->batch * p->total_q : p->total_q;
-    pa.hq = p->num_heads_q;
-    pa.head_dim = p->head_dim;
-    pa.lse_cols = p->total_q;
-    pa.bcast = p->broadcast_q;
-    e = launch_bwd_pre(pa, stream);
-    if (e != hipSuccess) return JFA_ERR_HIP;
+      BwdPreArgs pa{};
+      pa.o = (const __bf16*)o;
+      pa.dout = (const __bf16*)dout;
+      pa.delta = delta;
+      pa.rows = (int64_t)p->batch * p->total_q;   // [B, Nq] rows of O and dO
+      pa.hq = p->num_heads_q;
+      pa.head_dim = p->head_dim;
+      pa.lse_cols = p->total_q;
+      pa.bcast = 1;
+      e = launch_bwd_pre(pa, stream);
+      if (e != hipSuccess) return JFA_ERR_HIP;
     }
 
     // dQ: query-stationary
