@@ -170,6 +170,14 @@ STALL_PROFILE = os.path.join(ROOT, "profiles", "wave_state_counters_bench_step.m
 BENCH_CMD = "python3 $REPO/bench.py --steps 2 --warmup 1 --cpu-sample 0 --single-launch-steps 0"
 
 
+def _run_of(db: str):
+    """(directory, -o name) of a rocprofv3 output database path such as <dir>/<name>_results.db,
+    for quoting the command that wrote it."""
+    d = os.path.dirname(db) or "."
+    name = os.path.basename(db)
+    return d, name[: -len("_results.db")] if name.endswith("_results.db") else name
+
+
 def source_digest() -> str:
     """Digest of the kernel sources and build options: stored counter data is only
     reported while it still describes the kernels that run."""
@@ -261,11 +269,11 @@ def pmc_summary(fetch_db: str, write_db: str, copy_mib: int, out: str):
         "Commands (repository root on the MI355X box = $REPO; one counter per run):",
         "",
         "```",
-        f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE -d $REPO/gpurun_out/pmc_fetch "
-        f"-o fetch -- {BENCH_CMD}",
-        f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE -d $REPO/gpurun_out/pmc_write "
-        f"-o write -- {BENCH_CMD}",
-        "python3 bench.py --pmc-summary gpurun_out/pmc_fetch/fetch_results.db gpurun_out/pmc_write/write_results.db",
+        f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc FETCH_SIZE -d $REPO/{_run_of(fetch_db)[0]} "
+        f"-o {_run_of(fetch_db)[1]} -- {BENCH_CMD}",
+        f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc WRITE_SIZE -d $REPO/{_run_of(write_db)[0]} "
+        f"-o {_run_of(write_db)[1]} -- {BENCH_CMD}",
+        f"python3 bench.py --pmc-summary {fetch_db} {write_db}",
         "```",
         "",
         f"Calibration: the benchmark's plain device copy of {copy_mib} MiB reads {fcal:.0f} KiB (FETCH_SIZE) and "
@@ -317,8 +325,8 @@ def counter_summary(db: str, out: str):
         "",
         "```",
         "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc " + " ".join(COUNTERS)
-        + f" --kernel-trace -d $REPO/gpurun_out/pmc_mfma -o mfma -- {BENCH_CMD}",
-        "python3 bench.py --counter-summary gpurun_out/pmc_mfma/mfma_results.db",
+        + f" --kernel-trace -d $REPO/{_run_of(db)[0]} -o {_run_of(db)[1]} -- {BENCH_CMD}",
+        f"python3 bench.py --counter-summary {db}",
         "```",
         "",
         "Per launch (mean over the run's launches of each kernel).  Derived columns:",
@@ -394,8 +402,8 @@ def stall_summary(db: str, out: str):
         "",
         "```",
         "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --pmc " + " ".join(STALL_COUNTERS)
-        + f" --kernel-trace -d $REPO/gpurun_out/pmc_stall -o stall -- {BENCH_CMD}",
-        "python3 bench.py --stall-summary gpurun_out/pmc_stall/stall_results.db",
+        + f" --kernel-trace -d $REPO/{_run_of(db)[0]} -o {_run_of(db)[1]} -- {BENCH_CMD}",
+        f"python3 bench.py --stall-summary {db}",
         "```",
         "",
         "The SQ counters are wave-cycles summed over all resident waves (quad-cycle units), so every column but the "
@@ -464,9 +472,9 @@ def trace_summary(db: str, timed: str, out: str):
         "",
         "```",
         "cd /tmp && export TMPDIR=/tmp && timeout -s KILL 300 rocprofv3 --kernel-trace --stats -d "
-        "$REPO/gpurun_out/prof_bench -o bench -- python3 $REPO/bench.py --steps 10 --warmup 3 --cpu-sample 0 "
-        "--single-launch-steps 0 > $REPO/gpurun_out/prof_bench.json",
-        "python3 bench.py --trace-summary gpurun_out/prof_bench/bench_results.db gpurun_out/prof_bench.json",
+        f"$REPO/{_run_of(db)[0]} -o {_run_of(db)[1]} -- python3 $REPO/bench.py --steps 10 --warmup 3 --cpu-sample 0 "
+        f"--single-launch-steps 0 > $REPO/{timed}",
+        f"python3 bench.py --trace-summary {db} {timed}",
         "```",
         "",
         "Per-kernel summary (top_kernels view of the rocpd database; all launches, warmup included):",
