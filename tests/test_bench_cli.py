@@ -85,3 +85,32 @@ def test_wave_state_fractions(tmp_path, monkeypatch):
     assert row["waves_per_simd"] == pytest.approx(2.0)
     assert row["issuing"] == pytest.approx(0.5) and row["wait_issue"] == pytest.approx(0.3)
     assert row["wait_dep"] == pytest.approx(0.2) and row["lds"] == pytest.approx(0.1)
+
+
+def test_mfma_summary_derived_columns(tmp_path, monkeypatch):
+    """The library GEMM row: executed flops from the MOPS counter, clock from GRBM_GUI_ACTIVE
+    over the 8 XCDs, MFMA busy over all 1024 SIMDs at that clock."""
+    import types
+    import numpy as np
+    import workloads
+    tiny = types.SimpleNamespace(cu_q=np.array([0, 4]), cu_k=np.array([0, 4]), causal=False,
+                                 q=np.zeros((4, 1, 8)))
+    for f in ("dense_causal", "gem", "broadcast_q"):
+        monkeypatch.setattr(workloads, f, lambda *a, **k: tiny)
+    db = str(tmp_path / "mfma_results.db")
+    ms, ghz, busy = 1.0, 1.7, 0.7
+    cyc = ghz * 1e9 * ms * 1e-3
+    flops = 2.0 * 8192 ** 3
+    counters = {c: 0.0 for c in bench.COUNTERS}
+    counters.update({"SQ_INSTS_VALU_MFMA_MOPS_BF16": flops / 512.0, "GRBM_GUI_ACTIVE": 8 * cyc,
+                     "SQ_VALU_MFMA_BUSY_CYCLES": busy * cyc * 1024, "SQ_INSTS_MFMA": flops / 32768.0,
+                     "SQ_INSTS_LDS": 0.5 * flops / 32768.0})
+    _counter_db(db, [(1, "Cijk_Ailk_Bljk_BBS_BH_test", int(ms * 1e6), counters)])
+    out = tmp_path / "mfma.md"
+    monkeypatch.setattr(bench, "source_digest", lambda: "digest-a")
+    bench.counter_summary(db, str(out))
+    row = json.loads(out.read_text().strip().splitlines()[-1])["per_launch"]["library_gemm_bf16_8192"]["gemm"]
+    assert row["mfma_tflops"] == pytest.approx(flops / (ms * 1e-3) / 1e12)
+    assert row["mfma_util"] == pytest.approx(row["mfma_tflops"] / bench.MFMA_BF16_PEAK_TFLOPS)
+    assert row["clock_ghz"] == pytest.approx(ghz) and row["mfma_busy"] == pytest.approx(busy)
+    assert row["exec_over_alg"] == pytest.approx(1.0) and row["lds_per_mfma"] == pytest.approx(0.5)
