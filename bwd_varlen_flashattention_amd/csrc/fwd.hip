@@ -17,8 +17,10 @@
 //     over 512 threads), so one wave's softmax VALU work overlaps the other's
 //     MFMAs; d = 192 and 256 run one 4-wave workgroup per CU, whose Q fragment
 //     and accumulator fill a SIMD's registers;
-//   * K/V tiles of 64 keys are double-buffered in LDS: the global loads of tile
-//     j+1 are in flight while tile j is consumed;
+//   * K/V tiles of 64 keys are staged through LDS while earlier tiles are
+//     consumed: at d >= 128 in four stages, loaded two tiles ahead, with one
+//     workgroup barrier per two tiles; otherwise double-buffered, one barrier
+//     per tile;
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 so each lane owns one query column:
 //     the row max/sum reductions are in-lane plus one permlane32 swap;
 //   * the S^T accumulator, rounded to fp16, is directly the B operand of
