@@ -77,25 +77,27 @@ struct FwdTile {
   static constexpr int KS8 = D / 64;        // k-steps of K Q^T (e4m3)
   static constexpr int DB = D / 32;         // 32-wide output column blocks
   static constexpr int K_LDS_BYTES = BN * KP * EB;
-  // epilogue: each wave's 32 x D output block goes through LDS.  The K and V^T
-  // stages hold them except for e4m3 with 8 waves (a smaller K stage); that case
-  // has LDS of its own (one workgroup per CU).
-  static constexpr int NW = NT / 64;
-  static constexpr int EP = D + 8;
-  static constexpr bool EP_ALL_VT = NW * 32 * EP <= 2 * D * VTP;
-  static constexpr bool EP_SPLIT = (NW / 2) * 32 * EP <= 2 * D * VTP && (NW / 2) * 32 * EP <= K_LDS_BYTES;
-  static constexpr int EP_OWN = (!EP_ALL_VT && !EP_SPLIT && NT == 512) ? NW * 32 * EP : 1;
   // 4-wave workgroups at d <= 128: two per CU; larger heads need the whole
   // register file of one wave per SIMD (Q fragment + output accumulator)
   static constexpr int WG_PER_CU = (NT == 256 && D <= 128) ? 2 : 1;
   static_assert(BN * CH % NT == 0, "tile load split");
   static_assert(!FP8 || D % 64 == 0, "e4m3 k-steps are 64 deep");
-  // K/V stages: four for d >= 128 where they fit, with tiles loaded two steps
-  // ahead and a workgroup barrier after every second tile (dense causal forward
-  // -1.8 % at d = 128, -6 % at d = 256); two, with a barrier after every tile,
-  // otherwise (at d = 64 a tile's work is short and four stages were 2 % slower)
-  static constexpr int NST =
-      D >= 128 && WG_PER_CU * (4 * (K_LDS_BYTES + D * VTP * 2) + 2 * EP_OWN) <= 160 * 1024 ? 4 : 2;
+  // epilogue: each wave's 32 x D output block goes through LDS
+  static constexpr int NW = NT / 64;
+  static constexpr int EP = D + 8;
+  // K/V stages: four for d >= 128 where they and the epilogue blocks (then all
+  // in the V^T stages) fit, with tiles loaded two steps ahead and a workgroup
+  // barrier after every second tile (dense causal forward -2.6 % at d = 128, -6 %
+  // at d = 256); two, with a barrier after every tile, otherwise (at d = 64 a
+  // tile's work is short and four stages were 2 % slower)
+  static constexpr int NST = (D >= 128 && WG_PER_CU * 4 * (K_LDS_BYTES + D * VTP * 2) <= 159 * 1024 &&
+                              NW * 32 * EP <= 4 * D * VTP) ? 4 : 2;   // 1 KB left for the small shared state
+  // With two stages the blocks go in the V^T stages, or half of them in the K
+  // stages, except for e4m3 with 8 waves (a smaller K stage), which then has LDS
+  // of its own (one workgroup per CU).
+  static constexpr bool EP_ALL_VT = NW * 32 * EP <= NST * D * VTP;
+  static constexpr bool EP_SPLIT = (NW / 2) * 32 * EP <= 2 * D * VTP && (NW / 2) * 32 * EP <= K_LDS_BYTES;
+  static constexpr int EP_OWN = (!EP_ALL_VT && !EP_SPLIT && NT == 512) ? NW * 32 * EP : 1;
   static constexpr int AHEAD = NST / 2;     // steps between a tile's load and its use
   static_assert(WG_PER_CU * (NST * (K_LDS_BYTES + D * VTP * 2) + 2 * EP_OWN) <= 160 * 1024, "LDS budget");
 };
