@@ -11,6 +11,7 @@ import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -21,7 +22,7 @@ LIB = os.path.join(PKG, "libjfa.so")
 # barriers before every LDS stage refill and epilogue); selected at run time with
 # the JFA_LIBRARY environment variable.
 DEBUG_SYNC_LIB = os.path.join(PKG, "libjfa_debug_sync.so")
-SOURCES = ["api.cpp", "sched.hip", "fwd.hip", "fwd_ilp.hip", "bwd.hip", "decode.hip", "check.hip"]
+SOURCES = ["api.cpp", "sched.hip", "fwd.hip", "fwd_ilp.hip", "bwd.hip", "bwd_wide.hip", "decode.hip", "check.hip"]
 ARCH = "gfx950"
 # Per-source code-generation options.  The backward's key-stationary kernel runs
 # one wave per SIMD, so its LDS reads must be issued well ahead of the MFMAs that
@@ -29,8 +30,11 @@ ARCH = "gfx950"
 # The forward's kernels are split over two units built from the same source:
 # the latency-first scheduler for d <= 96 and the non-causal d = 128 kernels
 # (3-7% faster there), the iterative ILP scheduler for the causal d = 128 and
-# all d >= 192 kernels (3-13% faster there).
+# all d >= 192 kernels (3-13% faster there).  The backward's d >= 192 kernels
+# are a unit of their own whose MFMA builtins take the VGPR form (their dK/dV
+# accumulators are kept in AGPRs by hand-written MFMAs instead).
 EXTRA_FLAGS = {"bwd.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"],
+               "bwd_wide.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp", "-mllvm", "-amdgpu-mfma-vgpr-form"],
                "fwd.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
                "fwd_ilp.hip": ["-mllvm", "-amdgpu-sched-strategy=iterative-ilp"]}
 
@@ -59,6 +63,19 @@ def _compile(src: str, build_dir: str = BUILD, defines: tuple = ()) -> str:
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
+
+
+def device_asm(src: str, defines: tuple = ()) -> str:
+    """gfx950 assembly of one source, compiled with the options the build uses."""
+    with tempfile.TemporaryDirectory() as d:
+        out = os.path.join(d, "unit.s")
+        cmd = [_hipcc(), *common_flags(), *EXTRA_FLAGS.get(src, []), *[f"-D{x}" for x in defines],
+               "-x", "hip", "-S", "--cuda-device-only", os.path.join(CSRC, src), "-o", out]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        with open(out) as f:
+            return f.read()
 
 
 def build(verbose: bool = False, debug_sync: bool = False) -> str:

@@ -38,6 +38,12 @@
 // more than the repeated MFMA work.  Neither kernel refills an LDS stage while
 // any reader of it is unfinished (one barrier per stage), the single-buffer
 // K hazard described in the bug-hunting section of the B300 page.
+//
+// Two compilation units.  bwd_wide.hip includes this file with
+// JFA_BWD_WIDE_UNIT defined and emits only the d >= 192 dK/dV kernels and the
+// d = 192 dQ kernels, built with the MFMA builtins in their VGPR form: there the
+// dK/dV accumulators live in AGPRs through hand-written MFMAs
+// (DkvTile::ACC_AGPR).  This unit emits the rest.
 #include <algorithm>
 #include <type_traits>
 
@@ -46,6 +52,7 @@
 
 namespace jfa {
 
+#ifndef JFA_BWD_WIDE_UNIT
 // ----------------------------------------------------------------------------- preprocess
 constexpr int kPreThreads = 256;
 
@@ -137,6 +144,7 @@ hipError_t launch_dq_convert(const DqConvertArgs& a, hipStream_t stream) {
   hipLaunchKernelGGL(dq_convert_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
+#endif  // JFA_BWD_WIDE_UNIT
 
 // Stored order of the four 4-row quarters of a 16-row group in a transposed
 // tile: an S/dP accumulator hands lane half h the rows {4h..4h+3, 8+4h..8+4h+3}
@@ -201,6 +209,14 @@ struct DkvTile {
   static constexpr int QBLOCKS = (BM / 4) * (D / 8);   // 4-row x 8-column staging blocks
   static constexpr int KS = D / 16;
   static constexpr int DB = DC / 32;         // 32-wide blocks of the owned slice
+  // d >= 192: the dV^T/dK^T MFMAs are hand-written with their accumulators in
+  // AGPRs, while the S/dP products stay compiler-generated in VGPRs (the MFMA
+  // form bwd_wide.hip, which builds these kernels, asks for).  With every MFMA in AGPR form each S/dP entry needed its own
+  // v_accvgpr_read before the softmax; here those copies go and fewer registers
+  // are needed (no spills at d = 192): dK/dV 6-7.5 % faster at d = 192 and 256.
+  // At d <= 128 the fixed MFMA order of the hand-written statements cost more
+  // than that (5-7 % slower), so those kernels keep the compiler's MFMAs.
+  static constexpr bool ACC_AGPR = D >= 192;
   static_assert(QBLOCKS <= NT, "one Q block per thread");
   static_assert(D % DC == 0 && DC % 32 == 0, "slice width");
   static_assert(2 * (2 * BM * QP + 2 * DC * QTP) * 2 + 4 * BM * 4 <= 160 * 1024, "LDS budget");
@@ -438,6 +454,20 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
       // P = exp2(S*c - LSE*log2e); dS = P * (dP - delta); then
       // dV^T[d][key] += dO^T P ; dK^T[d][key] += Q^T dS  (A operands from the transposed tiles)
       auto grads = [&](int qb, const f32x16& sacc, const f32x16& pacc) {
+        // AGPR path: the A operands first, so their LDS reads complete under the
+        // softmax VALU work (the hand-written MFMAs keep their program order)
+        bf16x8 dfr[DB][2], qfr[DB][2];
+        if constexpr (T::ACC_AGPR) {
+#pragma unroll
+          for (int db = 0; db < DB; ++db) {
+            const __bf16* dtp = &dot_lds[buf][(32 * db + l32) * QTP + 32 * qb + 8 * hh];
+            const __bf16* qtp = &qt_lds[buf][(32 * db + l32) * QTP + 32 * qb + 8 * hh];
+            dfr[db][0] = *(const bf16x8*)(dtp);
+            dfr[db][1] = *(const bf16x8*)(dtp + 16);
+            qfr[db][0] = *(const bf16x8*)(qtp);
+            qfr[db][1] = *(const bf16x8*)(qtp + 16);
+          }
+        }
         float pv[16], dsv[16];
 #pragma unroll
         for (int r4 = 0; r4 < 4; ++r4) {
@@ -457,12 +487,16 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
         const bf16x8 sb0 = to_bf16x8(dsv), sb1 = to_bf16x8(dsv + 8);
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
-          const __bf16* dtp = &dot_lds[buf][(32 * db + l32) * QTP + 32 * qb + 8 * hh];
-          const __bf16* qtp = &qt_lds[buf][(32 * db + l32) * QTP + 32 * qb + 8 * hh];
-          dvt[db] = mfma32x32x16(*(const bf16x8*)(dtp), pb0, dvt[db]);
-          dvt[db] = mfma32x32x16(*(const bf16x8*)(dtp + 16), pb1, dvt[db]);
-          dkt[db] = mfma32x32x16(*(const bf16x8*)(qtp), sb0, dkt[db]);
-          dkt[db] = mfma32x32x16(*(const bf16x8*)(qtp + 16), sb1, dkt[db]);
+          if constexpr (T::ACC_AGPR) {
+            mfma4_acc_agpr(dvt[db], dkt[db], dfr[db][0], dfr[db][1], qfr[db][0], qfr[db][1], pb0, pb1, sb0, sb1);
+          } else {
+            const __bf16* dtp = &dot_lds[buf][(32 * db + l32) * QTP + 32 * qb + 8 * hh];
+            const __bf16* qtp = &qt_lds[buf][(32 * db + l32) * QTP + 32 * qb + 8 * hh];
+            dvt[db] = mfma32x32x16(*(const bf16x8*)(dtp), pb0, dvt[db]);
+            dvt[db] = mfma32x32x16(*(const bf16x8*)(dtp + 16), pb1, dvt[db]);
+            dkt[db] = mfma32x32x16(*(const bf16x8*)(qtp), sb0, dkt[db]);
+            dkt[db] = mfma32x32x16(*(const bf16x8*)(qtp + 16), sb1, dkt[db]);
+          }
         }
       };
       if constexpr (BM == 64) {
@@ -481,6 +515,10 @@ __global__ __launch_bounds__(256) void bwd_dkdv_kernel(BwdArgs a) {
           grads(qb, sacc, pacc);
         }
       }
+      // Every path out of the step (to the next step, the other step loop or the
+      // epilogue) starts after this wait, so the copies of the accumulators the
+      // compiler may place where those paths join read finished results.
+      if constexpr (T::ACC_AGPR) agpr_settle(dkt, dvt);
       debug_barrier();
       // Self-attention: unconditional, so the staging shares the step's basic block
       // and the scheduler can interleave it with the gradient MFMAs (dense causal
@@ -1000,6 +1038,7 @@ __global__ __launch_bounds__((DqTile<D, NARROW>::NT), (DqTile<D, NARROW>::WG_PER
   }
 }
 
+#ifndef JFA_BWD_WIDE_UNIT
 int bwd_dkdv_tile() { return DkvTile<128>::BN; }
 int bwd_dkdv_rows(int head_dim) { return head_dim <= 128 ? DkvTile<128>::BM : DkvTile<256>::BM; }
 int bwd_dkdv_slices(int head_dim) {
@@ -1017,6 +1056,7 @@ int bwd_dq_blocks_per_cu(int head_dim, bool narrow) {
   return head_dim == 64 ? DqTile<64>::WG_PER_CU : head_dim == 96 ? DqTile<96>::WG_PER_CU
        : head_dim == 128 ? DqTile<128>::WG_PER_CU : DqTile<256>::WG_PER_CU;
 }
+#endif  // JFA_BWD_WIDE_UNIT
 
 template <int D>
 static hipError_t launch_dkdv_d(const BwdArgs& a, int grid, hipStream_t stream) {
@@ -1044,13 +1084,14 @@ static hipError_t launch_dq_d(const BwdArgs& a, int grid, hipStream_t stream) {
   return launch_dq_dn<D, false>(a, grid, stream);
 }
 
+#ifndef JFA_BWD_WIDE_UNIT
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int grid, hipStream_t stream) {
   switch (head_dim) {
     case 64: return launch_dkdv_d<64>(a, grid, stream);
     case 96: return launch_dkdv_d<96>(a, grid, stream);
     case 128: return launch_dkdv_d<128>(a, grid, stream);
-    case 192: return launch_dkdv_d<192>(a, grid, stream);
-    case 256: return launch_dkdv_d<256>(a, grid, stream);
+    case 192:
+    case 256: return launch_bwd_dkdv_wide(a, head_dim, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1060,10 +1101,25 @@ hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int grid, hipStream_t s
     case 64: return launch_dq_d<64>(a, grid, stream);
     case 96: return launch_dq_d<96>(a, grid, stream);
     case 128: return launch_dq_d<128>(a, grid, stream);
-    case 192: return launch_dq_d<192>(a, grid, stream);
+    case 192: return launch_bwd_dq_wide(a, head_dim, grid, stream);
     case 256: return launch_dq_d<256>(a, grid, stream);
     default: return hipErrorInvalidValue;
   }
 }
+#else
+hipError_t launch_bwd_dkdv_wide(const BwdArgs& a, int head_dim, int grid, hipStream_t stream) {
+  switch (head_dim) {
+    case 192: return launch_dkdv_d<192>(a, grid, stream);
+    case 256: return launch_dkdv_d<256>(a, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// The dQ kernel has no hand-written MFMAs; at d = 192 it is 2 % faster built here
+// (equal or slower at d = 256, which stays in the other unit).
+hipError_t launch_bwd_dq_wide(const BwdArgs& a, int head_dim, int grid, hipStream_t stream) {
+  return head_dim == 192 ? launch_dq_d<192>(a, grid, stream) : hipErrorInvalidValue;
+}
+#endif  // JFA_BWD_WIDE_UNIT
 
 }  // namespace jfa

@@ -109,6 +109,45 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+// dv += a0 p0 + a1 p1 and dk += b0 s0 + b1 s1 on v_mfma_f32_32x32x16_bf16 with
+// both accumulators in AGPRs (the caller's other MFMAs keep theirs in VGPRs).
+// The compiler does not see MFMAs inside inline asm, so this statement carries
+// the wait states it would otherwise place, as read from the code it emits for
+// the same builtin sequences: two before an MFMA whose operand a VALU or
+// v_accvgpr_write has just written (every statement starts with them); none
+// between MFMAs chained on the same accumulator; agpr_settle's before anything
+// else reads or writes the accumulators.  One statement holds the four MFMAs,
+// so nothing the compiler emits can land between them; volatile keeps the
+// statements in program order.
+__device__ __forceinline__ void mfma4_acc_agpr(f32x16& dv, f32x16& dk, bf16x8 a0, bf16x8 a1, bf16x8 b0,
+                                               bf16x8 b1, bf16x8 p0, bf16x8 p1, bf16x8 s0, bf16x8 s1) {
+  asm volatile(
+      "s_nop 1\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %2, %6, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %4, %8, %1\n\t"
+      "v_mfma_f32_32x32x16_bf16 %0, %3, %7, %0\n\t"
+      "v_mfma_f32_32x32x16_bf16 %1, %5, %9, %1"
+      : "+a"(dv), "+a"(dk)
+      : "v"(a0), "v"(a1), "v"(b0), "v"(b1), "v"(p0), "v"(p1), "v"(s0), "v"(s1));
+}
+
+// 16 wait states after the last mfma4_acc_agpr (the compiler places 12 before
+// reading a 32x32x16 result).  Every accumulator is an operand, so the statement
+// follows every MFMA that writes one and precedes every later use of any of them.
+template <int N>
+__device__ __forceinline__ void agpr_settle(f32x16 (&x)[N], f32x16 (&y)[N]) {
+#define JFA_SETTLE "s_nop 15"
+  if constexpr (N == 4) {
+    asm volatile(JFA_SETTLE : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]), "+a"(y[0]), "+a"(y[1]), "+a"(y[2]),
+                 "+a"(y[3]));
+  } else {
+    static_assert(N == 6, "accumulator blocks of the d >= 192 dK/dV kernels");
+    asm volatile(JFA_SETTLE : "+a"(x[0]), "+a"(x[1]), "+a"(x[2]), "+a"(x[3]), "+a"(x[4]), "+a"(x[5]), "+a"(y[0]),
+                 "+a"(y[1]), "+a"(y[2]), "+a"(y[3]), "+a"(y[4]), "+a"(y[5]));
+  }
+#undef JFA_SETTLE
+}
+
 __device__ __forceinline__ f32x16 mfma32x32x16_f16(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }

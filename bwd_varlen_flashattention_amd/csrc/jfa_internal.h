@@ -141,6 +141,10 @@ struct BwdArgs {
 };
 hipError_t launch_bwd_dkdv(const BwdArgs& a, int head_dim, int grid, hipStream_t stream);
 hipError_t launch_bwd_dq(const BwdArgs& a, int head_dim, int grid, hipStream_t stream);
+// emitted by bwd_wide.hip (called by the two above): dK/dV at d = 192 and 256,
+// dQ at d = 192
+hipError_t launch_bwd_dkdv_wide(const BwdArgs& a, int head_dim, int grid, hipStream_t stream);
+hipError_t launch_bwd_dq_wide(const BwdArgs& a, int head_dim, int grid, hipStream_t stream);
 int bwd_dkdv_tile();                       // keys per dK/dV item
 int bwd_dkdv_rows(int head_dim);           // query rows per dK/dV step
 int bwd_dkdv_slices(int head_dim);         // head-dim slices (dK/dV items) per key tile
