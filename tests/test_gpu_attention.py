@@ -96,12 +96,13 @@ def test_ragged(jfa, d, causal, hq, hkv):
     _compare_full(_run_self(jfa, inp), _oracle_self(inp))
 
 
-@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("d", [64, 128, 192, 256])
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("hq,hkv", [(16, 2), (16, 1)])
 def test_wide_gqa_groups(jfa, d, causal, hq, hkv):
-    """GQA ratios 8 and 16: every dK/dV item sums its gradients over that many query heads,
-    and the forward / dQ items of one KV head run together."""
+    """GQA ratios 8 and 16: every dK/dV item sums its gradients over that many query heads
+    (at d >= 192 in the AGPR accumulators of the hand-written MFMAs, across that many
+    steps), and the forward / dQ items of one KV head run together."""
     inp = workloads.jagged(300 + d + hq // hkv, [1, 77, 300, 129, 0, 513], None, hq, hkv, d, causal)
     _say(f"wide GQA d={d} causal={causal} hq={hq} hkv={hkv}")
     _compare_full(_run_self(jfa, inp), _oracle_self(inp))
@@ -405,9 +406,10 @@ def test_large_head_dim_long_causal_sampled(jfa, d):
     _compare_sampled(inp, got, _oracle_self(inp, seqs=[0, 2]))
 
 
-def test_large_head_dim_repeatability(jfa):
-    """d = 256: the sliced dK/dV and every other output are bitwise identical across runs."""
-    inp = workloads.jagged(13, [300, 129, 64], None, 4, 2, 256, True)
+@pytest.mark.parametrize("d", [192, 256])
+def test_large_head_dim_repeatability(jfa, d):
+    """d = 192 / 256 (at 256 the sliced dK/dV): every output is bitwise identical across runs."""
+    inp = workloads.jagged(13, [300, 129, 64], None, 4, 2, d, True)
     first = _run_self(jfa, inp)
     for _ in range(4):
         got = _run_self(jfa, inp)
